@@ -1,0 +1,16 @@
+"""Reader for the key = value golden fixtures under tests/golden/."""
+import os
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def read(name):
+    out = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            k, v = (x.strip() for x in line.split("=", 1))
+            out[k] = v
+    return out

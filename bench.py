@@ -1,0 +1,224 @@
+#!/usr/bin/env python3
+"""Benchmark: effective masked-attention TFLOP/s of one ring rank's share on one GPU.
+
+Workload (default): the packed multimodal layout, 65536 tokens (text spans,
+1024-token image pairs grouped bidirectionally, generated images with p=0.3),
+24 query / 24 key-value heads, d=128, bf16, P=8 simulated ring steps on the
+busiest rank's 8192-token PTRR shard.
+
+One timed step = the whole hot path on resident inputs: P forward ring steps
+(fp32 state carried in HBM, finalize on each tile's last step), the backward
+prep (delta = rowsum(dO * O)) and P backward ring steps (dQ carried, dK/dV per
+shard).  The planner runs once per packed batch before timing (it is reused by
+every layer), as do plan upload and the input permutation.
+
+Only unmasked FLOPs count: 4*d*Hq per legal (query, key) pair forward,
+10*d*Hq backward.  `value` is the forward rate (the forward is the quoted
+pass of this workload); the forward+backward rate is reported beside it.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA, 2.4 GHz (AMD spec)
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=3, help="workload index 1..5")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU seconds of the oracle baseline sample")
+    ap.add_argument("--fwd-only", action="store_true", help="time only the forward pass")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this size (counter calibration)")
+    return ap.parse_args()
+
+
+def cpu_baseline(lay, plan_pairs_fn, rows_all, q, k, v, target_s):
+    """Time the fp64 oracle on whole samples of the measured rank's share."""
+    from oracle import attention as oatt
+    from oracle.mask import legal, take
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    sample = lay.sample
+    ranges = oatt.sample_ranges(sample)
+    smp_of_row = sample[rows_all]
+    order = list(dict.fromkeys(smp_of_row.tolist()))
+    rng = np.random.default_rng(0)
+    rng.shuffle(order)
+    done_rows, pairs, used = 0, 0, []
+    t0 = time.perf_counter()
+    for sid in order:
+        sel = rows_all[smp_of_row == sid]
+        a, b = ranges[sid]
+        pairs += int(legal(take(lay.tracks(), sel), take(lay.tracks(), np.arange(a, b)),
+                           lay.window).sum())
+        oatt.forward_rows(lay.tracks(), lay.window, q, k, v, sel, 1.0 / np.sqrt(lay.d))
+        done_rows += len(sel)
+        used.append(sid)
+        if time.perf_counter() - t0 >= target_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = 4 * lay.d * lay.hq * pairs
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"fp64 oracle forward of {done_rows} query rows of the measured rank "
+                      f"({len(used)} whole samples, {pairs} legal pairs) in {dt:.1f} s; "
+                      f"host {platform.processor() or platform.machine()}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import torch
+    import block_sparse_masked_metadata_amd as bsm
+    from workloads import config, qkv
+
+    lay = config(args.config)
+    t0 = time.perf_counter()
+    plan = bsm.Plan.from_layout(lay)
+    plan_s = time.perf_counter() - t0
+    r = plan.info["busiest_rank"]
+    R, S = lay.ranks, plan.info["shard_tokens"]
+    dp = bsm.DevicePlan(plan, r)
+    perm = plan.permutation().astype(np.int64)
+    rows = perm[r * S:(r + 1) * S]
+    pairs = plan.pairs()[r]
+    total_pairs = int(pairs.sum())
+    d = 128
+    hd = bsm.heads(lay.hq, lay.hkv, d, 1.0 / np.sqrt(lay.d))
+    full = qkv(lay.n, lay.hq, lay.hkv, d, lay.seed, "cuda", with_do=True)
+    pidx = torch.from_numpy(perm).cuda()
+    ridx = torch.from_numpy(rows).cuda()
+    q = full[0][ridx].contiguous()
+    dout = full[3][ridx].contiguous()
+    k_all = full[1][pidx].contiguous()
+    v_all = full[2][pidx].contiguous()
+    ks = [k_all[j * S:(j + 1) * S] for j in range(R)]
+    vs = [v_all[j * S:(j + 1) * S] for j in range(R)]
+    state = bsm.new_state(S, lay.hq, d)
+    o = torch.empty(S, lay.hq, d, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(lay.hq, S, dtype=torch.float32, device="cuda")
+    dq = torch.empty(S, lay.hq, d, dtype=torch.float32, device="cuda")
+    dks = [torch.zeros(S, lay.hkv, d, dtype=torch.float32, device="cuda") for _ in range(R)]
+    dvs = [torch.zeros(S, lay.hkv, d, dtype=torch.float32, device="cuda") for _ in range(R)]
+    fwd_steps = [s for s in range(R) if dp.info["fwd_items"][s] > 0]
+    do_bwd = not args.fwd_only
+
+    def forward(events=None):
+        for s in fwd_steps:
+            j = (r - s) % R
+            if events is not None:
+                events.append(torch.cuda.Event(enable_timing=True))
+                events[-1].record()
+            bsm.fwd_step(dp, s, hd, q, ks[j], vs[j], state, o, lse)
+            if events is not None:
+                events.append(torch.cuda.Event(enable_timing=True))
+                events[-1].record()
+
+    def backward():
+        bsm.bwd_ring(dp, hd, q, ks, vs, dout, o, lse, grads=(dq, dks, dvs))
+
+    for _ in range(args.warmup):
+        forward()
+        if do_bwd:
+            backward()
+    torch.cuda.synchronize()
+
+    launch_ev = []
+    marks = []
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        f0 = torch.cuda.Event(enable_timing=True)
+        f1 = torch.cuda.Event(enable_timing=True)
+        f0.record()
+        forward(launch_ev)
+        f1.record()
+        marks.append((f0, f1))
+        if do_bwd:
+            backward()
+    end = torch.cuda.Event(enable_timing=True)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+
+    total_ms = start.elapsed_time(end)
+    fwd_ms = sum(a.elapsed_time(b) for a, b in marks) / args.steps
+    step_ms = total_ms / args.steps
+    bwd_ms = step_ms - fwd_ms if do_bwd else 0.0
+    launches = [launch_ev[i].elapsed_time(launch_ev[i + 1]) for i in range(0, len(launch_ev), 2)]
+    avg_launch_ms = sum(launches) / len(launches)
+    fwd_flops = 4 * d * lay.hq * total_pairs
+    bwd_flops = 10 * d * lay.hq * total_pairs
+    fwd_tflops = fwd_flops / (fwd_ms * 1e-3) / 1e12
+    per_launch_flops = fwd_flops / len(fwd_steps)
+    achieved = per_launch_flops / (avg_launch_ms * 1e-3) / 1e12
+
+    if args.copy_mib:
+        src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    out = {
+        "metric": "effective masked-attention TFLOP/s (fwd, fwd+bwd) and % of bf16 MFMA peak, 1 GPU",
+        "value": round(fwd_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": lay.name, "tokens": lay.n, "ring_steps": R, "rank": r,
+                   "query_rows": S, "hq": lay.hq, "hkv": lay.hkv, "d": d,
+                   "legal_pairs": total_pairs, "layout": lay.order},
+        "pct_of_peak": round(100 * fwd_tflops / PEAK_BF16_TFLOPS, 2),
+        "fwd_ms": round(fwd_ms, 4),
+        "fwd_tflops": round(fwd_tflops, 2),
+        "fwd_bwd": None if not do_bwd else {
+            "ms": round(step_ms, 4), "bwd_ms": round(bwd_ms, 4),
+            "tflops": round((fwd_flops + bwd_flops) / (step_ms * 1e-3) / 1e12, 2),
+            "bwd_tflops": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 2),
+            "pct_of_peak": round(100 * (fwd_flops + bwd_flops) / (step_ms * 1e-3) / 1e12
+                                 / PEAK_BF16_TFLOPS, 2)},
+        "roofline": {"bound": "mfma", "kernel": "fwd_kernel", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "avg_launch_us": round(avg_launch_ms * 1e3, 2),
+                     "launches_per_step": len(fwd_steps)},
+        "planner_s": round(plan_s, 4),
+        "wall_s": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        qc, kc, vc = (t.cpu() for t in full[:3])
+        out["cpu_baseline"] = cpu_baseline(lay, None, rows, qc, kc, vc, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

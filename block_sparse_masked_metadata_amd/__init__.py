@@ -1,0 +1,15 @@
+"""Exact block-sparse masked attention for packed multimodal sequences on MI355X.
+
+One ring rank's share on one gfx950 GPU: a host planner (metadata tracks ->
+exact tile classes + PTRR order), HIP kernels that carry the fp32 online-softmax
+state across ring steps, and backward kernels against the final LSE.  The
+compute lives in libbsm.so (C ABI, include/bsm.h); `_capi` binds it 1:1 and
+`ring` adds torch-facing step loops.  Importing fails if libbsm.so is missing.
+"""
+from . import _capi
+from ._capi import BsmError, LIB_PATH
+from .ring import (Plan, DevicePlan, heads, new_state, fwd_step, fwd_ring, fwd_single,
+                   bwd_prep, bwd_ring)
+
+__all__ = ["_capi", "BsmError", "LIB_PATH", "Plan", "DevicePlan", "heads", "new_state",
+           "fwd_step", "fwd_ring", "fwd_single", "bwd_prep", "bwd_ring"]

@@ -1,0 +1,230 @@
+"""ctypes binding of libbsm.so: one Python function per C entry point, same names.
+
+Argument marshalling only: host arrays are passed as numpy buffers, device
+buffers as integer addresses, streams as integer hipStream_t handles.  Every
+non-zero status raises BsmError with the library's error text.  Importing this
+module fails loudly (ImportError) when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbsm.so")
+
+# PyTorch-ROCm ships its own HIP runtime (same SONAME as the system one).  Load
+# torch first so that libbsm binds to the runtime already in the process; two
+# HIP runtimes in one process crash.
+try:
+    import torch  # noqa: F401
+except ImportError:  # the C ABI itself does not need torch
+    pass
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"libbsm.so is not built ({LIB_PATH}); run "
+                      "`python -m block_sparse_masked_metadata_amd.build`")
+_lib = C.CDLL(LIB_PATH)
+
+BSM_OK, BSM_E_INVALID, BSM_E_UNSUPPORTED, BSM_E_NOMEM, BSM_E_HIP = 0, -1, -2, -3, -4
+BSM_WINDOW_INF = 0x7FFFFFFF
+BSM_ORDER_CONTIGUOUS, BSM_ORDER_PTRR, BSM_ORDER_EXPLICIT = 0, 1, 2
+BSM_TILE_EMPTY, BSM_TILE_PARTIAL, BSM_TILE_FULL = 0, 1, 2
+BSM_FWD_KEEP_STATE = 1
+
+ORDERS = {"contiguous": BSM_ORDER_CONTIGUOUS, "ptrr": BSM_ORDER_PTRR,
+          "explicit": BSM_ORDER_EXPLICIT}
+
+EXPORTS = [
+    "bsm_last_error", "bsm_version", "bsm_plan_build", "bsm_plan_free", "bsm_plan_get_info",
+    "bsm_plan_permutation", "bsm_plan_block_cost", "bsm_plan_step_map", "bsm_plan_pairs",
+    "bsm_dplan_bytes", "bsm_dplan_upload", "bsm_dplan_free", "bsm_dplan_get_info",
+    "bsm_fwd_step", "bsm_fwd_single", "bsm_bwd_prep", "bsm_bwd_step",
+]
+
+
+class BsmError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"libbsm error {code}: {msg}")
+        self.code = code
+
+
+class bsm_plan_desc(C.Structure):
+    _fields_ = [("n", C.c_int64), ("sample", C.c_void_p), ("seg", C.c_void_p),
+                ("noise", C.c_void_p), ("pos", C.c_void_p), ("window", C.c_int32),
+                ("ranks", C.c_int32), ("block", C.c_int32), ("order", C.c_int32),
+                ("explicit_block_perm", C.c_void_p), ("threads", C.c_int32)]
+
+
+class bsm_plan_info(C.Structure):
+    _fields_ = [("n", C.c_int64), ("ranks", C.c_int32), ("block", C.c_int32),
+                ("order", C.c_int32), ("window", C.c_int32), ("shard_tokens", C.c_int64),
+                ("tiles_per_shard", C.c_int32), ("tiles_total", C.c_int32),
+                ("busiest_rank", C.c_int32), ("reserved", C.c_int32),
+                ("total_pairs", C.c_int64), ("candidate_pairs", C.c_int64),
+                ("full_tiles", C.c_int64), ("partial_tiles", C.c_int64),
+                ("build_seconds", C.c_double)]
+
+
+class bsm_dplan_info(C.Structure):
+    _fields_ = [("rank", C.c_int32), ("ranks", C.c_int32), ("shard_tokens", C.c_int64),
+                ("tiles_per_shard", C.c_int32), ("window", C.c_int32),
+                ("fwd_items", C.c_int64 * 64), ("bwd_items", C.c_int64 * 64),
+                ("step_pairs", C.c_int64 * 64), ("single_items", C.c_int64)]
+
+
+class bsm_heads(C.Structure):
+    _fields_ = [("hq", C.c_int32), ("hkv", C.c_int32), ("d", C.c_int32), ("scale", C.c_float)]
+
+
+_P = C.c_void_p
+_sig = {
+    "bsm_last_error": (C.c_char_p, []),
+    "bsm_version": (C.c_int32, []),
+    "bsm_plan_build": (C.c_int, [C.POINTER(bsm_plan_desc), C.POINTER(_P)]),
+    "bsm_plan_free": (None, [_P]),
+    "bsm_plan_get_info": (C.c_int, [_P, C.POINTER(bsm_plan_info)]),
+    "bsm_plan_permutation": (C.c_int, [_P, _P]),
+    "bsm_plan_block_cost": (C.c_int, [_P, _P, _P]),
+    "bsm_plan_step_map": (C.c_int, [_P, C.c_int32, C.c_int32, _P, C.POINTER(C.c_int64)]),
+    "bsm_plan_pairs": (C.c_int, [_P, _P]),
+    "bsm_dplan_bytes": (C.c_int, [_P, C.c_int32, C.POINTER(C.c_int64)]),
+    "bsm_dplan_upload": (C.c_int, [_P, C.c_int32, _P, C.c_int64, _P, C.POINTER(_P)]),
+    "bsm_dplan_free": (None, [_P]),
+    "bsm_dplan_get_info": (C.c_int, [_P, C.POINTER(bsm_dplan_info)]),
+    "bsm_fwd_step": (C.c_int, [_P, C.c_int32, C.POINTER(bsm_heads), _P, _P, _P, _P, _P, _P,
+                               _P, _P, C.c_int32, _P]),
+    "bsm_fwd_single": (C.c_int, [_P, C.POINTER(bsm_heads), _P, _P, _P, _P, _P, _P, _P, _P,
+                                 C.c_int32, _P]),
+    "bsm_bwd_prep": (C.c_int, [C.POINTER(bsm_heads), C.c_int64, _P, _P, _P, _P]),
+    "bsm_bwd_step": (C.c_int, [_P, C.c_int32, C.POINTER(bsm_heads), _P, _P, _P, _P, _P, _P,
+                               _P, _P, _P, _P]),
+}
+for _name, (_res, _args) in _sig.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+
+def bsm_last_error() -> str:
+    return _lib.bsm_last_error().decode()
+
+
+def bsm_version() -> int:
+    return int(_lib.bsm_version())
+
+
+def _check(rc):
+    if rc != BSM_OK:
+        raise BsmError(rc, bsm_last_error())
+
+
+def _i32(a):
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def bsm_plan_build(sample, seg, noise, pos, window, ranks, block=128, order=BSM_ORDER_PTRR,
+                   explicit_block_perm=None, threads=0):
+    """Returns an opaque plan handle (int); free with bsm_plan_free."""
+    arrs = [_i32(x) for x in (sample, seg, noise, pos)]
+    n = len(arrs[0])
+    if any(len(a) != n for a in arrs):
+        raise ValueError("tracks must have equal length")
+    ebp = None if explicit_block_perm is None else _i32(explicit_block_perm)
+    desc = bsm_plan_desc(n, *(a.ctypes.data for a in arrs), int(min(window, BSM_WINDOW_INF)),
+                         int(ranks), int(block), int(order),
+                         None if ebp is None else ebp.ctypes.data, int(threads))
+    out = _P()
+    _check(_lib.bsm_plan_build(C.byref(desc), C.byref(out)))
+    return out.value
+
+
+def bsm_plan_free(plan):
+    _lib.bsm_plan_free(plan)
+
+
+def bsm_plan_get_info(plan) -> dict:
+    info = bsm_plan_info()
+    _check(_lib.bsm_plan_get_info(plan, C.byref(info)))
+    return {k: getattr(info, k) for k, _ in bsm_plan_info._fields_}
+
+
+def bsm_plan_permutation(plan):
+    n = bsm_plan_get_info(plan)["n"]
+    out = np.empty(n, np.int32)
+    _check(_lib.bsm_plan_permutation(plan, out.ctypes.data))
+    return out
+
+
+def bsm_plan_block_cost(plan):
+    t = bsm_plan_get_info(plan)["tiles_total"]
+    cost = np.empty(t, np.int64)
+    owner = np.empty(t, np.int32)
+    _check(_lib.bsm_plan_block_cost(plan, cost.ctypes.data, owner.ctypes.data))
+    return cost, owner
+
+
+def bsm_plan_step_map(plan, r, s):
+    t = bsm_plan_get_info(plan)["tiles_per_shard"]
+    mp = np.empty((t, t), np.uint8)
+    pairs = C.c_int64()
+    _check(_lib.bsm_plan_step_map(plan, int(r), int(s), mp.ctypes.data, C.byref(pairs)))
+    return mp, pairs.value
+
+
+def bsm_plan_pairs(plan):
+    rk = bsm_plan_get_info(plan)["ranks"]
+    out = np.empty((rk, rk), np.int64)
+    _check(_lib.bsm_plan_pairs(plan, out.ctypes.data))
+    return out
+
+
+def bsm_dplan_bytes(plan, r) -> int:
+    b = C.c_int64()
+    _check(_lib.bsm_dplan_bytes(plan, int(r), C.byref(b)))
+    return b.value
+
+
+def bsm_dplan_upload(plan, r, dev_ptr, nbytes, stream):
+    out = _P()
+    _check(_lib.bsm_dplan_upload(plan, int(r), dev_ptr, int(nbytes), stream, C.byref(out)))
+    return out.value
+
+
+def bsm_dplan_free(dplan):
+    _lib.bsm_dplan_free(dplan)
+
+
+def bsm_dplan_get_info(dplan) -> dict:
+    info = bsm_dplan_info()
+    _check(_lib.bsm_dplan_get_info(dplan, C.byref(info)))
+    rk = info.ranks
+    return {"rank": info.rank, "ranks": rk, "shard_tokens": info.shard_tokens,
+            "tiles_per_shard": info.tiles_per_shard, "window": info.window,
+            "fwd_items": list(info.fwd_items[:rk]), "bwd_items": list(info.bwd_items[:rk]),
+            "step_pairs": list(info.step_pairs[:rk]), "single_items": info.single_items}
+
+
+def _heads(hq, hkv, d, scale):
+    return bsm_heads(int(hq), int(hkv), int(d), float(scale))
+
+
+def bsm_fwd_step(dplan, s, heads, q, k, v, o_acc, m, l, o, lse, flags, stream):
+    _check(_lib.bsm_fwd_step(dplan, int(s), C.byref(heads), q, k, v, o_acc, m, l, o, lse,
+                             int(flags), stream))
+
+
+def bsm_fwd_single(dplan, heads, q, k_all, v_all, o_acc, m, l, o, lse, flags, stream):
+    _check(_lib.bsm_fwd_single(dplan, C.byref(heads), q, k_all, v_all, o_acc, m, l, o, lse,
+                               int(flags), stream))
+
+
+def bsm_bwd_prep(heads, rows, o, dout, delta, stream):
+    _check(_lib.bsm_bwd_prep(C.byref(heads), int(rows), o, dout, delta, stream))
+
+
+def bsm_bwd_step(dplan, s, heads, q, k, v, dout, lse, delta, dq_acc, dk, dv, stream):
+    _check(_lib.bsm_bwd_step(dplan, int(s), C.byref(heads), q, k, v, dout, lse, delta,
+                             dq_acc, dk, dv, stream))

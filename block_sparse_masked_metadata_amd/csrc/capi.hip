@@ -1,0 +1,504 @@
+// C ABI of libbsm.so (declared in include/bsm.h): argument checks, device-plan
+// packing and launch wrappers.  No device memory is allocated here; every
+// device buffer belongs to the caller.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "kernels.hpp"
+#include "planner.hpp"
+
+namespace bsm {
+
+namespace {
+thread_local std::string g_error;
+
+bool debug_sync() {
+  static const bool on = [] {
+    const char* e = std::getenv("BSM_DEBUG_SYNC");
+    return e && e[0] == '1';
+  }();
+  return on;
+}
+
+int hip_status(hipError_t e, const char* what, hipStream_t stream) {
+  if (e == hipSuccess && debug_sync()) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) {
+    set_error(std::string(what) + ": " + hipGetErrorString(e));
+    return BSM_E_HIP;
+  }
+  return BSM_OK;
+}
+
+int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
+
+struct StepLists {
+  std::vector<int4> fitems, bitems;
+  int64_t pairs = 0;
+};
+}  // namespace
+
+void set_error(const std::string& msg) { g_error = msg; }
+
+// Host image of one rank's device plan.
+struct Packed {
+  std::vector<int4> tracks;
+  std::vector<StepLists> steps;
+  std::vector<int4> sitems;
+  std::vector<int2> entries;
+  // byte offsets in the device buffer
+  int64_t off_tracks = 0, off_items = 0, off_entries = 0, bytes = 0;
+  std::vector<int64_t> off_f, off_b;
+  int64_t off_s = 0;
+};
+
+static void pack(const Plan& p, int32_t r, Packed& pk) {
+  const int32_t R = p.ranks, T = p.tps;
+  const int64_t S = p.shard;
+  pk.tracks.resize(p.n);
+  for (int64_t i = 0; i < p.n; ++i) {
+    const int32_t t = p.perm[i];
+    pk.tracks[i] = make_int4(p.sample[t], p.seg[t], p.noise[t], p.pos[t]);
+  }
+  auto tlen = [&](int32_t a) { return (int32_t)std::min<int64_t>(kTile, S - (int64_t)a * kTile); };
+  // per step row lists: rows[s][a] = (b, class) ascending b
+  std::vector<std::vector<std::vector<std::pair<int32_t, uint8_t>>>> rows(
+      R, std::vector<std::vector<std::pair<int32_t, uint8_t>>>(T));
+  std::vector<int64_t> step_pairs(R, 0);
+  for (int32_t a = 0; a < T; ++a) {
+    const int32_t tq = p.tiles_new[(int64_t)r * T + a];
+    for (int64_t e = p.pptr[tq]; e < p.pptr[tq + 1]; ++e) {
+      const int32_t tk = p.pkey[e];
+      const int32_t j = p.owner[tk];
+      const int32_t s = ((r - j) % R + R) % R;
+      rows[s][a].push_back({p.local[tk], p.pclass[e]});
+      step_pairs[s] += p.pcount[e];
+    }
+  }
+  std::vector<int32_t> first(T, -1), last(T, -1);
+  for (int32_t s = 0; s < R; ++s)
+    for (int32_t a = 0; a < T; ++a) {
+      std::sort(rows[s][a].begin(), rows[s][a].end());
+      if (!rows[s][a].empty()) {
+        if (first[a] < 0) first[a] = s;
+        last[a] = s;
+      }
+    }
+  auto by_len = [](const int4& x, const int4& y) { return x.w != y.w ? x.w > y.w : x.x < y.x; };
+  pk.steps.assign(R, StepLists());
+  pk.entries.clear();
+  for (int32_t s = 0; s < R; ++s) {
+    StepLists& st = pk.steps[s];
+    st.pairs = step_pairs[s];
+    // forward / dQ: query-tile major
+    for (int32_t a = 0; a < T; ++a) {
+      if (rows[s][a].empty()) continue;
+      const int32_t flags = (first[a] == s ? kFirst : 0) | (last[a] == s ? kLast : 0);
+      st.fitems.push_back(make_int4(a, flags, (int32_t)pk.entries.size(), (int32_t)rows[s][a].size()));
+      for (auto& bc : rows[s][a]) {
+        const int32_t kl = tlen(bc.first);
+        const bool part = bc.second == BSM_TILE_PARTIAL || kl < kTile;
+        pk.entries.push_back(make_int2(bc.first * kTile, kl | (part ? kPartialBit : 0)));
+      }
+    }
+    std::stable_sort(st.fitems.begin(), st.fitems.end(), by_len);
+    // dK/dV: key-tile major (column lists, ascending query tile)
+    std::vector<std::vector<std::pair<int32_t, uint8_t>>> cols(T);
+    for (int32_t a = 0; a < T; ++a)
+      for (auto& bc : rows[s][a]) cols[bc.first].push_back({a, bc.second});
+    for (int32_t b = 0; b < T; ++b) {
+      if (cols[b].empty()) continue;
+      st.bitems.push_back(make_int4(b, 0, (int32_t)pk.entries.size(), (int32_t)cols[b].size()));
+      for (auto& ac : cols[b]) {
+        const int32_t ql = tlen(ac.first);
+        const bool part = ac.second == BSM_TILE_PARTIAL || ql < kTile;
+        pk.entries.push_back(make_int2(ac.first * kTile, ql | (part ? kPartialBit : 0)));
+      }
+    }
+    std::stable_sort(st.bitems.begin(), st.bitems.end(), by_len);
+  }
+  // merged single-pass lists: ring step order, then ascending key tile
+  pk.sitems.clear();
+  for (int32_t a = 0; a < T; ++a) {
+    const int32_t beg = (int32_t)pk.entries.size();
+    for (int32_t s = 0; s < R; ++s) {
+      const int32_t j = ((r - s) % R + R) % R;
+      for (auto& bc : rows[s][a]) {
+        const int32_t kl = tlen(bc.first);
+        const bool part = bc.second == BSM_TILE_PARTIAL || kl < kTile;
+        pk.entries.push_back(make_int2((int32_t)(j * S + (int64_t)bc.first * kTile),
+                                       kl | (part ? kPartialBit : 0)));
+      }
+    }
+    const int32_t cnt = (int32_t)pk.entries.size() - beg;
+    if (cnt) pk.sitems.push_back(make_int4(a, kFirst | kLast, beg, cnt));
+  }
+  std::stable_sort(pk.sitems.begin(), pk.sitems.end(), by_len);
+
+  // byte layout
+  int64_t off = 0;
+  pk.off_tracks = off;
+  off = align256(off + p.n * (int64_t)sizeof(int4));
+  pk.off_items = off;
+  pk.off_f.assign(R, 0);
+  pk.off_b.assign(R, 0);
+  for (int32_t s = 0; s < R; ++s) {
+    pk.off_f[s] = off;
+    off = align256(off + (int64_t)pk.steps[s].fitems.size() * sizeof(int4));
+    pk.off_b[s] = off;
+    off = align256(off + (int64_t)pk.steps[s].bitems.size() * sizeof(int4));
+  }
+  pk.off_s = off;
+  off = align256(off + (int64_t)pk.sitems.size() * sizeof(int4));
+  pk.off_entries = off;
+  off = align256(off + (int64_t)pk.entries.size() * sizeof(int2));
+  pk.bytes = std::max<int64_t>(off, 256);
+}
+
+}  // namespace bsm
+
+struct bsm_dplan {
+  int32_t r = 0, R = 1, tps = 0, window = 0;
+  int64_t S = 0, n = 0;
+  const int4* tracks = nullptr;
+  const int2* entries = nullptr;
+  const int4* fitems[64] = {};
+  const int4* bitems[64] = {};
+  int64_t nf[64] = {}, nb[64] = {}, pairs[64] = {};
+  const int4* sitems = nullptr;
+  int64_t ns = 0;
+};
+
+using namespace bsm;
+
+namespace {
+
+int check_heads(const bsm_heads* h) {
+  if (!h) { set_error("heads is NULL"); return BSM_E_INVALID; }
+  if (h->hq < 1 || h->hkv < 1 || h->hq % h->hkv) {
+    set_error("need hq >= 1, hkv >= 1 and hq % hkv == 0");
+    return BSM_E_INVALID;
+  }
+  if (h->d != kHeadDim) { set_error("only d == 128 is supported"); return BSM_E_UNSUPPORTED; }
+  if (!(h->scale > 0.f)) { set_error("scale must be > 0"); return BSM_E_INVALID; }
+  return BSM_OK;
+}
+
+int32_t heads_per_xcd(int32_t hq) { return hq % 8 == 0 ? hq / 8 : 0; }
+
+const uint16_t* bf(const void* p) { return (const uint16_t*)p; }
+
+}  // namespace
+
+extern "C" {
+
+const char* bsm_last_error(void) { return g_error.c_str(); }
+
+int32_t bsm_version(void) { return 100; }
+
+int bsm_plan_build(const bsm_plan_desc* desc, bsm_plan** out) {
+  if (!desc || !out) { set_error("null argument"); return BSM_E_INVALID; }
+  *out = nullptr;
+  bsm_plan* p = new (std::nothrow) bsm_plan();
+  if (!p) { set_error("out of host memory"); return BSM_E_NOMEM; }
+  int rc;
+  try {
+    rc = build_plan(*desc, p->p);
+  } catch (const std::bad_alloc&) {
+    set_error("out of host memory");
+    rc = BSM_E_NOMEM;
+  }
+  if (rc) {
+    delete p;
+    return rc;
+  }
+  *out = p;
+  return BSM_OK;
+}
+
+void bsm_plan_free(bsm_plan* plan) { delete plan; }
+
+int bsm_plan_get_info(const bsm_plan* plan, bsm_plan_info* out) {
+  if (!plan || !out) { set_error("null argument"); return BSM_E_INVALID; }
+  const Plan& p = plan->p;
+  std::memset(out, 0, sizeof(*out));
+  out->n = p.n;
+  out->ranks = p.ranks;
+  out->block = p.block;
+  out->order = p.order;
+  out->window = p.window;
+  out->shard_tokens = p.shard;
+  out->tiles_per_shard = p.tps;
+  out->tiles_total = p.ntiles;
+  out->busiest_rank = p.busiest;
+  out->total_pairs = p.total_pairs;
+  out->candidate_pairs = p.candidates;
+  out->full_tiles = p.nfull;
+  out->partial_tiles = p.npartial;
+  out->build_seconds = p.seconds;
+  return BSM_OK;
+}
+
+int bsm_plan_permutation(const bsm_plan* plan, int32_t* new_to_orig) {
+  if (!plan || !new_to_orig) { set_error("null argument"); return BSM_E_INVALID; }
+  std::copy(plan->p.perm.begin(), plan->p.perm.end(), new_to_orig);
+  return BSM_OK;
+}
+
+int bsm_plan_block_cost(const bsm_plan* plan, int64_t* cost, int32_t* owner) {
+  if (!plan) { set_error("null plan"); return BSM_E_INVALID; }
+  if (cost) std::copy(plan->p.cost.begin(), plan->p.cost.end(), cost);
+  if (owner) std::copy(plan->p.owner.begin(), plan->p.owner.end(), owner);
+  return BSM_OK;
+}
+
+int bsm_plan_step_map(const bsm_plan* plan, int32_t r, int32_t s, uint8_t* map, int64_t* pairs) {
+  if (!plan) { set_error("null plan"); return BSM_E_INVALID; }
+  if (r < 0 || r >= plan->p.ranks || s < 0 || s >= plan->p.ranks) {
+    set_error("rank or step out of range");
+    return BSM_E_INVALID;
+  }
+  const int64_t t = step_map(plan->p, r, s, map);
+  if (pairs) *pairs = t;
+  return BSM_OK;
+}
+
+int bsm_plan_pairs(const bsm_plan* plan, int64_t* pairs) {
+  if (!plan || !pairs) { set_error("null argument"); return BSM_E_INVALID; }
+  const int32_t R = plan->p.ranks;
+  for (int32_t r = 0; r < R; ++r)
+    for (int32_t s = 0; s < R; ++s) pairs[(int64_t)r * R + s] = step_map(plan->p, r, s, nullptr);
+  return BSM_OK;
+}
+
+int bsm_dplan_bytes(const bsm_plan* plan, int32_t r, int64_t* bytes) {
+  if (!plan || !bytes) { set_error("null argument"); return BSM_E_INVALID; }
+  if (r < 0 || r >= plan->p.ranks) { set_error("rank out of range"); return BSM_E_INVALID; }
+  if (plan->p.block != kTile) { set_error("device plans need block == 128"); return BSM_E_UNSUPPORTED; }
+  try {
+    Packed pk;
+    pack(plan->p, r, pk);
+    *bytes = pk.bytes;
+  } catch (const std::bad_alloc&) {
+    set_error("out of host memory");
+    return BSM_E_NOMEM;
+  }
+  return BSM_OK;
+}
+
+int bsm_dplan_upload(const bsm_plan* plan, int32_t r, void* dev, int64_t bytes, void* stream,
+                     bsm_dplan** out) {
+  if (!plan || !dev || !out) { set_error("null argument"); return BSM_E_INVALID; }
+  *out = nullptr;
+  if (r < 0 || r >= plan->p.ranks) { set_error("rank out of range"); return BSM_E_INVALID; }
+  if (plan->p.block != kTile) { set_error("device plans need block == 128"); return BSM_E_UNSUPPORTED; }
+  const Plan& p = plan->p;
+  try {
+    Packed pk;
+    pack(p, r, pk);
+    if (bytes < pk.bytes) {
+      set_error("device plan buffer too small: need " + std::to_string(pk.bytes) + " bytes");
+      return BSM_E_NOMEM;
+    }
+    std::vector<char> img(pk.bytes, 0);
+    std::memcpy(img.data() + pk.off_tracks, pk.tracks.data(), pk.tracks.size() * sizeof(int4));
+    for (int32_t s = 0; s < p.ranks; ++s) {
+      std::memcpy(img.data() + pk.off_f[s], pk.steps[s].fitems.data(), pk.steps[s].fitems.size() * sizeof(int4));
+      std::memcpy(img.data() + pk.off_b[s], pk.steps[s].bitems.data(), pk.steps[s].bitems.size() * sizeof(int4));
+    }
+    std::memcpy(img.data() + pk.off_s, pk.sitems.data(), pk.sitems.size() * sizeof(int4));
+    std::memcpy(img.data() + pk.off_entries, pk.entries.data(), pk.entries.size() * sizeof(int2));
+    hipStream_t st = (hipStream_t)stream;
+    int rc = hip_status(hipMemcpyAsync(dev, img.data(), pk.bytes, hipMemcpyHostToDevice, st),
+                        "plan upload", st);
+    if (rc) return rc;
+    rc = hip_status(hipStreamSynchronize(st), "plan upload sync", st);
+    if (rc) return rc;
+    bsm_dplan* d = new bsm_dplan();
+    char* base = (char*)dev;
+    d->r = r;
+    d->R = p.ranks;
+    d->tps = p.tps;
+    d->window = p.window;
+    d->S = p.shard;
+    d->n = p.n;
+    d->tracks = (const int4*)(base + pk.off_tracks);
+    d->entries = (const int2*)(base + pk.off_entries);
+    for (int32_t s = 0; s < p.ranks; ++s) {
+      d->fitems[s] = (const int4*)(base + pk.off_f[s]);
+      d->bitems[s] = (const int4*)(base + pk.off_b[s]);
+      d->nf[s] = (int64_t)pk.steps[s].fitems.size();
+      d->nb[s] = (int64_t)pk.steps[s].bitems.size();
+      d->pairs[s] = pk.steps[s].pairs;
+    }
+    d->sitems = (const int4*)(base + pk.off_s);
+    d->ns = (int64_t)pk.sitems.size();
+    *out = d;
+  } catch (const std::bad_alloc&) {
+    set_error("out of host memory");
+    return BSM_E_NOMEM;
+  }
+  return BSM_OK;
+}
+
+void bsm_dplan_free(bsm_dplan* dplan) { delete dplan; }
+
+int bsm_dplan_get_info(const bsm_dplan* d, bsm_dplan_info* out) {
+  if (!d || !out) { set_error("null argument"); return BSM_E_INVALID; }
+  std::memset(out, 0, sizeof(*out));
+  out->rank = d->r;
+  out->ranks = d->R;
+  out->shard_tokens = d->S;
+  out->tiles_per_shard = d->tps;
+  out->window = d->window;
+  for (int32_t s = 0; s < d->R; ++s) {
+    out->fwd_items[s] = d->nf[s];
+    out->bwd_items[s] = d->nb[s];
+    out->step_pairs[s] = d->pairs[s];
+  }
+  out->single_items = d->ns;
+  return BSM_OK;
+}
+
+int bsm_fwd_step(const bsm_dplan* d, int32_t s, const bsm_heads* heads, const void* q,
+                 const void* k, const void* v, float* o_acc, float* m, float* l, void* o,
+                 float* lse, int32_t flags, void* stream) {
+  if (!d) { set_error("null device plan"); return BSM_E_INVALID; }
+  int rc = check_heads(heads);
+  if (rc) return rc;
+  if (s < 0 || s >= d->R) { set_error("step out of range"); return BSM_E_INVALID; }
+  const bool keep = (flags & BSM_FWD_KEEP_STATE) != 0;
+  if (!q || !k || !v || !o_acc || !m || !l || (!keep && (!o || !lse))) {
+    set_error("null tensor pointer");
+    return BSM_E_INVALID;
+  }
+  if (d->nf[s] == 0) return BSM_OK;
+  const int32_t j = ((d->r - s) % d->R + d->R) % d->R;
+  FwdArgs a{};
+  a.items = d->fitems[s];
+  a.entries = d->entries;
+  a.nitems = (int32_t)d->nf[s];
+  a.hq = heads->hq;
+  a.hkv = heads->hkv;
+  a.heads_per_xcd = heads_per_xcd(heads->hq);
+  a.q = bf(q);
+  a.k = bf(k);
+  a.v = bf(v);
+  a.qtracks = d->tracks + (int64_t)d->r * d->S;
+  a.ktracks = d->tracks + (int64_t)j * d->S;
+  a.rows = d->S;
+  a.oacc = o_acc;
+  a.m = m;
+  a.l = l;
+  a.o = (uint16_t*)o;
+  a.lse = lse;
+  a.scale_log2 = heads->scale * 1.44269504088896340736f;
+  a.window = d->window;
+  a.keep_state = keep ? 1 : 0;
+  hipStream_t st = (hipStream_t)stream;
+  return hip_status(launch_fwd(a, st), "forward step launch", st);
+}
+
+int bsm_fwd_single(const bsm_dplan* d, const bsm_heads* heads, const void* q, const void* k_all,
+                   const void* v_all, float* o_acc, float* m, float* l, void* o, float* lse,
+                   int32_t flags, void* stream) {
+  if (!d) { set_error("null device plan"); return BSM_E_INVALID; }
+  int rc = check_heads(heads);
+  if (rc) return rc;
+  const bool keep = (flags & BSM_FWD_KEEP_STATE) != 0;
+  if (!q || !k_all || !v_all || (keep && (!o_acc || !m || !l)) || (!keep && (!o || !lse))) {
+    set_error("null tensor pointer");
+    return BSM_E_INVALID;
+  }
+  if (d->ns == 0) return BSM_OK;
+  FwdArgs a{};
+  a.items = d->sitems;
+  a.entries = d->entries;
+  a.nitems = (int32_t)d->ns;
+  a.hq = heads->hq;
+  a.hkv = heads->hkv;
+  a.heads_per_xcd = heads_per_xcd(heads->hq);
+  a.q = bf(q);
+  a.k = bf(k_all);
+  a.v = bf(v_all);
+  a.qtracks = d->tracks + (int64_t)d->r * d->S;
+  a.ktracks = d->tracks;
+  a.rows = d->S;
+  a.oacc = o_acc;
+  a.m = m;
+  a.l = l;
+  a.o = (uint16_t*)o;
+  a.lse = lse;
+  a.scale_log2 = heads->scale * 1.44269504088896340736f;
+  a.window = d->window;
+  a.keep_state = keep ? 1 : 0;
+  hipStream_t st = (hipStream_t)stream;
+  return hip_status(launch_fwd(a, st), "forward single launch", st);
+}
+
+int bsm_bwd_prep(const bsm_heads* heads, int64_t rows, const void* o, const void* dout,
+                 float* delta, void* stream) {
+  int rc = check_heads(heads);
+  if (rc) return rc;
+  if (rows < 1) { set_error("rows must be >= 1"); return BSM_E_INVALID; }
+  if (!o || !dout || !delta) { set_error("null tensor pointer"); return BSM_E_INVALID; }
+  hipStream_t st = (hipStream_t)stream;
+  return hip_status(launch_bwd_prep(rows, heads->hq, bf(o), bf(dout), delta, st), "bwd prep launch", st);
+}
+
+int bsm_bwd_step(const bsm_dplan* d, int32_t s, const bsm_heads* heads, const void* q,
+                 const void* k, const void* v, const void* dout, const float* lse,
+                 const float* delta, float* dq_acc, float* dk, float* dv, void* stream) {
+  if (!d) { set_error("null device plan"); return BSM_E_INVALID; }
+  int rc = check_heads(heads);
+  if (rc) return rc;
+  if (s < 0 || s >= d->R) { set_error("step out of range"); return BSM_E_INVALID; }
+  if (!q || !k || !v || !dout || !lse || !delta || !dq_acc || !dk || !dv) {
+    set_error("null tensor pointer");
+    return BSM_E_INVALID;
+  }
+  const int32_t j = ((d->r - s) % d->R + d->R) % d->R;
+  BwdArgs a{};
+  a.entries = d->entries;
+  a.hq = heads->hq;
+  a.hkv = heads->hkv;
+  a.heads_per_xcd = heads_per_xcd(heads->hq);
+  a.q = bf(q);
+  a.k = bf(k);
+  a.v = bf(v);
+  a.dout = bf(dout);
+  a.lse = lse;
+  a.delta = delta;
+  a.qtracks = d->tracks + (int64_t)d->r * d->S;
+  a.ktracks = d->tracks + (int64_t)j * d->S;
+  a.rows = d->S;
+  a.krows = d->S;
+  a.dq = dq_acc;
+  a.dk = dk;
+  a.dv = dv;
+  a.scale = heads->scale;
+  a.scale_log2 = heads->scale * 1.44269504088896340736f;
+  a.window = d->window;
+  hipStream_t st = (hipStream_t)stream;
+  if (d->nf[s]) {
+    a.items = d->fitems[s];
+    a.nitems = (int32_t)d->nf[s];
+    rc = hip_status(launch_bwd_dq(a, st), "bwd dq launch", st);
+    if (rc) return rc;
+  }
+  if (d->nb[s]) {
+    a.items = d->bitems[s];
+    a.nitems = (int32_t)d->nb[s];
+    a.heads_per_xcd = heads->hkv % 8 == 0 ? heads->hkv / 8 : 0;
+    rc = hip_status(launch_bwd_dkdv(a, st), "bwd dkdv launch", st);
+  }
+  return rc;
+}
+
+}  // extern "C"

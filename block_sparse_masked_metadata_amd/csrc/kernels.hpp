@@ -1,0 +1,78 @@
+// Device-side data layout and kernel launchers (internal to libbsm.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace bsm {
+
+constexpr int kHeadDim = 128;   // d
+constexpr int kTile = 128;      // query and key tile tokens
+
+// Work item of a list-driven kernel (int4 in device memory):
+//   x = tile index (query tile for forward / dQ, key tile for dK/dV)
+//   y = flags (kFirst: the tile's first step with work, kLast: its last)
+//   z = first entry of the tile's list, w = number of entries
+enum : int32_t { kFirst = 1, kLast = 2 };
+
+// List entry (int2): x = first row of the partner tile in the partner buffer,
+//                    y = valid rows of the partner tile | (partial << 16)
+// A partner tile with fewer than 128 valid rows is always marked partial.
+constexpr int32_t kPartialBit = 1 << 16;
+
+// Per-token tracks in plan order (int4): sample, seg, noise, pos.
+// bf16 tensors are passed as raw 16-bit patterns (uint16_t).
+
+struct FwdArgs {
+  const int4* items;
+  const int2* entries;
+  int32_t nitems;
+  int32_t hq, hkv;
+  int32_t heads_per_xcd;   // >0: XCD-aware block->(item, head) map
+  const uint16_t* q;  // [S, Hq, d]
+  const uint16_t* k;  // [*, Hkv, d]
+  const uint16_t* v;
+  const int4* qtracks;      // tracks of the query shard rows
+  const int4* ktracks;      // tracks of the key buffer rows
+  int64_t rows;             // S: query shard rows (state stride / ragged bound)
+  float* oacc;              // [S, Hq, d] fp32
+  float* m;                 // [Hq, S]
+  float* l;                 // [Hq, S]
+  uint16_t* o;        // [S, Hq, d]
+  float* lse;               // [Hq, S]
+  float scale_log2;         // scale * log2(e)
+  int32_t window;
+  int32_t keep_state;
+};
+
+struct BwdArgs {
+  const int4* items;
+  const int2* entries;
+  int32_t nitems;
+  int32_t hq, hkv;
+  int32_t heads_per_xcd;
+  const uint16_t* q;    // [S, Hq, d]
+  const uint16_t* k;    // [Sk, Hkv, d]
+  const uint16_t* v;
+  const uint16_t* dout; // [S, Hq, d]
+  const float* lse;           // [Hq, S] natural log
+  const float* delta;         // [Hq, S]
+  const int4* qtracks;
+  const int4* ktracks;
+  int64_t rows;               // S (query rows)
+  int64_t krows;              // key rows of the k/v buffers
+  float* dq;                  // [S, Hq, d]
+  float* dk;                  // [Sk, Hkv, d]
+  float* dv;
+  float scale;                // softmax scale
+  float scale_log2;
+  int32_t window;
+};
+
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_prep(int64_t rows, int32_t hq, const uint16_t* o,
+                           const uint16_t* dout, float* delta, hipStream_t stream);
+hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);
+
+}  // namespace bsm

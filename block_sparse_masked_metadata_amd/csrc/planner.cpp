@@ -1,0 +1,307 @@
+// Host planner: metadata tracks -> exact tile classes, pair counts, PTRR order.
+//
+// MARBLE ("exact sequence parallelism for packed multimodal masks"):
+//   section 01, mask_mod code block   - the legality predicate over the tracks
+//   section 03, "Block classification" - full / empty / partial tile pairs,
+//                                         classified from per-tile summaries
+//   section 03, "PTRR"                 - sort blocks by cost, deal in rounds of
+//                                         R, reverse every other round, keep
+//                                         each rank's blocks in sequence order
+//   section 04, "Planning cost"        - built once per batch on CPU threads
+//
+// Classification is exact: a tile pair is FULL when every valid token pair is
+// legal, EMPTY when none is, PARTIAL otherwise.  Per-tile summaries (min/max of
+// every track) decide a pair only when they prove it; every other candidate
+// pair is counted token pair by token pair.  Candidate key tiles of a query
+// tile are the tiles whose sample-id range meets the query tile's, which is a
+// contiguous run of tiles because samples are contiguous runs in the original
+// order and tiles are contiguous pieces of it.
+
+#include "planner.hpp"
+
+#include <algorithm>
+#include <atomic>
+#include <chrono>
+#include <numeric>
+#include <thread>
+
+namespace bsm {
+
+namespace {
+
+struct Summary {
+  int32_t smin, smax, gmin, gmax, nmin, nmax, pmin, pmax;
+};
+
+Summary summarize(const Plan& p, int64_t a, int64_t b) {
+  Summary s{p.sample[a], p.sample[b - 1], INT32_MAX, INT32_MIN, INT32_MAX, INT32_MIN,
+            p.pos[a], p.pos[b - 1]};
+  for (int64_t i = a; i < b; ++i) {
+    s.gmin = std::min(s.gmin, p.seg[i]);
+    s.gmax = std::max(s.gmax, p.seg[i]);
+    s.nmin = std::min(s.nmin, p.noise[i]);
+    s.nmax = std::max(s.nmax, p.noise[i]);
+  }
+  return s;
+}
+
+// Exact number of legal pairs between query tokens [qa, qb) and key tokens [ka, kb).
+int64_t count_pairs(const Plan& p, int64_t qa, int64_t qb, int64_t ka, int64_t kb) {
+  const int32_t* ks = p.sample.data() + ka;
+  const int32_t* kg = p.seg.data() + ka;
+  const int32_t* kn = p.noise.data() + ka;
+  const int32_t* kp = p.pos.data() + ka;
+  const int64_t nk = kb - ka;
+  const int32_t w = p.window;
+  int64_t total = 0;
+  for (int64_t q = qa; q < qb; ++q) {
+    const int32_t sq = p.sample[q], gq = p.seg[q], nq = p.noise[q], pq = p.pos[q];
+    int32_t c = 0;
+    for (int64_t j = 0; j < nk; ++j) {
+      const int32_t d = pq - kp[j];  // positions lie in [0, 2^31): no overflow
+      const bool causal = (d >= 0) & (d < w);
+      const bool span = (gq == kg[j]) & (kg[j] >= 0);
+      const bool keep = (kn[j] < 0) | (nq == kn[j]);
+      c += (int32_t)((causal | span) & keep & (sq == ks[j]));
+    }
+    total += c;
+  }
+  return total;
+}
+
+// Summary-only proof: +1 provably FULL, -1 provably EMPTY, 0 undecided.
+int prove(const Summary& q, const Summary& k, int32_t w) {
+  if (q.smax < k.smin || k.smax < q.smin) return -1;
+  // every key is one noise span that no query belongs to
+  if (k.nmin == k.nmax && k.nmin >= 0 && (q.nmax < k.nmin || q.nmin > k.nmin)) return -1;
+  const int64_t dmax = (int64_t)q.pmax - k.pmin;  // largest pos_q - pos_k
+  const int64_t dmin = (int64_t)q.pmin - k.pmax;  // smallest
+  const bool causal_none = dmax < 0 || dmin >= w;
+  const bool span_none = q.gmax < 0 || k.gmax < 0 || q.gmax < k.gmin || k.gmax < q.gmin;
+  if (causal_none && span_none) return -1;
+  const bool one_sample = q.smin == q.smax && k.smin == k.smax && q.smin == k.smin;
+  const bool keep_all = k.nmax < 0 ||
+                        (q.nmin == q.nmax && k.nmin == k.nmax && q.nmin == k.nmin);
+  const bool causal_all = dmin >= 0 && dmax < w;
+  const bool span_all = q.gmin == q.gmax && k.gmin == k.gmax && q.gmin == k.gmin && k.gmin >= 0;
+  if (one_sample && keep_all && (causal_all || span_all)) return 1;
+  return 0;
+}
+
+int validate(const bsm_plan_desc& d) {
+  if (d.n < 1 || d.n > (int64_t(1) << 30)) { set_error("n must be in [1, 2^30]"); return BSM_E_INVALID; }
+  if (!d.sample || !d.seg || !d.noise || !d.pos) { set_error("null track pointer"); return BSM_E_INVALID; }
+  if (d.window < 1) { set_error("window must be >= 1"); return BSM_E_INVALID; }
+  if (d.ranks < 1 || d.ranks > 64) { set_error("ranks must be in [1, 64]"); return BSM_E_INVALID; }
+  if (d.block < 1 || d.block > (1 << 20)) { set_error("block must be in [1, 2^20]"); return BSM_E_INVALID; }
+  if (d.order == BSM_ORDER_CONTIGUOUS) {
+    if (d.n % d.ranks) { set_error("contiguous order needs n % ranks == 0"); return BSM_E_INVALID; }
+  } else if (d.order == BSM_ORDER_PTRR || d.order == BSM_ORDER_EXPLICIT) {
+    if (d.n % ((int64_t)d.block * d.ranks)) {
+      set_error("block orders need n % (block * ranks) == 0");
+      return BSM_E_INVALID;
+    }
+    if (d.order == BSM_ORDER_EXPLICIT && !d.explicit_block_perm) {
+      set_error("explicit order needs explicit_block_perm");
+      return BSM_E_INVALID;
+    }
+  } else {
+    set_error("unknown order");
+    return BSM_E_INVALID;
+  }
+  for (int64_t i = 0; i < d.n; ++i) {
+    if (d.seg[i] < -1 || d.noise[i] < -1) { set_error("seg and noise ids must be >= -1"); return BSM_E_INVALID; }
+    if (d.pos[i] < 0) { set_error("pos must be >= 0"); return BSM_E_INVALID; }
+    if (i > 0) {
+      if (d.sample[i] < d.sample[i - 1]) {
+        set_error("samples must be contiguous runs with non-decreasing ids");
+        return BSM_E_INVALID;
+      }
+      if (d.pos[i] <= d.pos[i - 1]) { set_error("pos must be strictly increasing"); return BSM_E_INVALID; }
+    }
+  }
+  return BSM_OK;
+}
+
+template <class F>
+void parallel_for(int64_t count, int threads, F&& fn) {
+  if (threads <= 1 || count < 2) {
+    for (int64_t i = 0; i < count; ++i) fn(i);
+    return;
+  }
+  std::atomic<int64_t> next{0};
+  std::vector<std::thread> pool;
+  const int nt = (int)std::min<int64_t>(threads, count);
+  for (int t = 0; t < nt; ++t)
+    pool.emplace_back([&] {
+      for (;;) {
+        const int64_t i = next.fetch_add(1);
+        if (i >= count) break;
+        fn(i);
+      }
+    });
+  for (auto& th : pool) th.join();
+}
+
+}  // namespace
+
+int build_plan(const bsm_plan_desc& d, Plan& p) {
+  const auto t0 = std::chrono::steady_clock::now();
+  int rc = validate(d);
+  if (rc) return rc;
+  p.n = d.n;
+  p.ranks = d.ranks;
+  p.block = d.block;
+  p.order = d.order;
+  p.window = d.window;
+  p.shard = d.n / d.ranks;
+  p.sample.assign(d.sample, d.sample + d.n);
+  p.seg.assign(d.seg, d.seg + d.n);
+  p.noise.assign(d.noise, d.noise + d.n);
+  p.pos.assign(d.pos, d.pos + d.n);
+
+  // tiles in the original order
+  if (d.order == BSM_ORDER_CONTIGUOUS) {
+    p.tps = (int32_t)((p.shard + d.block - 1) / d.block);
+    for (int32_t r = 0; r < d.ranks; ++r)
+      for (int32_t t = 0; t < p.tps; ++t) {
+        const int64_t a = r * p.shard + (int64_t)t * d.block;
+        p.tstart.push_back(a);
+        p.tend.push_back(std::min(a + d.block, (r + 1) * p.shard));
+      }
+  } else {
+    p.tps = (int32_t)(p.shard / d.block);
+    for (int64_t a = 0; a < d.n; a += d.block) {
+      p.tstart.push_back(a);
+      p.tend.push_back(a + d.block);
+    }
+  }
+  p.ntiles = (int32_t)p.tstart.size();
+  const int32_t nt = p.ntiles;
+
+  std::vector<Summary> sum(nt);
+  for (int32_t t = 0; t < nt; ++t) sum[t] = summarize(p, p.tstart[t], p.tend[t]);
+
+  // candidate key tile range [lo, hi) per query tile: sample ranges intersect
+  std::vector<int32_t> smaxs(nt), smins(nt);
+  for (int32_t t = 0; t < nt; ++t) {
+    smins[t] = sum[t].smin;
+    smaxs[t] = sum[t].smax;
+  }
+  int threads = d.threads;
+  if (threads <= 0) threads = (int)std::max(1u, std::thread::hardware_concurrency());
+
+  std::vector<std::vector<int32_t>> rk(nt);
+  std::vector<std::vector<int64_t>> rc_(nt);
+  std::vector<std::vector<uint8_t>> rcl(nt);
+  std::vector<int64_t> cand(nt, 0);
+  parallel_for(nt, threads, [&](int64_t tq) {
+    const Summary& qs = sum[tq];
+    const int32_t lo = (int32_t)(std::lower_bound(smaxs.begin(), smaxs.end(), qs.smin) - smaxs.begin());
+    const int32_t hi = (int32_t)(std::upper_bound(smins.begin(), smins.end(), qs.smax) - smins.begin());
+    const int64_t qlen = p.tile_len((int32_t)tq);
+    for (int32_t tk = lo; tk < hi; ++tk) {
+      ++cand[tq];
+      const int proof = prove(qs, sum[tk], p.window);
+      if (proof < 0) continue;
+      const int64_t full = qlen * p.tile_len(tk);
+      const int64_t c = proof > 0 ? full
+                                  : count_pairs(p, p.tstart[tq], p.tend[tq], p.tstart[tk], p.tend[tk]);
+      if (c == 0) continue;
+      rk[tq].push_back(tk);
+      rc_[tq].push_back(c);
+      rcl[tq].push_back(c == full ? BSM_TILE_FULL : BSM_TILE_PARTIAL);
+    }
+  });
+
+  p.pptr.assign(nt + 1, 0);
+  p.cost.assign(nt, 0);
+  for (int32_t t = 0; t < nt; ++t) {
+    p.pptr[t + 1] = p.pptr[t] + (int64_t)rk[t].size();
+    p.candidates += cand[t];
+  }
+  p.pkey.resize(p.pptr[nt]);
+  p.pcount.resize(p.pptr[nt]);
+  p.pclass.resize(p.pptr[nt]);
+  for (int32_t t = 0; t < nt; ++t) {
+    std::copy(rk[t].begin(), rk[t].end(), p.pkey.begin() + p.pptr[t]);
+    std::copy(rc_[t].begin(), rc_[t].end(), p.pcount.begin() + p.pptr[t]);
+    std::copy(rcl[t].begin(), rcl[t].end(), p.pclass.begin() + p.pptr[t]);
+    for (int64_t c : rc_[t]) p.cost[t] += c;
+    for (uint8_t c : rcl[t]) (c == BSM_TILE_FULL ? p.nfull : p.npartial)++;
+    p.total_pairs += p.cost[t];
+  }
+
+  // token order
+  p.tiles_new.resize(nt);
+  if (d.order == BSM_ORDER_CONTIGUOUS) {
+    std::iota(p.tiles_new.begin(), p.tiles_new.end(), 0);
+  } else if (d.order == BSM_ORDER_PTRR) {
+    std::vector<int32_t> order(nt);
+    std::iota(order.begin(), order.end(), 0);
+    std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
+      return p.cost[a] != p.cost[b] ? p.cost[a] > p.cost[b] : a < b;
+    });
+    std::vector<int32_t> own(nt);
+    for (int32_t i = 0; i < nt; ++i) {
+      const int32_t round = i / d.ranks, slot = i % d.ranks;
+      own[order[i]] = (round % 2 == 0) ? slot : d.ranks - 1 - slot;
+    }
+    int32_t k = 0;
+    for (int32_t r = 0; r < d.ranks; ++r)
+      for (int32_t t = 0; t < nt; ++t)
+        if (own[t] == r) p.tiles_new[k++] = t;
+  } else {
+    std::vector<uint8_t> seen(nt, 0);
+    for (int32_t i = 0; i < nt; ++i) {
+      const int32_t t = d.explicit_block_perm[i];
+      if (t < 0 || t >= nt || seen[t]) {
+        set_error("explicit_block_perm is not a permutation of the blocks");
+        return BSM_E_INVALID;
+      }
+      seen[t] = 1;
+      p.tiles_new[i] = t;
+    }
+  }
+  p.owner.resize(nt);
+  p.local.resize(nt);
+  for (int32_t i = 0; i < nt; ++i) {
+    p.owner[p.tiles_new[i]] = i / p.tps;
+    p.local[p.tiles_new[i]] = i % p.tps;
+  }
+  p.perm.clear();
+  p.perm.reserve(d.n);
+  for (int32_t i = 0; i < nt; ++i)
+    for (int64_t x = p.tstart[p.tiles_new[i]]; x < p.tend[p.tiles_new[i]]; ++x) p.perm.push_back((int32_t)x);
+
+  // busiest rank: most legal pairs over all keys, ties -> lowest rank
+  int64_t best = -1;
+  for (int32_t r = 0; r < d.ranks; ++r) {
+    int64_t tot = 0;
+    for (int32_t a = 0; a < p.tps; ++a) tot += p.cost[p.tiles_new[r * p.tps + a]];
+    if (tot > best) {
+      best = tot;
+      p.busiest = r;
+    }
+  }
+  p.seconds = std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
+  return BSM_OK;
+}
+
+int64_t step_map(const Plan& p, int32_t r, int32_t s, uint8_t* map) {
+  const int32_t j = ((r - s) % p.ranks + p.ranks) % p.ranks;
+  if (map) std::fill(map, map + (int64_t)p.tps * p.tps, (uint8_t)BSM_TILE_EMPTY);
+  int64_t total = 0;
+  for (int32_t a = 0; a < p.tps; ++a) {
+    const int32_t tq = p.tiles_new[r * p.tps + a];
+    for (int64_t e = p.pptr[tq]; e < p.pptr[tq + 1]; ++e) {
+      const int32_t tk = p.pkey[e];
+      if (p.owner[tk] != j) continue;
+      if (map) map[(int64_t)a * p.tps + p.local[tk]] = p.pclass[e];
+      total += p.pcount[e];
+    }
+  }
+  return total;
+}
+
+}  // namespace bsm

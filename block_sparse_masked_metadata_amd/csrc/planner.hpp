@@ -1,0 +1,52 @@
+// Host planner internals shared by planner.cpp and capi.cpp (C++17, no HIP).
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "bsm.h"
+
+namespace bsm {
+
+// Per-thread error text behind bsm_last_error().
+void set_error(const std::string& msg);
+
+struct Plan {
+  int64_t n = 0;
+  int32_t ranks = 1, block = 128, order = 0, window = BSM_WINDOW_INF;
+  int64_t shard = 0;            // tokens per shard
+  int32_t tps = 0;              // tiles per shard
+  int32_t ntiles = 0;           // ranks * tps
+  // tiles in the ORIGINAL order: [tstart, tend)
+  std::vector<int64_t> tstart, tend;
+  std::vector<int32_t> tiles_new;  // new tile position -> original tile
+  std::vector<int32_t> owner;      // original tile -> shard
+  std::vector<int32_t> local;      // original tile -> index in its shard
+  std::vector<int64_t> cost;       // legal pairs of the tile's queries
+  // non-empty tile pairs, CSR over original query tiles, ascending key tile
+  std::vector<int64_t> pptr;
+  std::vector<int32_t> pkey;
+  std::vector<int64_t> pcount;
+  std::vector<uint8_t> pclass;
+  std::vector<int32_t> perm;       // new token -> original token
+  // tracks, original order
+  std::vector<int32_t> sample, seg, noise, pos;
+  int32_t busiest = 0;
+  int64_t total_pairs = 0, candidates = 0, nfull = 0, npartial = 0;
+  double seconds = 0;
+
+  int64_t tile_len(int32_t t) const { return tend[t] - tstart[t]; }
+};
+
+// Build; returns BSM_OK or an error code (error text set).
+int build_plan(const bsm_plan_desc& desc, Plan& out);
+
+// Legal pairs of rank r at step s and optional tile map.
+int64_t step_map(const Plan& p, int32_t r, int32_t s, uint8_t* map);
+
+}  // namespace bsm
+
+struct bsm_plan {
+  bsm::Plan p;
+};

@@ -1,0 +1,190 @@
+"""Torch-facing helpers over the C ABI: plans, device plans and the step loops.
+
+Argument marshalling and orchestration only.  Every step of the path runs in
+libbsm's kernels; PyTorch provides device memory (caller-owned buffers) and the
+current HIP stream.  Layouts follow include/bsm.h.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from . import _capi as C
+
+
+def _stream():
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t, dtype, shape, name):
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name}: expected contiguous {dtype} cuda tensor of shape {tuple(shape)}, "
+                         f"got {t.dtype} {tuple(t.shape)} contiguous={t.is_contiguous()}")
+
+
+class Plan:
+    """Host plan (owned handle).  `tracks` = (sample, seg, noise, pos) in original order."""
+
+    def __init__(self, tracks, window, ranks, block=128, order="ptrr", explicit_block_perm=None,
+                 threads=0):
+        self.handle = C.bsm_plan_build(*tracks, window, ranks, block, C.ORDERS[order],
+                                       explicit_block_perm, threads)
+        self.info = C.bsm_plan_get_info(self.handle)
+
+    @classmethod
+    def from_layout(cls, layout, threads=0):
+        return cls(layout.tracks(), layout.window, layout.ranks, layout.block, layout.order,
+                   threads=threads)
+
+    def permutation(self):
+        return C.bsm_plan_permutation(self.handle)
+
+    def step_map(self, r, s):
+        return C.bsm_plan_step_map(self.handle, r, s)
+
+    def pairs(self):
+        return C.bsm_plan_pairs(self.handle)
+
+    def block_cost(self):
+        return C.bsm_plan_block_cost(self.handle)
+
+    def close(self):
+        if self.handle:
+            C.bsm_plan_free(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class DevicePlan:
+    """Rank r's device plan in a torch uint8 buffer (the library allocates nothing)."""
+
+    def __init__(self, plan: Plan, r: int, device="cuda"):
+        import torch
+        nbytes = C.bsm_dplan_bytes(plan.handle, r)
+        self.buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.handle = C.bsm_dplan_upload(plan.handle, r, self.buf.data_ptr(), nbytes, _stream())
+        self.info = C.bsm_dplan_get_info(self.handle)
+        self.rank = r
+        self.ranks = plan.info["ranks"]
+        self.rows = plan.info["shard_tokens"]
+
+    def close(self):
+        if self.handle:
+            C.bsm_dplan_free(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def heads(hq, hkv, d=128, scale=None):
+    return C._heads(hq, hkv, d, 1.0 / math.sqrt(d) if scale is None else scale)
+
+
+def new_state(rows, hq, d, device="cuda"):
+    """Uninitialized fp32 state (O_acc, m, l): the first step initializes it in-kernel."""
+    import torch
+    return (torch.empty(rows, hq, d, dtype=torch.float32, device=device),
+            torch.empty(hq, rows, dtype=torch.float32, device=device),
+            torch.empty(hq, rows, dtype=torch.float32, device=device))
+
+
+def fwd_step(dp: DevicePlan, s, hd, q, k, v, state, o, lse, keep_state=False):
+    o_acc, m, l = state
+    C.bsm_fwd_step(dp.handle, s, hd, _ptr(q), _ptr(k), _ptr(v), _ptr(o_acc), _ptr(m), _ptr(l),
+                   _ptr(o), _ptr(lse), C.BSM_FWD_KEEP_STATE if keep_state else 0, _stream())
+
+
+def fwd_ring(dp: DevicePlan, hd, q, k_shards, v_shards, state=None, out=None, keep_state=False,
+             steps=None):
+    """Run ring steps s = 0..R-1 (shard j = (r - s) mod R from k_shards[j]).
+
+    Returns (o, lse, state)."""
+    import torch
+    rows = dp.rows
+    _need(q, torch.bfloat16, (rows, hd.hq, hd.d), "q")
+    for j in range(dp.ranks):
+        _need(k_shards[j], torch.bfloat16, (rows, hd.hkv, hd.d), f"k_shards[{j}]")
+        _need(v_shards[j], torch.bfloat16, (rows, hd.hkv, hd.d), f"v_shards[{j}]")
+    if state is None:
+        state = new_state(rows, hd.hq, hd.d, q.device)
+    if out is None:
+        out = (torch.empty(rows, hd.hq, hd.d, dtype=torch.bfloat16, device=q.device),
+               torch.empty(hd.hq, rows, dtype=torch.float32, device=q.device))
+    o, lse = out
+    for s in (range(dp.ranks) if steps is None else steps):
+        j = (dp.rank - s) % dp.ranks
+        fwd_step(dp, s, hd, q, k_shards[j], v_shards[j], state, o, lse, keep_state)
+    return o, lse, state
+
+
+def fwd_single(dp: DevicePlan, hd, q, k_all, v_all, keep_state=False, out=None):
+    """Single pass over all shards (k_all/v_all = shards concatenated in plan order)."""
+    import torch
+    rows = dp.rows
+    _need(q, torch.bfloat16, (rows, hd.hq, hd.d), "q")
+    _need(k_all, torch.bfloat16, (rows * dp.ranks, hd.hkv, hd.d), "k_all")
+    _need(v_all, torch.bfloat16, (rows * dp.ranks, hd.hkv, hd.d), "v_all")
+    if keep_state:
+        state = new_state(rows, hd.hq, hd.d, q.device)
+        C.bsm_fwd_single(dp.handle, hd, _ptr(q), _ptr(k_all), _ptr(v_all), *(_ptr(t) for t in state),
+                         None, None, C.BSM_FWD_KEEP_STATE, _stream())
+        return state
+    if out is None:
+        out = (torch.empty(rows, hd.hq, hd.d, dtype=torch.bfloat16, device=q.device),
+               torch.empty(hd.hq, rows, dtype=torch.float32, device=q.device))
+    o, lse = out
+    C.bsm_fwd_single(dp.handle, hd, _ptr(q), _ptr(k_all), _ptr(v_all), None, None, None,
+                     _ptr(o), _ptr(lse), 0, _stream())
+    return o, lse
+
+
+def bwd_prep(hd, o, dout, delta=None):
+    import torch
+    rows = o.shape[0]
+    if delta is None:
+        delta = torch.empty(hd.hq, rows, dtype=torch.float32, device=o.device)
+    C.bsm_bwd_prep(hd, rows, _ptr(o), _ptr(dout), _ptr(delta), _stream())
+    return delta
+
+
+def bwd_ring(dp: DevicePlan, hd, q, k_shards, v_shards, dout, o, lse, grads=None, steps=None):
+    """Backward over ring steps s = 0..R-1.  Returns (dq, dk_shards, dv_shards) in fp32.
+
+    dk/dv shards are accumulated (+=) by the kernels: they are cleared here
+    first, as the owner of a travelling accumulator would before the first
+    contribution."""
+    import torch
+    rows = dp.rows
+    _need(dout, torch.bfloat16, (rows, hd.hq, hd.d), "dout")
+    delta = bwd_prep(hd, o, dout)
+    if grads is None:
+        dq = torch.empty(rows, hd.hq, hd.d, dtype=torch.float32, device=q.device)
+        dks = [torch.zeros(rows, hd.hkv, hd.d, dtype=torch.float32, device=q.device)
+               for _ in range(dp.ranks)]
+        dvs = [torch.zeros(rows, hd.hkv, hd.d, dtype=torch.float32, device=q.device)
+               for _ in range(dp.ranks)]
+    else:
+        dq, dks, dvs = grads
+        for t in dks + dvs:
+            t.zero_()
+    for s in (range(dp.ranks) if steps is None else steps):
+        j = (dp.rank - s) % dp.ranks
+        C.bsm_bwd_step(dp.handle, s, hd, _ptr(q), _ptr(k_shards[j]), _ptr(v_shards[j]),
+                       _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq), _ptr(dks[j]), _ptr(dvs[j]),
+                       _stream())
+    return dq, dks, dvs

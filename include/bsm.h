@@ -1,0 +1,286 @@
+/*
+ * bsm.h - exact block-sparse masked attention for packed multimodal sequences,
+ * one ring rank's share on one MI355X (gfx950).
+ *
+ * C ABI of libbsm.so.  Plain integers, host pointers and device pointers only.
+ *
+ * Conventions for every entry point
+ *   - Return value: BSM_OK (0) on success, a negative BSM_E_* code otherwise.
+ *     No entry point aborts, throws or exits; bsm_last_error() returns a
+ *     thread-local description of the most recent failure on that thread.
+ *   - Argument and shape errors are reported before anything is launched.
+ *   - GPU entry points enqueue work on the caller's stream (`stream` is a
+ *     hipStream_t; NULL means the default stream) and never synchronize.
+ *     Faults inside a kernel surface at the caller's next synchronization;
+ *     with the environment variable BSM_DEBUG_SYNC=1 every entry point
+ *     synchronizes its stream and reports such faults as BSM_E_HIP.
+ *   - The library never allocates device memory.  Every device buffer is
+ *     allocated by the caller, who keeps ownership.  Host plans are owned by
+ *     the library and released with bsm_plan_free / bsm_dplan_free.
+ *   - Tensor layouts (all contiguous, 16-byte aligned device memory):
+ *       Q, O, dO          bf16  [rows, Hq, d]     token-major
+ *       K, V              bf16  [keys, Hkv, d]
+ *       O_acc, dQ         fp32  [rows, Hq, d]
+ *       dK, dV            fp32  [keys, Hkv, d]
+ *       m, l, LSE, delta  fp32  [Hq, rows]        head-major
+ *     d must be 128.  Query head h reads key/value head h / (Hq / Hkv).
+ *
+ * Terms (MARBLE, "exact sequence parallelism for packed multimodal masks"):
+ *   ring of R ranks; at step s rank r holds the key/value shard of rank
+ *   j = (r - s) mod R (section 03, "Block classification", ring submasks);
+ *   tiles are 128 query tokens x 128 key tokens.
+ */
+#ifndef BSM_H
+#define BSM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---- */
+enum {
+  BSM_OK = 0,
+  BSM_E_INVALID = -1,      /* bad argument, shape or metadata               */
+  BSM_E_UNSUPPORTED = -2,  /* valid but not supported (e.g. d != 128)       */
+  BSM_E_NOMEM = -3,        /* host allocation failed / caller buffer small  */
+  BSM_E_HIP = -4           /* a HIP runtime call or kernel launch failed    */
+};
+
+/* Window value for global (non-sliding-window) layers. */
+#define BSM_WINDOW_INF 0x7fffffff
+
+/* Token orders (MARBLE section 04, "Layout transforms"). */
+enum {
+  BSM_ORDER_CONTIGUOUS = 0, /* shard r = tokens [r*N/R, (r+1)*N/R); tiles are
+                               `block`-token pieces of a shard, last ragged   */
+  BSM_ORDER_PTRR = 1,       /* processing-time round robin over blocks        */
+  BSM_ORDER_EXPLICIT = 2    /* caller-given permutation of blocks             */
+};
+
+/* Tile classes (MARBLE section 03, "Block classification"). */
+enum { BSM_TILE_EMPTY = 0, BSM_TILE_PARTIAL = 1, BSM_TILE_FULL = 2 };
+
+/* Flags of the forward entry points. */
+enum {
+  BSM_FWD_KEEP_STATE = 1   /* never finalize: always store (O_acc, m, l),
+                              even on a tile's last step; O and LSE untouched */
+};
+
+/* Thread-local text of the last failure on the calling thread ("" if none). */
+const char* bsm_last_error(void);
+
+/* Library version, e.g. 100 for 0.1.0. */
+int32_t bsm_version(void);
+
+/* ====================================================================== *
+ *  Host planner (pure CPU).                                               *
+ * ====================================================================== */
+
+typedef struct bsm_plan bsm_plan;
+
+/*
+ * Per-token metadata of one packed sequence, in its ORIGINAL order
+ * (MARBLE section 01, the four tracks and the mask_mod code block):
+ *   sample[i]  sample id; each sample is one contiguous run, ids non-decreasing
+ *   seg[i]     id of the bidirectional span / group, -1 for causal tokens
+ *   noise[i]   id of the generated (noise) span, -1 otherwise
+ *   pos[i]     original position, strictly increasing, >= 0
+ * A query q may attend a key k iff
+ *   ((0 <= pos[q]-pos[k] < window) or (seg[q] == seg[k] and seg[k] >= 0))
+ *   and (noise[k] < 0 or noise[q] == noise[k]) and sample[q] == sample[k].
+ * All pointers are host memory, read during the call only.
+ */
+typedef struct {
+  int64_t n;                 /* tokens, 1 <= n <= 2^30                        */
+  const int32_t* sample;
+  const int32_t* seg;
+  const int32_t* noise;
+  const int32_t* pos;
+  int32_t window;            /* >= 1; BSM_WINDOW_INF for global layers        */
+  int32_t ranks;             /* ring degree R, 1..64                          */
+  int32_t block;             /* tile / PTRR block tokens; 128 for the kernels */
+  int32_t order;             /* BSM_ORDER_*                                   */
+  const int32_t* explicit_block_perm; /* ORDER_EXPLICIT: new block i is original
+                                         block explicit_block_perm[i]; else NULL */
+  int32_t threads;           /* planner threads; <= 0: all hardware threads   */
+} bsm_plan_desc;
+
+/*
+ * Build the plan (MARBLE section 03: "Block classification" and "PTRR";
+ * section 04 "Planning cost": built once per packed batch from metadata only,
+ * reused by every layer, forward and backward).
+ *   - Validates the tracks (BSM_E_INVALID on violation).
+ *   - Classifies every (query tile, key tile) pair exactly: the number of
+ *     legal token pairs among the tile's valid tokens decides EMPTY (0),
+ *     FULL (all) or PARTIAL.  Per-tile summaries only skip work; they never
+ *     decide a class that enumeration would decide differently.
+ *   - PTRR: tile cost = exact legal pairs of the tile's queries over all keys;
+ *     sort by cost descending, ties by ascending original index; deal in
+ *     rounds of R, even rounds to ranks 0..R-1, odd rounds to R-1..0; each
+ *     rank keeps its tiles in ascending original order.
+ *   ORDER_PTRR / ORDER_EXPLICIT need n % (block * ranks) == 0;
+ *   ORDER_CONTIGUOUS needs n % ranks == 0.
+ * On success *out owns a new plan (free with bsm_plan_free).
+ */
+int bsm_plan_build(const bsm_plan_desc* desc, bsm_plan** out);
+void bsm_plan_free(bsm_plan* plan);
+
+typedef struct {
+  int64_t n;
+  int32_t ranks;
+  int32_t block;
+  int32_t order;
+  int32_t window;
+  int64_t shard_tokens;      /* n / ranks                                      */
+  int32_t tiles_per_shard;   /* ceil(shard_tokens / block)                     */
+  int32_t tiles_total;       /* ranks * tiles_per_shard                        */
+  int32_t busiest_rank;      /* most legal pairs, ties -> lowest rank          */
+  int32_t reserved;
+  int64_t total_pairs;       /* legal pairs of the whole sequence              */
+  int64_t candidate_pairs;   /* tile pairs whose samples overlap               */
+  int64_t full_tiles;        /* tile pairs classified FULL (all ranks/steps)   */
+  int64_t partial_tiles;     /* tile pairs classified PARTIAL                  */
+  double build_seconds;      /* wall time of bsm_plan_build                    */
+} bsm_plan_info;
+
+int bsm_plan_get_info(const bsm_plan* plan, bsm_plan_info* out);
+
+/* Token permutation: new_to_orig[new] = original index (host int32[n]). */
+int bsm_plan_permutation(const bsm_plan* plan, int32_t* new_to_orig);
+
+/* Per ORIGINAL tile: cost (legal pairs, int64[tiles_total]) and owner rank
+ * (int32[tiles_total]).  Either pointer may be NULL. */
+int bsm_plan_block_cost(const bsm_plan* plan, int64_t* cost, int32_t* owner);
+
+/* Tile map of rank r at step s: map[a * tiles_per_shard + b] = class of
+ * (query tile a of rank r, key tile b of shard (r - s) mod R), host
+ * uint8[tiles_per_shard^2]; *pairs (may be NULL) = legal token pairs. */
+int bsm_plan_step_map(const bsm_plan* plan, int32_t r, int32_t s, uint8_t* map,
+                      int64_t* pairs);
+
+/* pairs[r * R + s] = legal pairs of rank r at step s (host int64[R*R]). */
+int bsm_plan_pairs(const bsm_plan* plan, int64_t* pairs);
+
+/* ====================================================================== *
+ *  Device plan: one rank's lists, packed into caller-owned device memory. *
+ * ====================================================================== */
+
+typedef struct bsm_dplan bsm_dplan;
+
+/* Bytes the device plan of rank r needs (256-byte aligned sections). */
+int bsm_dplan_bytes(const bsm_plan* plan, int32_t r, int64_t* bytes);
+
+/*
+ * Pack rank r's device plan (permuted tracks, per-step forward row lists and
+ * backward column lists, the merged single-pass list) on the host and copy it
+ * into `dev` (caller device memory of >= bsm_dplan_bytes bytes) on `stream`;
+ * the call synchronizes `stream` before it returns (a plan is uploaded once per
+ * packed batch, outside any timed loop).  Requires block == 128.  `dev` must
+ * stay allocated while the handle is used.  *out: new handle (host memory,
+ * free with bsm_dplan_free, which does not touch `dev`).
+ */
+int bsm_dplan_upload(const bsm_plan* plan, int32_t r, void* dev, int64_t bytes,
+                     void* stream, bsm_dplan** out);
+void bsm_dplan_free(bsm_dplan* dplan);
+
+typedef struct {
+  int32_t rank;
+  int32_t ranks;
+  int64_t shard_tokens;
+  int32_t tiles_per_shard;
+  int32_t window;
+  int64_t fwd_items[64];     /* query tiles with work at step s               */
+  int64_t bwd_items[64];     /* key tiles with work at step s                 */
+  int64_t step_pairs[64];    /* legal pairs at step s                         */
+  int64_t single_items;      /* query tiles with work in the merged list      */
+} bsm_dplan_info;
+
+int bsm_dplan_get_info(const bsm_dplan* dplan, bsm_dplan_info* out);
+
+/* ====================================================================== *
+ *  Forward.                                                               *
+ * ====================================================================== */
+
+typedef struct {
+  int32_t hq;     /* query heads                                          */
+  int32_t hkv;    /* key/value heads, hq % hkv == 0                        */
+  int32_t d;      /* head dim, must be 128                                 */
+  float scale;    /* softmax scale, usually 1/sqrt(d)                      */
+} bsm_heads;
+
+/*
+ * One ring step of the online forward (MARBLE section 03, "Exact ring
+ * attention accumulation"): for every query tile of the rank with a
+ * non-empty list at step s and every query head, fold the listed key tiles of
+ * shard j = (r - s) mod R into the fp32 running state.
+ *   q      bf16 [S, Hq, d]   the rank's query shard in plan order
+ *   k, v   bf16 [S, Hkv, d]  shard j in plan order
+ *   o_acc  fp32 [S, Hq, d]   unnormalized accumulator   (carried state)
+ *   m      fp32 [Hq, S]      running row max of scale*log2(e)*q.k (base-2
+ *                            units), -inf before the first legal key
+ *   l      fp32 [Hq, S]      running row sum of 2^(x - m)
+ *   o      bf16 [S, Hq, d]   written at a tile's last non-empty step
+ *   lse    fp32 [Hq, S]      natural-log LSE, written with o
+ * A tile's first non-empty step initializes the state in-kernel (m = -inf,
+ * l = 0, O_acc = 0), so the state buffers need no clearing; later steps read
+ * it; the last non-empty step writes O = O_acc / l (bf16, round to nearest
+ * even) and LSE = ln 2 * (m + log2 l) instead of storing the state, unless
+ * flags has BSM_FWD_KEEP_STATE.  Rows with no legal key get O = 0 and
+ * LSE = -inf.  Steps without work return BSM_OK without a launch.  S is the
+ * plan's shard_tokens; rows of a ragged last tile beyond S are never touched.
+ */
+int bsm_fwd_step(const bsm_dplan* dplan, int32_t s, const bsm_heads* heads,
+                 const void* q, const void* k, const void* v,
+                 float* o_acc, float* m, float* l, void* o, float* lse,
+                 int32_t flags, void* stream);
+
+/*
+ * Single pass over all R shards at once (the one-GPU result the ring must
+ * equal): k_all, v_all bf16 [N, Hkv, d] hold all shards in plan order
+ * (shard j at rows [j*S, (j+1)*S)).  Tiles are visited in the same order as
+ * the ring visits them, with the state kept in registers, so the result is
+ * bitwise identical to the R ring steps.  With BSM_FWD_KEEP_STATE it stores
+ * (o_acc, m, l) instead of (o, lse); otherwise o_acc, m, l may be NULL.
+ */
+int bsm_fwd_single(const bsm_dplan* dplan, const bsm_heads* heads,
+                   const void* q, const void* k_all, const void* v_all,
+                   float* o_acc, float* m, float* l, void* o, float* lse,
+                   int32_t flags, void* stream);
+
+/* ====================================================================== *
+ *  Backward.                                                              *
+ * ====================================================================== */
+
+/*
+ * delta[h][i] = sum_c dO[i][h][c] * O[i][h][c] in fp32 (the row term of the
+ * softmax backward), from the bf16 O the forward wrote.  rows >= 1.
+ */
+int bsm_bwd_prep(const bsm_heads* heads, int64_t rows, const void* o, const void* dout,
+                 float* delta, void* stream);
+
+/*
+ * One ring step of the backward (MARBLE section 03: each step runs the
+ * attention backward against the FINAL LSE; the fp32 dQ accumulator is carried
+ * across steps, and each key shard's fp32 dK/dV accumulator travels with it).
+ *   q, dout         bf16 [S, Hq, d]    the rank's queries and output gradient
+ *   k, v            bf16 [S, Hkv, d]   shard j = (r - s) mod R
+ *   lse, delta      fp32 [Hq, S]       from the forward / bsm_bwd_prep
+ *   dq_acc          fp32 [S, Hq, d]    carried: a query tile's first step with
+ *                                      work overwrites, later steps add
+ *   dk, dv          fp32 [S, Hkv, d]   shard j's accumulators: this call ADDS
+ *                                      the rank's contribution (caller clears
+ *                                      them before the first contribution)
+ * With grouped heads, dk/dv of a key/value head sum over its query heads.
+ */
+int bsm_bwd_step(const bsm_dplan* dplan, int32_t s, const bsm_heads* heads,
+                 const void* q, const void* k, const void* v, const void* dout,
+                 const float* lse, const float* delta,
+                 float* dq_acc, float* dk, float* dv, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSM_H */

@@ -1,0 +1,215 @@
+"""GPU parity of the forward ring steps against the fp64 oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_masked_metadata_amd as bsm
+from workloads import (ring_toy, toy_qkv, random_small, packed_text, packed_multimodal,
+                       sliding_window, long_mixed)
+from oracle import attention as oatt
+from oracle.mask import legal, take
+from gpu_common import Case, O_TOL, LSE_TOL, max_err, needs_gpu
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not needs_gpu, reason="needs a GPU")]
+
+
+def _check_rows(case, o, lse, sel=None, tol_o=O_TOL, tol_lse=LSE_TOL):
+    """Compare GPU rows (indices into the rank's shard) with the oracle.
+
+    The O bar applies to the value the kernel rounds to bf16 (O_acc / l from a
+    KEEP_STATE run of the same steps); the bf16 output must be exactly that
+    value rounded to nearest even.  LSE is compared as written."""
+    sel = np.arange(case.S) if sel is None else np.asarray(sel)
+    q, k, v = case.cpu(0), case.cpu(1), case.cpu(2)
+    o_ref, lse_ref = oatt.forward_rows(case.lay.tracks(), case.lay.window, q, k, v,
+                                       case.rows[sel], 1.0 / np.sqrt(case.lay.d))
+    tsel = torch.from_numpy(sel).cuda()
+    _, _, (acc, m, l) = case.ring(keep_state=True)
+    acc = acc[tsel].cpu()
+    l = l[:, tsel].cpu().T[:, :, None]
+    o32 = torch.where(l > 0, acc / torch.where(l > 0, l, torch.ones_like(l)), torch.zeros_like(acc))
+    og = o[tsel].cpu()
+    assert torch.equal(og, o32.to(torch.bfloat16)), "bf16 O is not RNE(O_acc / l)"
+    lg = lse[:, tsel].cpu().numpy()
+    eo = max_err(o32.numpy(), o_ref)
+    eob = max_err(og.float().numpy(), o_ref)
+    el = max_err(lg, lse_ref)
+    print(f"  rows={len(sel)} max|dO32|={eo:.3e} max|dO_bf16|={eob:.3e} max|dLSE|={el:.3e}",
+          flush=True)
+    assert eo <= tol_o and el <= tol_lse
+    return eo, el
+
+
+def test_ring_toy():
+    """The NumPy page's 16-token, 4-rank toy: inputs rounded to bf16 and the
+    head dim zero-padded 8 -> 128 (exact), scale 1/sqrt(8), every rank."""
+    lay = ring_toy()
+    q8, k8, v8 = toy_qkv()
+    pad = lambda x: torch.nn.functional.pad(torch.from_numpy(x), (0, 120)).to(torch.bfloat16)[:, None, :]
+    t = tuple(pad(x).cuda() for x in (q8, k8, v8))
+    for r in range(4):
+        case = Case(lay, rank=r, tensors=t)
+        o, lse, _ = case.ring()
+        torch.cuda.synchronize()
+        _check_rows(case, o, lse)
+        assert torch.all(o[:, :, 8:] == 0)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_layouts_all_modes(seed):
+    rng = np.random.default_rng(900 + seed)
+    ranks = [1, 2, 4, 3, 8, 2][seed]
+    order = ["ptrr", "contiguous"][seed % 2]
+    n = 128 * ranks * [2, 3, 1, 2, 1, 4][seed]
+    lay = random_small(rng, n, max_span=300)
+    lay.ranks, lay.order, lay.seed = ranks, order, 40 + seed
+    lay.hq, lay.hkv = [(4, 2), (2, 2), (8, 1), (4, 4), (6, 3), (2, 1)][seed]
+    lay.d = 128
+    for r in range(ranks):
+        case = Case(lay, rank=r)
+        o, lse, _ = case.ring()
+        torch.cuda.synchronize()
+        _check_rows(case, o, lse)
+
+
+def test_packed_text_full_share():
+    case = Case(packed_text())
+    o, lse, _ = case.ring()
+    torch.cuda.synchronize()
+    _check_rows(case, o, lse)
+
+
+def test_packed_multimodal_full_share():
+    case = Case(packed_multimodal())
+    o, lse, _ = case.ring()
+    torch.cuda.synchronize()
+    _check_rows(case, o, lse)
+
+
+def test_sliding_window_full_size_sampled():
+    case = Case(sliding_window())
+    o, lse, _ = case.ring()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    sel = np.concatenate([np.arange(0, 4200, 97), rng.choice(case.S, 200, replace=False)])
+    _check_rows(case, o, lse, np.unique(sel))
+
+
+def test_long_mixed_full_size_sampled():
+    case = Case(long_mixed())
+    o, lse, _ = case.ring()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(2)
+    _check_rows(case, o, lse, np.sort(rng.choice(case.S, 256, replace=False)))
+
+
+def test_ring_equals_single_bitwise():
+    """The carried fp32 state makes the ring equal the single pass exactly
+    (MARBLE section 03: ring output equals a single GPU's)."""
+    for lay in (packed_multimodal(), packed_text()):
+        case = Case(lay)
+        _, _, st_ring = case.ring(keep_state=True)
+        st_single = case.single(keep_state=True)
+        o1, l1, _ = case.ring()
+        o2, l2 = case.single()
+        torch.cuda.synchronize()
+        for a, b in zip(st_ring, st_single):
+            assert torch.equal(a, b)
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_state_host_round_trip_resume():
+    """Stop after 4 steps, move the state to the host, free it, upload it into
+    fresh buffers and finish: bitwise equal to the uninterrupted ring.  (Tiles
+    whose last step is early write O/LSE during the first half, so both halves
+    share the output buffers.)"""
+    case = Case(packed_multimodal())
+    o_ref, l_ref, _ = case.ring()
+    o = torch.full_like(o_ref, float("nan"))
+    l = torch.full_like(l_ref, float("nan"))
+    _, _, st = case.ring(steps=range(4), out=(o, l))
+    host = [t.cpu() for t in st]
+    del st
+    torch.cuda.empty_cache()
+    st2 = tuple(t.cuda() for t in host)
+    case.ring(steps=range(4, 8), state=st2, out=(o, l))
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(l, l_ref)
+
+
+def test_unit_values_and_zero_queries():
+    """V = 1 gives O = 1; Q = 0 gives LSE = ln(#legal keys) per row, where the
+    count is the mask's, and O = mean of the legal values."""
+    lay = packed_multimodal()
+    base = Case(lay)
+    q0 = torch.zeros_like(base.full[0])
+    ones = torch.ones_like(base.full[2])
+    case = Case(lay, tensors=(base.full[0], base.full[1], ones))
+    o, lse, _ = case.ring()
+    torch.cuda.synchronize()
+    assert float((o.float() - 1).abs().max()) <= 1e-2
+    case = Case(lay, tensors=(q0, base.full[1], base.full[2]))
+    o, lse, _ = case.ring()
+    torch.cuda.synchronize()
+    sel = np.arange(0, case.S, 37)
+    cnt = oatt.legal_counts(lay.tracks(), lay.window, case.rows[sel])
+    lg = lse[:, torch.from_numpy(sel).cuda()].cpu().numpy()
+    np.testing.assert_allclose(lg, np.broadcast_to(np.log(cnt), lg.shape), rtol=2e-6)
+    _check_rows(case, o, lse, sel)
+
+
+def test_sample_isolation_exact():
+    """V = 1 on one sample and 0 elsewhere: rows of other samples get exactly 0;
+    perturbing other samples' K/V leaves the sample's rows bitwise unchanged."""
+    lay = packed_text()
+    base = Case(lay)
+    smp = torch.from_numpy(lay.sample.astype(np.int64)).cuda()
+    target = int(lay.sample[base.rows[0]])
+    vsel = torch.where((smp == target)[:, None, None], 1.0, 0.0).to(torch.bfloat16)
+    vsel = vsel.expand_as(base.full[2]).contiguous()
+    case = Case(lay, tensors=(base.full[0], base.full[1], vsel))
+    o, _, _ = case.ring()
+    torch.cuda.synchronize()
+    mine = torch.from_numpy(lay.sample[case.rows] == target).cuda()
+    assert torch.all(o[~mine] == 0)
+    o_ref, l_ref, _ = base.ring()
+    k2 = base.full[1].clone()
+    v2 = base.full[2].clone()
+    other = (smp != target)
+    k2[other] = k2[other] * 3 + 1
+    v2[other] = -v2[other]
+    pert = Case(lay, tensors=(base.full[0], k2, v2))
+    o2, l2, _ = pert.ring()
+    torch.cuda.synchronize()
+    assert torch.equal(o2[mine], o_ref[mine]) and torch.equal(l2[:, mine], l_ref[:, mine])
+
+
+def test_layout_invariance_ptrr_vs_contiguous():
+    """Same keys per query in either token order: outputs agree per original token."""
+    lay = packed_text()
+    a = Case(lay)
+    lay_c = packed_text()
+    lay_c.order = "contiguous"
+    outs = {}
+    for c in [a] + [Case(lay_c, rank=r, tensors=a.full) for r in range(lay.ranks)]:
+        o, lse, _ = c.ring()
+        torch.cuda.synchronize()
+        for i, t in enumerate(c.rows[:: 61]):
+            outs.setdefault(int(t), []).append(o[i * 61].float().cpu())
+    for t, vals in outs.items():
+        for v in vals[1:]:
+            assert float((v - vals[0]).abs().max()) <= 1e-2
+
+
+def test_fwd_errors_before_launch():
+    case = Case(packed_text())
+    C = bsm._capi
+    hd = bsm.heads(32, 8, 64)
+    with pytest.raises(bsm.BsmError) as e:
+        C.bsm_fwd_single(case.dp.handle, hd, case.q.data_ptr(), case.k_all.data_ptr(),
+                         case.v_all.data_ptr(), None, None, None, case.q.data_ptr(),
+                         case.q.data_ptr(), 0, None)
+    assert e.value.code == C.BSM_E_UNSUPPORTED
+    with pytest.raises(bsm.BsmError) as e:
+        C.bsm_fwd_step(case.dp.handle, 99, case.heads, 1, 1, 1, 1, 1, 1, 1, 1, 0, None)
+    assert e.value.code == C.BSM_E_INVALID

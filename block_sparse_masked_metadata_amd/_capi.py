@@ -13,7 +13,7 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libbsm.so")
+LIB_PATH = os.environ.get("BSM_LIB") or os.path.join(_HERE, "libbsm.so")  # BSM_LIB: alternate build
 
 # PyTorch-ROCm ships its own HIP runtime (same SONAME as the system one).  Load
 # torch first so that libbsm binds to the runtime already in the process; two

@@ -39,8 +39,6 @@ typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
 typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s16x8;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-constexpr int KLD = 136;  // K tile row stride in LDS, bf16 elements (272 B)
-constexpr int VLD = 160;  // V tile row stride in LDS, bf16 elements (320 B)
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.693147180559945309f;
 
@@ -79,10 +77,80 @@ __device__ inline void map_block(int32_t b, int32_t nitems, int32_t hq, int32_t 
   if (item >= nitems) item = -1;
 }
 
+// ---- LDS sub-tiles: 64 key rows x 256 B, unpadded, 16-byte chunks XOR-swizzled ----
+// K: chunk c of row r sits in slot c ^ (r & 15), so the MFMA A-operand reads
+//    (one chunk of 16 consecutive rows per 16 lanes) hit 16 distinct slots.
+// V: chunk c of row r sits in slot c ^ 4(r & 3), so each transpose read
+//    (4 rows x 4 chunks per 32 lanes) hits 16 distinct slots.
+__device__ inline int k_slot(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
+__device__ inline int v_slot(int r, int c) { return r * 256 + ((c ^ ((r & 3) << 2)) << 4); }
+
+constexpr int kSub = 64;             // keys per sub-tile (half of a listed 128-key tile)
+constexpr int kListCache = 512;      // list entries of an item kept in LDS
+constexpr float kRescaleGap = 8.0f;  // base-2 units: the reference max may lag by 2^8
+
+// One sub-tile of K, V (and key tracks) staged through registers: thread t
+// holds chunk t%16 of rows t/16 + 16i (i = 0..3), so every 16 lanes read one
+// 256-byte row contiguously.  Rows past `len` are zero.
+struct SubTile {
+  uint4 k[4], v[4];
+  int4 kt;
+};
+
+// kbytes/vbytes: uniform base addresses; byte offsets stay below 2^32 (a key
+// buffer holds fewer than 2^32 bytes: at most 2^30 rows of one head group).
+__device__ inline void fetch_sub(SubTile& t, const char* kbytes, const char* vbytes,
+                                 const int4* ktracks, int64_t k0, int len, bool partial,
+                                 uint32_t row_bytes, int tid) {
+  t.kt = make_int4(-1, -1, -1, 0);
+  if (partial && tid < len) t.kt = ktracks[k0 + tid];
+  const uint32_t off = (uint32_t)(k0 + (tid >> 4)) * row_bytes + (uint32_t)(tid & 15) * 16u;
+  if (len == kSub) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      t.k[i] = *(const uint4*)(kbytes + (off + 16u * i * row_bytes));
+      t.v[i] = *(const uint4*)(vbytes + (off + 16u * i * row_bytes));
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = (tid >> 4) + 16 * i;
+      t.k[i] = make_uint4(0, 0, 0, 0);
+      t.v[i] = make_uint4(0, 0, 0, 0);
+      if (row < len) {
+        t.k[i] = *(const uint4*)(kbytes + (off + 16u * i * row_bytes));
+        t.v[i] = *(const uint4*)(vbytes + (off + 16u * i * row_bytes));
+      }
+    }
+  }
+}
+
+__device__ inline void store_sub(const SubTile& t, char* sK, char* sV, int4* sKT, int tid) {
+  const int c = tid & 15;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = (tid >> 4) + 16 * i;
+    *(uint4*)(sK + k_slot(row, c)) = t.k[i];
+    *(uint4*)(sV + v_slot(row, c)) = t.v[i];
+  }
+  if (tid < kSub) sKT[tid] = t.kt;
+}
+
+// Sub-tile n of an item: half n%2 of list entry n/2.
+__device__ inline void sub_bounds(const int2 ent, int n, int64_t& k0, int& len, bool& partial) {
+  const int half = n & 1;
+  const int klen = ent.y & 0xffff;
+  k0 = (int64_t)ent.x + half * kSub;
+  len = klen - half * kSub;
+  len = len < 0 ? 0 : (len > kSub ? kSub : len);
+  partial = (ent.y & kPartialBit) != 0;
+}
+
 __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned short sK[kTile * KLD];
-  __shared__ __attribute__((aligned(16))) unsigned short sV[kTile * VLD];
-  __shared__ int4 sKT[kTile];
+  __shared__ __attribute__((aligned(1024))) char sK[kSub * 256];
+  __shared__ __attribute__((aligned(1024))) char sV[kSub * 256];
+  __shared__ int4 sKT[kSub];
+  __shared__ int2 sEnt[kListCache];
 
   int32_t item, h;
   map_block((int32_t)blockIdx.x, a.nitems, a.hq, a.heads_per_xcd, item, h);
@@ -90,12 +158,30 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a) {
   const int4 it = a.items[item];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // the item's list goes to LDS in chunks of kListCache entries, so the loop
+  // never waits on a memory load for it
+  for (int i = tid; i < it.w && i < kListCache; i += 256) sEnt[i] = a.entries[it.z + i];
   const int l32 = lane & 31, hi = lane >> 5;
   const int64_t q0 = (int64_t)it.x * kTile;
   const int64_t qi = wave * 32 + l32;
   const bool qvalid = q0 + qi < a.rows;
   const int64_t qrow = q0 + qi;
   const int32_t kvh = h / (a.hq / a.hkv);
+  const uint32_t row_bytes = (uint32_t)a.hkv * kHeadDim * 2u;
+  const char* kbase = (const char*)(a.k + (int64_t)kvh * kHeadDim);
+  const char* vbase = (const char*)(a.v + (int64_t)kvh * kHeadDim);
+  const int nsub = 2 * it.w;
+
+  // prologue: fetch the first sub-tile, then Q and the state
+  SubTile pf;
+  int2 ent = a.entries[it.z];
+  {
+    int64_t k0;
+    int len;
+    bool part;
+    sub_bounds(ent, 0, k0, len, part);
+    fetch_sub(pf, kbase, vbase, a.ktracks, k0, len, part, row_bytes, tid);
+  }
 
   // Q^T as the B operand: lane holds query l32, channels [16kk + 8hi, +8).
   bf16x8 qf[8];
@@ -107,9 +193,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a) {
   }
   const int4 qt = qvalid ? a.qtracks[qrow] : make_int4(0, -1, -1, 0);
 
-  // Running state.  acc[db][r] = O^T[d = 32db + 8(r/4) + 4hi + r%4][query l32].
+  // Running state.  acc[db][r] = O^T[d = 32db + 8(r/4) + 4hi + r%4][query l32];
+  // mref is the base-2 reference the accumulator and l are scaled against.
   f32x16 acc[4];
-  float mrun = kNegInf, lrun = 0.f;
+  float mref = kNegInf, lrun = 0.f;
   const int64_t sidx = (int64_t)h * a.rows + qrow;
   float* op = a.oacc + (qrow * a.hq + h) * kHeadDim;
 #pragma unroll
@@ -117,7 +204,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
   if (!(it.y & kFirst) && qvalid) {
-    mrun = a.m[sidx];
+    mref = a.m[sidx];
     lrun = a.l[sidx];
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -130,110 +217,121 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a) {
         acc[db][4 * i + 3] = v4.w;
       }
   }
+  store_sub(pf, sK, sV, sKT, tid);
+  // Drain every prologue load here, once: a register loaded before the loop
+  // with a load still pending would make each iteration's first use of it
+  // wait on the memory counter, i.e. on the in-flight prefetch as well.
+  __builtin_amdgcn_s_waitcnt(0);
 
-  const int64_t kstride = (int64_t)a.hkv * kHeadDim;  // elements between key rows
-  const unsigned short* kbase = (const unsigned short*)a.k + (int64_t)kvh * kHeadDim;
-  const unsigned short* vbase = (const unsigned short*)a.v + (int64_t)kvh * kHeadDim;
-
-  // lane constants of the transpose reads (see the header comment)
+  // lane constants of the V transpose reads
   const int G = lane >> 4, jl = lane & 15;
   const int tr_row0 = 4 * (G >> 1) + (jl >> 2);
-  const int tr_col = 16 * (G & 1) + 4 * (jl & 3);
+  const int tr_chunk = 2 * (G & 1) + ((jl & 3) >> 1);  // + 4 db
+  const int tr_off8 = (jl & 1) * 8;
 
-  for (int e = 0; e < it.w; ++e) {
-    const int2 ent = a.entries[it.z + e];
-    const int64_t k0 = ent.x;
-    const int klen = ent.y & 0xffff;
-    const bool partial = (ent.y & kPartialBit) != 0;
-
-    __syncthreads();  // previous tile's LDS readers are done
-    {
-      uint4 kv[8], vv[8];
-      const int ch = tid & 15;
-#pragma unroll
-      for (int rd = 0; rd < 8; ++rd) {
-        const int row = rd * 16 + (tid >> 4);
-        kv[rd] = make_uint4(0, 0, 0, 0);
-        vv[rd] = make_uint4(0, 0, 0, 0);
-        if (row < klen) {
-          kv[rd] = *(const uint4*)(kbase + (k0 + row) * kstride + ch * 8);
-          vv[rd] = *(const uint4*)(vbase + (k0 + row) * kstride + ch * 8);
+  for (int n = 0; n < nsub; ++n) {
+    int64_t k0;
+    int len;
+    bool partial;
+    sub_bounds(ent, n, k0, len, partial);
+    __syncthreads();  // sub-tile n is in LDS
+    const bool more = n + 1 < nsub;
+    if (more) {
+      if (n & 1) {
+        const int e1 = (n + 1) >> 1;
+        if (e1 % kListCache == 0) {  // next chunk of the list (long lists only)
+          for (int i = tid; i < kListCache && e1 + i < it.w; i += 256) sEnt[i] = a.entries[it.z + e1 + i];
+          __syncthreads();
         }
+        ent = sEnt[e1 % kListCache];
       }
-#pragma unroll
-      for (int rd = 0; rd < 8; ++rd) {
-        const int row = rd * 16 + (tid >> 4);
-        *(uint4*)(sK + row * KLD + ch * 8) = kv[rd];
-        *(uint4*)(sV + row * VLD + ch * 8) = vv[rd];
-      }
-      if (partial && tid < kTile)
-        sKT[tid] = tid < klen ? a.ktracks[k0 + tid] : make_int4(-1, -1, -1, 0);
+      int64_t nk0;
+      int nlen;
+      bool npart;
+      sub_bounds(ent, n + 1, nk0, nlen, npart);
+      fetch_sub(pf, kbase, vbase, a.ktracks, nk0, nlen, npart, row_bytes, tid);
     }
-    __syncthreads();
 
     // S^T = K Q^T: s[kb][r] = S[query l32][key 32kb + 8(r/4) + 4hi + r%4]
-    f32x16 s[4];
+    // (operand reads are issued 4 at a time ahead of their MFMAs)
+    f32x16 s[2];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-      const unsigned short* kr = sK + (kb * 32 + l32) * KLD + hi * 8;
+      const int row = kb * 32 + l32;
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const bf16x8 kf = as_bf16x8(*(const uint4*)(kr + kk * 16));
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s[kb], 0, 0, 0);
+      for (int g = 0; g < 2; ++g) {
+        bf16x8 kf[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) kf[kk] = as_bf16x8(*(const uint4*)(sK + k_slot(row, 2 * (4 * g + kk) + hi)));
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // 4 LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // then 4 MFMAs
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[4 * g + kk], s[kb], 0, 0, 0);
       }
     }
+    if (partial) {  // mask before the max: -inf never wins it
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+          if (!(key < len && legal(qt, sKT[key], a.window))) s[kb][r] = kNegInf;
+        }
+    }
 
+    // online softmax in base-2 units against a lazily updated reference
     float mx = kNegInf;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = s[kb][r] * a.scale_log2;
-        if (partial) {
-          const int key = kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (!(key < klen && legal(qt, sKT[key], a.window))) x = kNegInf;
-        }
-        s[kb][r] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = fmaxf(mrun, mx);
-    const float base = (mnew == kNegInf) ? 0.f : mnew;
-    const float alpha = __builtin_amdgcn_exp2f(mrun - base);
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
+    if (__any(mx > mref + kRescaleGap)) {
+      const float mnew = mx > mref + kRescaleGap ? mx : mref;
+      // 1 when this row's reference stays (also when it is still -inf), 0 from -inf
+      const float alpha = mnew == mref ? 1.f : __builtin_amdgcn_exp2f(mref - mnew);
+      lrun *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+      mref = mnew;
+    }
+    const float nbase = (mref == kNegInf) ? 0.f : -mref;
     float ls = 0.f;
+    bf16x8 pb[4];  // P^T as the B operand of 4 MFMAs of 16 keys each
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(s[kb][r] - base);
-        s[kb][r] = p;
+      for (int i = 0; i < 8; ++i) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t >> 1][8 * (t & 1) + i], a.scale_log2, nbase));
         ls += p;
+        pb[t][i] = (__bf16)p;
       }
     ls += __shfl_xor(ls, 32);
-    lrun = lrun * alpha + ls;
-    mrun = mnew;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+    lrun += ls;
 
-    // O^T += V^T P^T, 16 keys per MFMA
+    // O^T += V^T P^T, 16 keys per MFMA (the 4 operand reads of a key group first)
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int kb = t >> 1, hf = t & 1;
-      bf16x8 pb;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) pb[i] = (__bf16)s[kb][8 * hf + i];
-      const unsigned short* v0 = sV + (kb * 32 + 16 * hf + tr_row0) * VLD + tr_col;
-      const unsigned short* v1 = v0 + 8 * VLD;
+    for (int t = 0; t < 4; ++t) {
+      const int r0 = 16 * t + tr_row0;
+      bf16x8 vf[4];
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const bf16x8 vf = lds_tr8(v0 + db * 32, v1 + db * 32);
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, acc[db], 0, 0, 0);
+        const char* p0 = sV + v_slot(r0, 4 * db + tr_chunk) + tr_off8;
+        const char* p1 = sV + v_slot(r0 + 8, 4 * db + tr_chunk) + tr_off8;
+        vf[db] = lds_tr8((const unsigned short*)p0, (const unsigned short*)p1);
       }
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);  // 8 transpose reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);  // then 4 MFMAs
+#pragma unroll
+      for (int db = 0; db < 4; ++db) acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], pb[t], acc[db], 0, 0, 0);
     }
+    __syncthreads();  // every wave is done with sub-tile n
+    if (more) store_sub(pf, sK, sV, sKT, tid);
   }
 
   if (!qvalid) return;
@@ -245,7 +343,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a) {
         *(float4*)(op + db * 32 + i * 8 + hi * 4) =
             make_float4(acc[db][4 * i], acc[db][4 * i + 1], acc[db][4 * i + 2], acc[db][4 * i + 3]);
     if (hi == 0) {
-      a.m[sidx] = mrun;
+      a.m[sidx] = mref;
       a.l[sidx] = lrun;
     }
   } else {
@@ -261,7 +359,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a) {
         for (int c = 0; c < 4; ++c) b4[c] = (__bf16)(any ? acc[db][4 * i + c] / lrun : 0.f);
         *(uint2*)(out + db * 32 + i * 8 + hi * 4) = __builtin_bit_cast(uint2, b4);
       }
-    if (hi == 0) a.lse[sidx] = lrun > 0.f ? (mrun + __log2f(lrun)) * kLn2 : kNegInf;
+    if (hi == 0) a.lse[sidx] = any ? (mref + __log2f(lrun)) * kLn2 : kNegInf;
   }
 }
 

@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU seconds of the oracle baseline sample")
     ap.add_argument("--fwd-only", action="store_true", help="time only the forward pass")
+    ap.add_argument("--single", action="store_true",
+                    help="diagnostic: time the one-launch single pass instead of the ring steps")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
     return ap.parse_args()
@@ -123,6 +125,15 @@ def main():
     do_bwd = not args.fwd_only
 
     def forward(events=None):
+        if args.single:
+            if events is not None:
+                events.append(torch.cuda.Event(enable_timing=True))
+                events[-1].record()
+            bsm.fwd_single(dp, hd, q, k_all, v_all, out=(o, lse))
+            if events is not None:
+                events.append(torch.cuda.Event(enable_timing=True))
+                events[-1].record()
+            return
         for s in fwd_steps:
             j = (r - s) % R
             if events is not None:
@@ -171,7 +182,7 @@ def main():
     fwd_flops = 4 * d * lay.hq * total_pairs
     bwd_flops = 10 * d * lay.hq * total_pairs
     fwd_tflops = fwd_flops / (fwd_ms * 1e-3) / 1e12
-    per_launch_flops = fwd_flops / len(fwd_steps)
+    per_launch_flops = fwd_flops / (1 if args.single else len(fwd_steps))
     achieved = per_launch_flops / (avg_launch_ms * 1e-3) / 1e12
 
     if args.copy_mib:
@@ -210,7 +221,8 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
                      "avg_launch_us": round(avg_launch_ms * 1e3, 2),
-                     "launches_per_step": len(fwd_steps)},
+                     "launches_per_step": 1 if args.single else len(fwd_steps)},
+        "mode": "single-pass diagnostic" if args.single else "ring",
         "planner_s": round(plan_s, 4),
         "wall_s": round(wall, 3),
     }

@@ -87,7 +87,7 @@ __device__ inline int v_slot(int r, int c) { return r * 256 + ((c ^ ((r & 3) << 
 
 constexpr int kSub = 64;             // keys per sub-tile (half of a listed 128-key tile)
 constexpr int kListCache = 512;      // list entries of an item kept in LDS
-constexpr float kRescaleGap = 8.0f;  // base-2 units: the reference max may lag by 2^8
+constexpr float kSumCap = 4096.0f;   // a lane sum below 2^12 keeps every p below 2^12
 
 // One sub-tile of K, V (and key tracks) staged through registers: thread t
 // holds chunk t%16 of rows t/16 + 16i (i = 0..3), so every 16 lanes read one
@@ -144,6 +144,55 @@ __device__ inline void sub_bounds(const int2 ent, int n, int64_t& k0, int& len, 
   len = klen - half * kSub;
   len = len < 0 ? 0 : (len > kSub ? kSub : len);
   partial = (ent.y & kPartialBit) != 0;
+}
+
+// S^T = K Q^T for one 64-key sub-tile: s[kb][r] = S[query l32][key 32kb + 8(r/4) + 4hi + r%4],
+// operand reads issued 4 at a time ahead of their MFMAs; on partial sub-tiles
+// illegal pairs (and keys past len) become -inf.
+__device__ inline void scores(f32x16 (&s)[2], const char* sK, const bf16x8 (&qf)[8], const int4* sKT,
+                              const int4 qt, bool partial, int len, int32_t window, int l32, int hi) {
+  __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+    const int row = kb * 32 + l32;
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      bf16x8 kf[4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) kf[kk] = as_bf16x8(*(const uint4*)(sK + k_slot(row, 2 * (4 * g + kk) + hi)));
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // 4 LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // then 4 MFMAs
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[4 * g + kk], s[kb], 0, 0, 0);
+    }
+  }
+  __builtin_amdgcn_s_setprio(0);
+  if (partial) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+        if (!(key < len && legal(qt, sKT[key], window))) s[kb][r] = kNegInf;
+      }
+  }
+}
+
+// p = 2^(s * scale_log2 + nbase) in place; returns the lane's sum of p.
+__device__ inline float exp_sum(f32x16 (&s)[2], float scale_log2, float nbase) {
+  float ls = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], scale_log2, nbase));
+      s[kb][r] = p;
+      ls += p;
+    }
+  return ls;
 }
 
 __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a) {
@@ -252,45 +301,33 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a) {
       fetch_sub(pf, kbase, vbase, a.ktracks, nk0, nlen, npart, row_bytes, tid);
     }
 
-    // S^T = K Q^T: s[kb][r] = S[query l32][key 32kb + 8(r/4) + 4hi + r%4]
-    // (operand reads are issued 4 at a time ahead of their MFMAs)
     f32x16 s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-      const int row = kb * 32 + l32;
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        bf16x8 kf[4];
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) kf[kk] = as_bf16x8(*(const uint4*)(sK + k_slot(row, 2 * (4 * g + kk) + hi)));
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // 4 LDS reads
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // then 4 MFMAs
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[4 * g + kk], s[kb], 0, 0, 0);
+    scores(s, sK, qf, sKT, qt, partial, len, a.window, l32, hi);
+
+    // Online softmax in base-2 units against a lazily updated reference mref.
+    // Common case: exponentiate against the current reference; every p stays
+    // below 2^12 whenever the lane's sum does, and then nothing moves.  When a
+    // row has no reference yet, or a lane's sum reaches 2^12 (the scores are
+    // then recomputed: K is still in LDS), the wave takes the tile's row
+    // maxima, moves the references and rescales O_acc and l.  Exact either
+    // way: O_acc and l always share one reference.
+    float ls;
+    bool fast = !__any(mref == kNegInf);
+    if (fast) {
+      ls = exp_sum(s, a.scale_log2, -mref);
+      if (__any(!(ls < kSumCap))) {
+        fast = false;
+        scores(s, sK, qf, sKT, qt, partial, len, a.window, l32, hi);
       }
     }
-    if (partial) {  // mask before the max: -inf never wins it
+    if (!fast) {
+      float mx = kNegInf;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (!(key < len && legal(qt, sKT[key], a.window))) s[kb][r] = kNegInf;
-        }
-    }
-
-    // online softmax in base-2 units against a lazily updated reference
-    float mx = kNegInf;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
-    if (__any(mx > mref + kRescaleGap)) {
-      const float mnew = mx > mref + kRescaleGap ? mx : mref;
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
+      const float mnew = fmaxf(mref, mx);
       // 1 when this row's reference stays (also when it is still -inf), 0 from -inf
       const float alpha = mnew == mref ? 1.f : __builtin_amdgcn_exp2f(mref - mnew);
       lrun *= alpha;
@@ -299,22 +336,18 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
       mref = mnew;
+      ls = exp_sum(s, a.scale_log2, mref == kNegInf ? 0.f : -mref);
     }
-    const float nbase = (mref == kNegInf) ? 0.f : -mref;
-    float ls = 0.f;
+    ls += __shfl_xor(ls, 32);
+    lrun += ls;
     bf16x8 pb[4];  // P^T as the B operand of 4 MFMAs of 16 keys each
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t >> 1][8 * (t & 1) + i], a.scale_log2, nbase));
-        ls += p;
-        pb[t][i] = (__bf16)p;
-      }
-    ls += __shfl_xor(ls, 32);
-    lrun += ls;
+      for (int i = 0; i < 8; ++i) pb[t][i] = (__bf16)s[t >> 1][8 * (t & 1) + i];
 
     // O^T += V^T P^T, 16 keys per MFMA (the 4 operand reads of a key group first)
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int r0 = 16 * t + tr_row0;
@@ -330,6 +363,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], pb[t], acc[db], 0, 0, 0);
     }
+    __builtin_amdgcn_s_setprio(0);
     __syncthreads();  // every wave is done with sub-tile n
     if (more) store_sub(pf, sK, sV, sKT, tid);
   }

@@ -10,82 +10,70 @@
 //   dQ_i += scale * dS_ij k_j,  dK_j += scale * dS_ij q_i,  dV_j += P_ij dO_i
 // (D_i = dO_i . O_i from the prep kernel).  Two deterministic kernels:
 //   dq   : one workgroup per (query tile, query head), walking the tile's row
-//          list; S^T and dP^T put one query per lane, so LSE_i and D_i are
-//          lane scalars; dQ^T += K^T dS^T reads K^T with the LDS transpose
-//          read.
+//          list in 64-key sub-tiles (the next one prefetched into registers);
+//          S^T and dP^T put one query per lane, so LSE_i and D_i are lane
+//          scalars; dQ^T += K^T dS^T reads K^T with the LDS transpose read.
 //   dkdv : one workgroup per (key tile, key/value head), walking the tile's
-//          column list and every query head of the group; S and dP put one
-//          key per lane; dV^T += dO^T P and dK^T += Q^T dS read dO^T and Q^T
-//          with the LDS transpose read.  K and V rows stay in registers.
+//          column list for every query head of the group in 64-query
+//          sub-tiles; S and dP put one key per lane; dV^T += dO^T P and
+//          dK^T += Q^T dS read dO^T and Q^T with the LDS transpose read.  K
+//          and V rows and both accumulators stay in registers (one wave per
+//          SIMD).
 
-#include "kernels.hpp"
+#include "tile_common.hpp"
 
 namespace bsm {
 namespace {
 
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
-typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
-typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s16x8;
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+using namespace dev;
 
-constexpr int LD = 136;  // LDS row stride of a staged 128x128 tile (bf16 elements)
-constexpr float kLog2e = 1.44269504088896340736f;
-constexpr float kInf = __builtin_inff();
+constexpr int kListCache = 512;  // list entries of an item kept in LDS at a time
 
-__device__ inline bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
-
-__device__ inline bf16x8 lds_tr8(const unsigned short* p0, const unsigned short* p1) {
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p1);
-  const s16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, both);
-}
-
-__device__ inline bool legal(const int4 q, const int4 k, int32_t window) {
-  const int32_t d = q.w - k.w;
-  const bool causal = (d >= 0) & (d < window);
-  const bool span = (q.y == k.y) & (k.y >= 0);
-  const bool keep = (k.z < 0) | (q.z == k.z);
-  return (causal | span) & keep & (q.x == k.x);
-}
-
-__device__ inline void map_block(int32_t b, int32_t nitems, int32_t heads, int32_t hpx,
-                                 int32_t& item, int32_t& h) {
-  if (hpx > 0) {
-    const int32_t x = b & 7, i = b >> 3;
-    item = i / hpx;
-    h = x * hpx + i % hpx;
-  } else {
-    item = b / heads;
-    h = b % heads;
+// Entry e of an item's list through an LDS window of kListCache entries.
+// Called by all threads at the same point right after a __syncthreads();
+// reloads the window (with its own barrier) when e falls outside it.
+__device__ inline int2 list_entry(int2* sEnt, int& base, const int2* entries, int4 it, int e, int tid) {
+  if (e < base || e >= base + kListCache) {
+    base = e - e % kListCache;
+    for (int i = tid; i < kListCache && base + i < it.w; i += 256) sEnt[i] = entries[it.z + base + i];
+    __syncthreads();
   }
-  if (item >= nitems) item = -1;
+  return sEnt[e - base];
 }
 
-// Stage rows [r0, r0+len) of a [rows, H, 128] bf16 tensor (head h) into a
-// padded LDS tile; rows >= len are zero.
-__device__ inline void stage_tile(unsigned short* dst, const unsigned short* src, int64_t r0,
-                                  int len, int64_t row_stride, int tid) {
-  uint4 v[8];
-  const int ch = tid & 15;
+// s += A_rows(tileA) . b1 and dp += A_rows(tileB) . b2 over the 128 channels:
+// row `row` of two staged tiles against two register operands, with the LDS
+// operand reads issued 4 at a time ahead of their MFMAs.
+__device__ inline void two_products(f32x16& s, f32x16& dp, const char* ta, const char* tb, int row,
+                                    const bf16x8 (&b1)[8], const bf16x8 (&b2)[8], int hi) {
 #pragma unroll
-  for (int rd = 0; rd < 8; ++rd) {
-    const int row = rd * 16 + (tid >> 4);
-    v[rd] = make_uint4(0, 0, 0, 0);
-    if (row < len) v[rd] = *(const uint4*)(src + (r0 + row) * row_stride + ch * 8);
+  for (int r = 0; r < 16; ++r) {
+    s[r] = 0.f;
+    dp[r] = 0.f;
   }
 #pragma unroll
-  for (int rd = 0; rd < 8; ++rd) {
-    const int row = rd * 16 + (tid >> 4);
-    *(uint4*)(dst + row * LD + ch * 8) = v[rd];
+  for (int g = 0; g < 4; ++g) {
+    bf16x8 x[2], y[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      x[k] = row_operand(ta, row, 2 * g + k, hi);
+      y[k] = row_operand(tb, row, 2 * g + k, hi);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // 4 LDS reads
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // then 4 MFMAs
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      s = mfma(x[k], b1[2 * g + k], s);
+      dp = mfma(y[k], b2[2 * g + k], dp);
+    }
   }
 }
 
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned short sK[kTile * LD];
-  __shared__ __attribute__((aligned(16))) unsigned short sV[kTile * LD];
-  __shared__ int4 sKT[kTile];
+  __shared__ __attribute__((aligned(1024))) char sK[kSub * 256];
+  __shared__ __attribute__((aligned(1024))) char sV[kSub * 256];
+  __shared__ int4 sKT[kSub];
+  __shared__ int2 sEnt[kListCache];
 
   int32_t item, h;
   map_block((int32_t)blockIdx.x, a.nitems, a.hq, a.heads_per_xcd, item, h);
@@ -96,7 +84,26 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
   const int64_t qrow = (int64_t)it.x * kTile + wave * 32 + l32;
   const bool qvalid = qrow < a.rows;
   const int32_t kvh = h / (a.hq / a.hkv);
+  const uint32_t row_bytes = (uint32_t)a.hkv * kHeadDim * 2u;
+  const char* kbase = (const char*)(a.k + (int64_t)kvh * kHeadDim);
+  const char* vbase = (const char*)(a.v + (int64_t)kvh * kHeadDim);
+  const int nsub = 2 * it.w;
 
+  for (int i = tid; i < it.w && i < kListCache; i += 256) sEnt[i] = a.entries[it.z + i];
+  int list_base = 0;
+
+  // prologue: first sub-tile, then Q, dO and the row scalars
+  PairStage pf;
+  int4 kt_pf = make_int4(-1, -1, -1, 0);
+  int2 ent = a.entries[it.z];
+  {
+    int64_t r0;
+    int len;
+    bool part;
+    sub_bounds(ent, 0, r0, len, part);
+    if (part && tid < len) kt_pf = a.ktracks[r0 + tid];
+    pf.fetch(kbase, vbase, r0, len, row_bytes, tid);
+  }
   bf16x8 qf[8], df[8];
   {
     const int64_t off = (qrow * a.hq + h) * kHeadDim + hi * 8;
@@ -109,77 +116,67 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
     }
   }
   const int64_t sidx = (int64_t)h * a.rows + qrow;
-  const float lse2 = qvalid ? a.lse[sidx] * kLog2e : kInf;
+  const float nlse2 = qvalid ? -a.lse[sidx] * kLog2e : kNegInf;  // invalid rows: p = 0
   const float dl = qvalid ? a.delta[sidx] : 0.f;
   const int4 qt = qvalid ? a.qtracks[qrow] : make_int4(0, -1, -1, 0);
 
-  f32x16 acc[4];
+  f32x16 acc[4];  // dQ^T[d = 32db + 8(r/4) + 4hi + r%4][query l32], unscaled
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+  pf.store(sK, sV, tid);
+  if (tid < kSub) sKT[tid] = kt_pf;
+  __builtin_amdgcn_s_waitcnt(0);  // no load is pending when the loop starts
+  const TrLane tr(lane);
 
-  const int64_t kstride = (int64_t)a.hkv * kHeadDim;
-  const unsigned short* kbase = (const unsigned short*)a.k + (int64_t)kvh * kHeadDim;
-  const unsigned short* vbase = (const unsigned short*)a.v + (int64_t)kvh * kHeadDim;
-  const int G = lane >> 4, jl = lane & 15;
-  const int tr_row0 = 4 * (G >> 1) + (jl >> 2);
-  const int tr_col = 16 * (G & 1) + 4 * (jl & 3);
-
-  for (int e = 0; e < it.w; ++e) {
-    const int2 ent = a.entries[it.z + e];
-    const int64_t k0 = ent.x;
-    const int klen = ent.y & 0xffff;
-    const bool partial = (ent.y & kPartialBit) != 0;
-    __syncthreads();
-    stage_tile(sK, kbase, k0, klen, kstride, tid);
-    stage_tile(sV, vbase, k0, klen, kstride, tid);
-    if (partial && tid < kTile) sKT[tid] = tid < klen ? a.ktracks[k0 + tid] : make_int4(-1, -1, -1, 0);
-    __syncthreads();
-
+  for (int n = 0; n < nsub; ++n) {
+    int64_t r0;
+    int len;
+    bool partial;
+    sub_bounds(ent, n, r0, len, partial);
+    __syncthreads();  // sub-tile n is in LDS
+    const bool more = n + 1 < nsub;
+    if (more) {
+      if (n & 1) ent = list_entry(sEnt, list_base, a.entries, it, (n + 1) >> 1, tid);
+      int64_t nr0;
+      int nlen;
+      bool npart;
+      sub_bounds(ent, n + 1, nr0, nlen, npart);
+      kt_pf = make_int4(-1, -1, -1, 0);
+      if (npart && tid < nlen) kt_pf = a.ktracks[nr0 + tid];
+      pf.fetch(kbase, vbase, nr0, nlen, row_bytes, tid);
+    }
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      f32x16 s[2], dp[2];
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        const int kb = 2 * half + k2;
+    for (int kc = 0; kc < 2; ++kc) {
+      f32x16 s, dp;
+      two_products(s, dp, sK, sV, kc * 32 + l32, qf, df, hi);
+      // s[r] = S[query l32][key 32kc + 8(r/4) + 4hi + r%4]
+      if (partial) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          s[k2][r] = 0.f;
-          dp[k2][r] = 0.f;
-        }
-        const unsigned short* kr = sK + (kb * 32 + l32) * LD + hi * 8;
-        const unsigned short* vr = sV + (kb * 32 + l32) * LD + hi * 8;
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-          s[k2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(*(const uint4*)(kr + kk * 16)), qf[kk], s[k2], 0, 0, 0);
-          dp[k2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(*(const uint4*)(vr + kk * 16)), df[kk], dp[k2], 0, 0, 0);
+          const int key = kc * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+          if (!(key < len && legal(qt, sKT[key], a.window))) s[r] = kNegInf;
         }
       }
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2)
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.scale_log2, nlse2));
+        dp[r] = p * (dp[r] - dl);
+      }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = (2 * half + k2) * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          bool ok = true;
-          if (partial) ok = key < klen && legal(qt, sKT[key], a.window);
-          const float p = ok ? __builtin_amdgcn_exp2f(s[k2][r] * a.scale_log2 - lse2) : 0.f;
-          dp[k2][r] = p * (dp[k2][r] - dl);
-        }
-      // dQ^T += K^T dS^T
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int k2 = t >> 1, hf = t & 1;
-        const int kb = 2 * half + k2;
+      for (int hf = 0; hf < 2; ++hf) {
         bf16x8 dsb;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) dsb[i] = (__bf16)dp[k2][8 * hf + i];
-        const unsigned short* k0p = sK + (kb * 32 + 16 * hf + tr_row0) * LD + tr_col;
-        const unsigned short* k1p = k0p + 8 * LD;
+        for (int i = 0; i < 8; ++i) dsb[i] = (__bf16)dp[8 * hf + i];
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_tr8(k0p + db * 32, k1p + db * 32), dsb, acc[db], 0, 0, 0);
+        for (int db = 0; db < 4; ++db) acc[db] = mfma(tr.read(sK, kc * 32 + 16 * hf, db), dsb, acc[db]);
       }
+    }
+    __syncthreads();  // every wave is done with sub-tile n
+    if (more) {
+      pf.store(sK, sV, tid);
+      if (tid < kSub) sKT[tid] = kt_pf;
     }
   }
 
@@ -200,12 +197,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
     }
 }
 
+// Row scalars and tracks of one 64-row query sub-tile, staged with Q and dO:
+// threads 0..63 carry -LSE*log2(e), 64..127 delta, 128..191 the query tracks.
+struct RowStage {
+  float v;
+  int4 t;
+};
+
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned short sQ[kTile * LD];
-  __shared__ __attribute__((aligned(16))) unsigned short sO[kTile * LD];
-  __shared__ float sL[kTile];
-  __shared__ float sD[kTile];
-  __shared__ int4 sQT[kTile];
+  __shared__ __attribute__((aligned(1024))) char sQ[kSub * 256];
+  __shared__ __attribute__((aligned(1024))) char sO[kSub * 256];
+  __shared__ __attribute__((aligned(16))) float sL[kSub];
+  __shared__ __attribute__((aligned(16))) float sD[kSub];
+  __shared__ int4 sQT[kSub];
+  __shared__ int2 sEnt[kListCache];
 
   int32_t item, g;
   map_block((int32_t)blockIdx.x, a.nitems, a.hkv, a.heads_per_xcd, item, g);
@@ -213,11 +218,49 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
   const int4 it = a.items[item];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, hi = lane >> 5;
-  const int kl = wave * 32 + l32;
-  const int64_t key = (int64_t)it.x * kTile + kl;
+  const int64_t key = (int64_t)it.x * kTile + wave * 32 + l32;
   const bool kvalid = key < a.krows;
   const int32_t grp = a.hq / a.hkv;
+  const uint32_t row_bytes = (uint32_t)a.hq * kHeadDim * 2u;
+  const int nsub = 2 * it.w;
+  const int total = grp * nsub;  // (query head of the group, sub-tile) pairs
 
+  for (int i = tid; i < it.w && i < kListCache; i += 256) sEnt[i] = a.entries[it.z + i];
+  int list_base = 0;
+
+  // Stage (head g*grp + m/nsub, sub-tile m%nsub) into registers.
+  PairStage pf;
+  RowStage rs;
+  int2 ent;
+  bool cur_partial = false, nxt_partial = false;
+  int cur_len = 0, nxt_len = 0;
+  auto fetch = [&](int m, int2 e2) {
+    const int32_t h = g * grp + m / nsub;
+    int64_t r0;
+    sub_bounds(e2, m % nsub, r0, nxt_len, nxt_partial);
+    rs.v = 0.f;
+    rs.t = make_int4(-2, -1, -1, 0);
+    if (tid < kSub) {
+      rs.v = tid < nxt_len ? -a.lse[(int64_t)h * a.rows + r0 + tid] * kLog2e : kNegInf;
+    } else if (tid < 2 * kSub) {
+      rs.v = tid - kSub < nxt_len ? a.delta[(int64_t)h * a.rows + r0 + tid - kSub] : 0.f;
+    } else if (tid < 3 * kSub) {
+      if (nxt_partial && tid - 2 * kSub < nxt_len) rs.t = a.qtracks[r0 + tid - 2 * kSub];
+    }
+    pf.fetch((const char*)(a.q + (int64_t)h * kHeadDim), (const char*)(a.dout + (int64_t)h * kHeadDim),
+             r0, nxt_len, row_bytes, tid);
+  };
+  auto stage = [&]() {
+    pf.store(sQ, sO, tid);
+    if (tid < kSub) sL[tid] = rs.v;
+    else if (tid < 2 * kSub) sD[tid - kSub] = rs.v;
+    else if (tid < 3 * kSub) sQT[tid - 2 * kSub] = rs.t;
+    cur_len = nxt_len;
+    cur_partial = nxt_partial;
+  };
+
+  ent = a.entries[it.z];
+  fetch(0, ent);
   bf16x8 kf[8], vf[8];
   {
     const int64_t off = (key * a.hkv + g) * kHeadDim + hi * 8;
@@ -230,8 +273,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
     }
   }
   const int4 kt = kvalid ? a.ktracks[key] : make_int4(-1, -1, -1, 0);
-
-  f32x16 dk[4], dv[4];
+  f32x16 dk[4], dv[4];  // dK^T / dV^T[d = 32db + 8(r/4) + 4hi + r%4][key]
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -239,76 +281,64 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
       dk[db][r] = 0.f;
       dv[db][r] = 0.f;
     }
+  stage();
+  __builtin_amdgcn_s_waitcnt(0);  // no load is pending when the loop starts
+  const TrLane tr(lane);
 
-  const int64_t qstride = (int64_t)a.hq * kHeadDim;
-  const int G = lane >> 4, jl = lane & 15;
-  const int tr_row0 = 4 * (G >> 1) + (jl >> 2);
-  const int tr_col = 16 * (G & 1) + 4 * (jl & 3);
-
-  for (int hh = 0; hh < grp; ++hh) {
-    const int32_t h = g * grp + hh;
-    const unsigned short* qbase = (const unsigned short*)a.q + (int64_t)h * kHeadDim;
-    const unsigned short* obase = (const unsigned short*)a.dout + (int64_t)h * kHeadDim;
-    for (int e = 0; e < it.w; ++e) {
-      const int2 ent = a.entries[it.z + e];
-      const int64_t q0 = ent.x;
-      const int qlen = ent.y & 0xffff;
-      const bool partial = (ent.y & kPartialBit) != 0;
-      __syncthreads();
-      stage_tile(sQ, qbase, q0, qlen, qstride, tid);
-      stage_tile(sO, obase, q0, qlen, qstride, tid);
-      if (tid < kTile) {
-        const bool ok = tid < qlen;
-        sL[tid] = ok ? a.lse[(int64_t)h * a.rows + q0 + tid] * kLog2e : kInf;
-        sD[tid] = ok ? a.delta[(int64_t)h * a.rows + q0 + tid] : 0.f;
-        if (partial) sQT[tid] = ok ? a.qtracks[q0 + tid] : make_int4(-2, -1, -1, 0);
-      }
-      __syncthreads();
-
+  for (int m = 0; m < total; ++m) {
+    const int len = cur_len;
+    const bool partial = cur_partial;
+    __syncthreads();  // sub-tile m is in LDS
+    const bool more = m + 1 < total;
+    if (more) {
+      const int n1 = (m + 1) % nsub;
+      if ((n1 & 1) == 0) ent = list_entry(sEnt, list_base, a.entries, it, n1 >> 1, tid);
+      fetch(m + 1, ent);
+    }
 #pragma unroll
-      for (int qc = 0; qc < 4; ++qc) {
-        f32x16 s, dp;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          s[r] = 0.f;
-          dp[r] = 0.f;
-        }
-        const unsigned short* qr = sQ + (qc * 32 + l32) * LD + hi * 8;
-        const unsigned short* orow = sO + (qc * 32 + l32) * LD + hi * 8;
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(*(const uint4*)(qr + kk * 16)), kf[kk], s, 0, 0, 0);
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(*(const uint4*)(orow + kk * 16)), vf[kk], dp, 0, 0, 0);
-        }
-        // lane: key kl; register r: query qc*32 + 8(r/4) + 4hi + r%4
+    for (int qc = 0; qc < 2; ++qc) {
+      f32x16 s, dp;
+      two_products(s, dp, sQ, sO, qc * 32 + l32, kf, vf, hi);
+      // lane: key; register r: query qc*32 + 8(r/4) + 4hi + r%4
+      if (partial) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int qi = qc * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          bool ok = true;
-          if (partial) ok = qi < qlen && legal(sQT[qi], kt, a.window);
-          const float p = ok ? __builtin_amdgcn_exp2f(s[r] * a.scale_log2 - sL[qi]) : 0.f;
+          if (!(qi < len && legal(sQT[qi], kt, a.window))) s[r] = kNegInf;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int q4 = qc * 32 + 8 * i + 4 * hi;
+        const float4 l4 = *(const float4*)(sL + q4);
+        const float4 d4 = *(const float4*)(sD + q4);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int r = 4 * i + c;
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.scale_log2, lv[c]));
           s[r] = p;
-          dp[r] = p * (dp[r] - sD[qi]);
+          dp[r] = p * (dp[r] - dv4[c]);
+        }
+      }
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        bf16x8 pb, dsb;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          pb[i] = (__bf16)s[8 * hf + i];
+          dsb[i] = (__bf16)dp[8 * hf + i];
         }
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          bf16x8 pb, dsb;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            pb[i] = (__bf16)s[8 * hf + i];
-            dsb[i] = (__bf16)dp[8 * hf + i];
-          }
-          const int row0 = (qc * 32 + 16 * hf + tr_row0) * LD + tr_col;
-#pragma unroll
-          for (int db = 0; db < 4; ++db) {
-            const bf16x8 of = lds_tr8(sO + row0 + db * 32, sO + row0 + 8 * LD + db * 32);
-            dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(of, pb, dv[db], 0, 0, 0);
-            const bf16x8 qfv = lds_tr8(sQ + row0 + db * 32, sQ + row0 + 8 * LD + db * 32);
-            dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qfv, dsb, dk[db], 0, 0, 0);
-          }
+        for (int db = 0; db < 4; ++db) {
+          dv[db] = mfma(tr.read(sO, qc * 32 + 16 * hf, db), pb, dv[db]);
+          dk[db] = mfma(tr.read(sQ, qc * 32 + 16 * hf, db), dsb, dk[db]);
         }
       }
     }
+    __syncthreads();  // every wave is done with sub-tile m
+    if (more) stage();
   }
 
   if (!kvalid) return;

@@ -48,6 +48,32 @@ def parse():
     return ap.parse_args()
 
 
+HERE = os.path.dirname(os.path.abspath(__file__))
+FWD_SOURCES = ["block_sparse_masked_metadata_amd/csrc/fwd.hip",
+               "block_sparse_masked_metadata_amd/csrc/kernels.hpp",
+               "block_sparse_masked_metadata_amd/csrc/tile_common.hpp"]
+TRAFFIC_PROFILE = "profiles/fwd_kernel_hbm_packed_multimodal_64k.md"
+
+
+def measured_traffic(workload):
+    """HBM bytes per forward launch from the committed counter summary, or None
+    when it is for another workload or the kernel sources changed since."""
+    import hashlib
+    if workload != "packed_multimodal_64k":
+        return None
+    try:
+        text = open(os.path.join(HERE, TRAFFIC_PROFILE)).read()
+        h = hashlib.sha256()
+        for f in FWD_SOURCES:
+            h.update(open(os.path.join(HERE, f), "rb").read())
+        kv = dict(line.split(" = ", 1) for line in text.splitlines() if " = " in line)
+        if kv.get("sources_sha256", "").strip() != h.hexdigest():
+            return None
+        return float(kv["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(lay, plan_pairs_fn, rows_all, q, k, v, target_s):
     """Time the fp64 oracle on whole samples of the measured rank's share."""
     from oracle import attention as oatt
@@ -219,7 +245,8 @@ def main():
                                  / PEAK_BF16_TFLOPS, 2)},
         "roofline": {"bound": "mfma", "kernel": "fwd_kernel", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None if args.single else measured_traffic(lay.name),
                      "avg_launch_us": round(avg_launch_ms * 1e3, 2),
                      "launches_per_step": 1 if args.single else len(fwd_steps)},
         "mode": "single-pass diagnostic" if args.single else "ring",

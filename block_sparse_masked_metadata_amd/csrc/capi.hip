@@ -192,6 +192,16 @@ int check_heads(const bsm_heads* h) {
 
 int32_t heads_per_xcd(int32_t hq) { return hq % 8 == 0 ? hq / 8 : 0; }
 
+// The kernels address a row buffer with 32-bit byte offsets: rows * heads *
+// d * 2 bytes must stay below 2^32.
+int check_rows(int64_t rows, int32_t heads, const char* what) {
+  if ((uint64_t)rows * (uint64_t)heads * kHeadDim * 2u >= (1ull << 32)) {
+    set_error(std::string(what) + ": buffers of 4 GiB or more per tensor are not supported");
+    return BSM_E_UNSUPPORTED;
+  }
+  return BSM_OK;
+}
+
 const uint16_t* bf(const void* p) { return (const uint16_t*)p; }
 
 }  // namespace
@@ -378,6 +388,7 @@ int bsm_fwd_step(const bsm_dplan* d, int32_t s, const bsm_heads* heads, const vo
     set_error("null tensor pointer");
     return BSM_E_INVALID;
   }
+  if ((rc = check_rows(d->S, heads->hq, "q")) || (rc = check_rows(d->S, heads->hkv, "k/v"))) return rc;
   if (d->nf[s] == 0) return BSM_OK;
   const int32_t j = ((d->r - s) % d->R + d->R) % d->R;
   FwdArgs a{};
@@ -416,6 +427,8 @@ int bsm_fwd_single(const bsm_dplan* d, const bsm_heads* heads, const void* q, co
     set_error("null tensor pointer");
     return BSM_E_INVALID;
   }
+  if ((rc = check_rows(d->S, heads->hq, "q")) || (rc = check_rows((int64_t)d->S * d->R, heads->hkv, "k_all/v_all")))
+    return rc;
   if (d->ns == 0) return BSM_OK;
   FwdArgs a{};
   a.items = d->sitems;
@@ -463,6 +476,7 @@ int bsm_bwd_step(const bsm_dplan* d, int32_t s, const bsm_heads* heads, const vo
     set_error("null tensor pointer");
     return BSM_E_INVALID;
   }
+  if ((rc = check_rows(d->S, heads->hq, "q/dout")) || (rc = check_rows(d->S, heads->hkv, "k/v"))) return rc;
   const int32_t j = ((d->r - s) % d->R + d->R) % d->R;
   BwdArgs a{};
   a.entries = d->entries;

@@ -52,13 +52,13 @@ __device__ inline bf16x8 lds_tr8(const unsigned short* p0, const unsigned short*
   return __builtin_bit_cast(bf16x8, both);
 }
 
+// The mask predicate of MARBLE section 01 over per-token tracks (x = sample,
+// y = seg, z = noise, w = pos).  The query's seg is pre-mapped to -2 when it
+// is negative, so seg equality alone means "same span".  pos - pos as an
+// unsigned number is below the window exactly when 0 <= d < window.
 __device__ inline bool legal(const int4 q, const int4 k, int32_t window) {
-  // tracks: x = sample, y = seg, z = noise, w = pos (MARBLE section 01)
-  const int32_t d = q.w - k.w;
-  const bool causal = (d >= 0) & (d < window);
-  const bool span = (q.y == k.y) & (k.y >= 0);
-  const bool keep = (k.z < 0) | (q.z == k.z);
-  return (causal | span) & keep & (q.x == k.x);
+  const uint32_t d = (uint32_t)(q.w - k.w);
+  return ((d < (uint32_t)window) | (q.y == k.y)) & ((k.z < 0) | (q.z == k.z)) & (q.x == k.x);
 }
 
 __device__ inline void map_block(int32_t b, int32_t nitems, int32_t hq, int32_t hpx,
@@ -97,29 +97,33 @@ struct SubTile {
   int4 kt;
 };
 
-// kbytes/vbytes: uniform base addresses; byte offsets stay below 2^32 (a key
-// buffer holds fewer than 2^32 bytes: at most 2^30 rows of one head group).
-__device__ inline void fetch_sub(SubTile& t, const char* kbytes, const char* vbytes,
-                                 const int4* ktracks, int64_t k0, int len, bool partial,
-                                 uint32_t row_bytes, int tid) {
-  t.kt = make_int4(-1, -1, -1, 0);
+// kbase/vbase: the head's element 0 of key row 0 (uniform).  k0 is uniform, so
+// the row base of a full sub-tile and the strides of its 4 loads are scalar;
+// `lane_off` = (t/16) * row_bytes + 16 (t%16) is loop-invariant.  Key-row byte
+// offsets stay below 2^32 (a key buffer holds fewer than 2^32 bytes).
+__device__ inline void fetch_sub(SubTile& t, const char* kbase, const char* vbase,
+                                 const int4* ktracks, int32_t k0, int len, bool partial,
+                                 uint32_t row_bytes, uint32_t lane_off, int tid) {
+  t.kt = make_int4(-1, -1, -1, 0);  // sample -1: no query is legal against it
   if (partial && tid < len) t.kt = ktracks[k0 + tid];
-  const uint32_t off = (uint32_t)(k0 + (tid >> 4)) * row_bytes + (uint32_t)(tid & 15) * 16u;
+  const uint32_t r0 = (uint32_t)k0 * row_bytes;
   if (len == kSub) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      t.k[i] = *(const uint4*)(kbytes + (off + 16u * i * row_bytes));
-      t.v[i] = *(const uint4*)(vbytes + (off + 16u * i * row_bytes));
+      const uint32_t ro = r0 + 16u * i * row_bytes;
+      t.k[i] = *(const uint4*)(kbase + ro + lane_off);
+      t.v[i] = *(const uint4*)(vbase + ro + lane_off);
     }
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = (tid >> 4) + 16 * i;
+      const uint32_t ro = r0 + 16u * i * row_bytes;
       t.k[i] = make_uint4(0, 0, 0, 0);
       t.v[i] = make_uint4(0, 0, 0, 0);
       if (row < len) {
-        t.k[i] = *(const uint4*)(kbytes + (off + 16u * i * row_bytes));
-        t.v[i] = *(const uint4*)(vbytes + (off + 16u * i * row_bytes));
+        t.k[i] = *(const uint4*)(kbase + ro + lane_off);
+        t.v[i] = *(const uint4*)(vbase + ro + lane_off);
       }
     }
   }
@@ -137,10 +141,10 @@ __device__ inline void store_sub(const SubTile& t, char* sK, char* sV, int4* sKT
 }
 
 // Sub-tile n of an item: half n%2 of list entry n/2.
-__device__ inline void sub_bounds(const int2 ent, int n, int64_t& k0, int& len, bool& partial) {
+__device__ inline void sub_bounds(const int2 ent, int n, int32_t& k0, int& len, bool& partial) {
   const int half = n & 1;
   const int klen = ent.y & 0xffff;
-  k0 = (int64_t)ent.x + half * kSub;
+  k0 = ent.x + half * kSub;
   len = klen - half * kSub;
   len = len < 0 ? 0 : (len > kSub ? kSub : len);
   partial = (ent.y & kPartialBit) != 0;
@@ -171,12 +175,14 @@ __device__ inline void scores(f32x16 (&s)[2], const char* sK, const bf16x8 (&qf)
   }
   __builtin_amdgcn_s_setprio(0);
   if (partial) {
+    // Keys past len carry sample -1 and fail the sample test.  Every lane of
+    // a half-wave reads the same key track (an LDS broadcast); no branches.
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-        if (!(key < len && legal(qt, sKT[key], window))) s[kb][r] = kNegInf;
+        s[kb][r] = legal(qt, sKT[key], window) ? s[kb][r] : kNegInf;
       }
   }
 }
@@ -223,13 +229,16 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a) {
 
   // prologue: fetch the first sub-tile, then Q and the state
   SubTile pf;
+  const uint32_t lane_off = (uint32_t)(tid >> 4) * row_bytes + (uint32_t)(tid & 15) * 16u;
   int2 ent = a.entries[it.z];
+  ent.x = __builtin_amdgcn_readfirstlane(ent.x);
+  ent.y = __builtin_amdgcn_readfirstlane(ent.y);
   {
-    int64_t k0;
+    int32_t k0;
     int len;
     bool part;
     sub_bounds(ent, 0, k0, len, part);
-    fetch_sub(pf, kbase, vbase, a.ktracks, k0, len, part, row_bytes, tid);
+    fetch_sub(pf, kbase, vbase, a.ktracks, k0, len, part, row_bytes, lane_off, tid);
   }
 
   // Q^T as the B operand: lane holds query l32, channels [16kk + 8hi, +8).
@@ -240,7 +249,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a) {
     for (int kk = 0; kk < 8; ++kk)
       qf[kk] = qvalid ? as_bf16x8(*(const uint4*)(qp + kk * 16)) : as_bf16x8(make_uint4(0, 0, 0, 0));
   }
-  const int4 qt = qvalid ? a.qtracks[qrow] : make_int4(0, -1, -1, 0);
+  int4 qt = qvalid ? a.qtracks[qrow] : make_int4(0, -1, -1, 0);
+  if (qt.y < 0) qt.y = -2;  // a query outside every span matches no key's seg
 
   // Running state.  acc[db][r] = O^T[d = 32db + 8(r/4) + 4hi + r%4][query l32];
   // mref is the base-2 reference the accumulator and l are scaled against.
@@ -279,7 +289,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a) {
   const int tr_off8 = (jl & 1) * 8;
 
   for (int n = 0; n < nsub; ++n) {
-    int64_t k0;
+    int32_t k0;
     int len;
     bool partial;
     sub_bounds(ent, n, k0, len, partial);
@@ -293,12 +303,14 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a) {
           __syncthreads();
         }
         ent = sEnt[e1 % kListCache];
+        ent.x = __builtin_amdgcn_readfirstlane(ent.x);
+        ent.y = __builtin_amdgcn_readfirstlane(ent.y);
       }
-      int64_t nk0;
+      int32_t nk0;
       int nlen;
       bool npart;
       sub_bounds(ent, n + 1, nk0, nlen, npart);
-      fetch_sub(pf, kbase, vbase, a.ktracks, nk0, nlen, npart, row_bytes, tid);
+      fetch_sub(pf, kbase, vbase, a.ktracks, nk0, nlen, npart, row_bytes, lane_off, tid);
     }
 
     f32x16 s[2];

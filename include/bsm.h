@@ -218,8 +218,11 @@ typedef struct {
  *   q      bf16 [S, Hq, d]   the rank's query shard in plan order
  *   k, v   bf16 [S, Hkv, d]  shard j in plan order
  *   o_acc  fp32 [S, Hq, d]   unnormalized accumulator   (carried state)
- *   m      fp32 [Hq, S]      running row max of scale*log2(e)*q.k (base-2
- *                            units), -inf before the first legal key
+ *   m      fp32 [Hq, S]      reference of the row in base-2 units
+ *                            (scale*log2(e)*q.k): the row max at the last
+ *                            rescale, -inf before the first legal key; o_acc
+ *                            and l are scaled by 2^-m, and later scores exceed
+ *                            m by less than 12 (every 2^(x - m) < 2^12)
  *   l      fp32 [Hq, S]      running row sum of 2^(x - m)
  *   o      bf16 [S, Hq, d]   written at a tile's last non-empty step
  *   lse    fp32 [Hq, S]      natural-log LSE, written with o
@@ -230,6 +233,8 @@ typedef struct {
  * flags has BSM_FWD_KEEP_STATE.  Rows with no legal key get O = 0 and
  * LSE = -inf.  Steps without work return BSM_OK without a launch.  S is the
  * plan's shard_tokens; rows of a ragged last tile beyond S are never touched.
+ * Every bf16 tensor must be under 4 GiB (the kernels use 32-bit byte
+ * offsets), else BSM_E_UNSUPPORTED.
  */
 int bsm_fwd_step(const bsm_dplan* dplan, int32_t s, const bsm_heads* heads,
                  const void* q, const void* k, const void* v,
@@ -243,6 +248,7 @@ int bsm_fwd_step(const bsm_dplan* dplan, int32_t s, const bsm_heads* heads,
  * the ring visits them, with the state kept in registers, so the result is
  * bitwise identical to the R ring steps.  With BSM_FWD_KEEP_STATE it stores
  * (o_acc, m, l) instead of (o, lse); otherwise o_acc, m, l may be NULL.
+ * k_all and v_all must each be under 4 GiB, else BSM_E_UNSUPPORTED.
  */
 int bsm_fwd_single(const bsm_dplan* dplan, const bsm_heads* heads,
                    const void* q, const void* k_all, const void* v_all,
@@ -273,6 +279,7 @@ int bsm_bwd_prep(const bsm_heads* heads, int64_t rows, const void* o, const void
  *                                      the rank's contribution (caller clears
  *                                      them before the first contribution)
  * With grouped heads, dk/dv of a key/value head sum over its query heads.
+ * Every bf16 tensor must be under 4 GiB, else BSM_E_UNSUPPORTED.
  */
 int bsm_bwd_step(const bsm_dplan* dplan, int32_t s, const bsm_heads* heads,
                  const void* q, const void* k, const void* v, const void* dout,

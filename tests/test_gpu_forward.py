@@ -213,3 +213,12 @@ def test_fwd_errors_before_launch():
     with pytest.raises(bsm.BsmError) as e:
         C.bsm_fwd_step(case.dp.handle, 99, case.heads, 1, 1, 1, 1, 1, 1, 1, 1, 0, None)
     assert e.value.code == C.BSM_E_INVALID
+    # 4096 x 4096 heads x 256 B = 4 GiB per key tensor: refused before any launch
+    # (the pointers are never dereferenced)
+    big = bsm.heads(4096, 4096)
+    for fn in (lambda: C.bsm_fwd_step(case.dp.handle, 0, big, 1, 1, 1, 1, 1, 1, 1, 1, 0, None),
+               lambda: C.bsm_bwd_step(case.dp.handle, 0, big, 1, 1, 1, 1, 1, 1, 1, 1, 1, None)):
+        with pytest.raises(bsm.BsmError) as e:
+            fn()
+        assert e.value.code == C.BSM_E_UNSUPPORTED
+        assert "4 GiB" in str(e.value)

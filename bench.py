@@ -74,6 +74,45 @@ def measured_traffic(workload):
         return None
 
 
+def fwd_algorithmic_bytes(plan, r, R, S, hq, hkv, d, single=False):
+    """HBM bytes the forward must move, per launch, from the plan's tile maps.
+
+    Per ring step s: Q of the query tiles with work (2*d*Hq per row); K and V of
+    the key tiles that appear in any of their lists (4*d*Hkv per key); the fp32
+    state (O_acc, m, l: (4*d + 8)*Hq per row) read unless it is the tile's first
+    step with work and written unless it is its last; at the last step O (bf16)
+    and LSE instead (2*d + 4 bytes per row and head).  The single pass moves Q,
+    the needed key tiles of every shard and the final O/LSE once."""
+    T = plan.info["tiles_per_shard"]
+    rows = np.minimum(128, S - 128 * np.arange(T)).astype(np.int64)
+    active, keyset = [], []
+    for s in range(R):
+        mp, _ = plan.step_map(r, s)
+        active.append((mp > 0).any(axis=1))
+        keyset.append((mp > 0).any(axis=0))
+    act = np.array(active)                      # [R, T]
+    has = act.any(axis=0)
+    first = np.where(has, act.argmax(axis=0), -1)
+    last = np.where(has, R - 1 - act[::-1].argmax(axis=0), -1)
+    state_row = (4 * d + 8) * hq
+    if single:
+        qrows = int(rows[has].sum())
+        kv = sum(int(rows[keyset[s]].sum()) for s in range(R)) * 4 * d * hkv
+        return [qrows * 2 * d * hq + kv + qrows * (2 * d + 4) * hq]
+    out = []
+    for s in range(R):
+        a = act[s]
+        if not a.any():
+            continue
+        q = int(rows[a].sum()) * 2 * d * hq
+        kv = int(rows[keyset[s]].sum()) * 4 * d * hkv
+        rd = int(rows[a & (first != s)].sum()) * state_row
+        wr = int(rows[a & (last != s)].sum()) * state_row
+        fin = int(rows[a & (last == s)].sum()) * (2 * d + 4) * hq
+        out.append(q + kv + rd + wr + fin)
+    return out
+
+
 def cpu_baseline(lay, plan_pairs_fn, rows_all, q, k, v, target_s):
     """Time the fp64 oracle on whole samples of the measured rank's share."""
     from oracle import attention as oatt
@@ -208,8 +247,19 @@ def main():
     fwd_flops = 4 * d * lay.hq * total_pairs
     bwd_flops = 10 * d * lay.hq * total_pairs
     fwd_tflops = fwd_flops / (fwd_ms * 1e-3) / 1e12
-    per_launch_flops = fwd_flops / (1 if args.single else len(fwd_steps))
-    achieved = per_launch_flops / (avg_launch_ms * 1e-3) / 1e12
+    nlaunch = 1 if args.single else len(fwd_steps)
+    per_launch_flops = fwd_flops / nlaunch
+    per_launch_bytes = sum(fwd_algorithmic_bytes(plan, r, R, S, lay.hq, lay.hkv, d, args.single)) / nlaunch
+    # roofline of the forward kernel: whichever of the MFMA and HBM times of its
+    # algorithmic work is longer bounds it
+    t_mfma = per_launch_flops / (PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = per_launch_bytes / (PEAK_HBM_GBS * 1e9)
+    mfma_tflops = per_launch_flops / (avg_launch_ms * 1e-3) / 1e12
+    hbm_gbs = per_launch_bytes / (avg_launch_ms * 1e-3) / 1e9
+    if t_hbm > t_mfma:
+        bound, achieved, peak, unit = "hbm", hbm_gbs, PEAK_HBM_GBS, "GB/s"
+    else:
+        bound, achieved, peak, unit = "mfma", mfma_tflops, PEAK_BF16_TFLOPS, "TFLOP/s"
 
     if args.copy_mib:
         src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device="cuda")
@@ -243,12 +293,20 @@ def main():
             "bwd_tflops": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 2),
             "pct_of_peak": round(100 * (fwd_flops + bwd_flops) / (step_ms * 1e-3) / 1e12
                                  / PEAK_BF16_TFLOPS, 2)},
-        "roofline": {"bound": "mfma", "kernel": "fwd_kernel", "achieved": round(achieved, 2),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"bound": bound, "kernel": "fwd_kernel", "achieved": round(achieved, 2),
+                     "peak": peak, "unit": unit,
+                     "frac": round(achieved / peak, 4),
                      "traffic": None if args.single else measured_traffic(lay.name),
+                     "algorithmic_bytes": int(per_launch_bytes),
+                     "algorithmic_flops": int(per_launch_flops),
+                     "flop_per_byte": round(per_launch_flops / per_launch_bytes, 1),
+                     "ridge_flop_per_byte": round(PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9), 1),
+                     "mfma_tflops": round(mfma_tflops, 2),
+                     "mfma_frac": round(mfma_tflops / PEAK_BF16_TFLOPS, 4),
+                     "hbm_gbs": round(hbm_gbs, 1),
+                     "hbm_frac": round(hbm_gbs / PEAK_HBM_GBS, 4),
                      "avg_launch_us": round(avg_launch_ms * 1e3, 2),
-                     "launches_per_step": 1 if args.single else len(fwd_steps)},
+                     "launches_per_step": nlaunch},
         "mode": "single-pass diagnostic" if args.single else "ring",
         "planner_s": round(plan_s, 4),
         "wall_s": round(wall, 3),

@@ -156,7 +156,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kc * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (!(key < len && legal(qt, sKT[key], a.window))) s[r] = kNegInf;
+          s[r] = legal(qt, sKT[key], a.window) ? s[r] : kNegInf;  // keys past len: sample -1
         }
       }
 #pragma unroll
@@ -285,6 +285,52 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
   __builtin_amdgcn_s_waitcnt(0);  // no load is pending when the loop starts
   const TrLane tr(lane);
 
+  // P = exp2(S * scale*log2(e) - LSE*log2(e)) and dS = P (dP - delta) for the
+  // 32 queries [q0, q0+32) of the staged sub-tile, as bf16 MFMA B operands
+  // (lane: key; register r: query q0 + 8(r/4) + 4hi + r%4).  On partial
+  // sub-tiles illegal pairs get P = 0; rows past len carry sample -2.
+  auto p_and_ds = [&](f32x16& s, f32x16& dp, bf16x8 (&pb)[2], bf16x8 (&dsb)[2], int q0, bool partial) {
+    if (partial) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qi = q0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+        s[r] = legal(sQT[qi], kt, a.window) ? s[r] : kNegInf;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q4 = q0 + 8 * i + 4 * hi;
+      const float4 l4 = *(const float4*)(sL + q4);
+      const float4 d4 = *(const float4*)(sD + q4);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+      const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int r = 4 * i + c;
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.scale_log2, lv[c]));
+        s[r] = p;
+        dp[r] = p * (dp[r] - dv4[c]);
+      }
+    }
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        pb[hf][i] = (__bf16)s[8 * hf + i];
+        dsb[hf][i] = (__bf16)dp[8 * hf + i];
+      }
+  };
+  // dV^T += dO^T P^T and dK^T += Q^T dS^T over the queries [q0, q0+32).
+  auto accumulate = [&](const bf16x8 (&pb)[2], const bf16x8 (&dsb)[2], int q0) {
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        dv[db] = mfma(tr.read(sO, q0 + 16 * hf, db), pb[hf], dv[db]);
+        dk[db] = mfma(tr.read(sQ, q0 + 16 * hf, db), dsb[hf], dk[db]);
+      }
+  };
+
   for (int m = 0; m < total; ++m) {
     const int len = cur_len;
     const bool partial = cur_partial;
@@ -295,48 +341,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
       if ((n1 & 1) == 0) ent = list_entry(sEnt, list_base, a.entries, it, n1 >> 1, tid);
       fetch(m + 1, ent);
     }
-#pragma unroll
-    for (int qc = 0; qc < 2; ++qc) {
-      f32x16 s, dp;
-      two_products(s, dp, sQ, sO, qc * 32 + l32, kf, vf, hi);
-      // lane: key; register r: query qc*32 + 8(r/4) + 4hi + r%4
-      if (partial) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qi = qc * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (!(qi < len && legal(sQT[qi], kt, a.window))) s[r] = kNegInf;
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int q4 = qc * 32 + 8 * i + 4 * hi;
-        const float4 l4 = *(const float4*)(sL + q4);
-        const float4 d4 = *(const float4*)(sD + q4);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-        const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int r = 4 * i + c;
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.scale_log2, lv[c]));
-          s[r] = p;
-          dp[r] = p * (dp[r] - dv4[c]);
-        }
-      }
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        bf16x8 pb, dsb;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          pb[i] = (__bf16)s[8 * hf + i];
-          dsb[i] = (__bf16)dp[8 * hf + i];
-        }
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          dv[db] = mfma(tr.read(sO, qc * 32 + 16 * hf, db), pb, dv[db]);
-          dk[db] = mfma(tr.read(sQ, qc * 32 + 16 * hf, db), dsb, dk[db]);
-        }
-      }
-    }
+    // The two 32-query halves qc are software-pipelined inside the wave: the
+    // S and dP MFMAs of half 1 run while the vector unit builds P and dS of
+    // half 0, and the dV/dK MFMAs of half 0 while it builds those of half 1.
+    f32x16 s0, dp0, s1, dp1;
+    bf16x8 pb0[2], ds0[2], pb1[2], ds1[2];
+    two_products(s0, dp0, sQ, sO, l32, kf, vf, hi);
+    two_products(s1, dp1, sQ, sO, 32 + l32, kf, vf, hi);
+    p_and_ds(s0, dp0, pb0, ds0, 0, partial);
+    accumulate(pb0, ds0, 0);
+    p_and_ds(s1, dp1, pb1, ds1, 32, partial);
+    accumulate(pb1, ds1, 32);
     __syncthreads();  // every wave is done with sub-tile m
     if (more) stage();
   }

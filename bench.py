@@ -8,8 +8,9 @@ busiest rank's 8192-token PTRR shard.
 
 One timed step = the whole hot path on resident inputs: P forward ring steps
 (fp32 state carried in HBM, finalize on each tile's last step), the backward
-prep (delta = rowsum(dO * O)) and P backward ring steps (dQ carried, dK/dV per
-shard).  The planner runs once per packed batch before timing (it is reused by
+prep (delta = rowsum(dO * O)), clearing the rank's own shard's dK/dV
+accumulators, and P backward ring steps (dQ carried, dK/dV added into each
+shard's travelling accumulator).  The planner runs once per packed batch before timing (it is reused by
 every layer), as do plan upload and the input permutation.
 
 Only unmasked FLOPs count: 4*d*Hq per legal (query, key) pair forward,
@@ -209,8 +210,20 @@ def main():
                 events.append(torch.cuda.Event(enable_timing=True))
                 events[-1].record()
 
+    delta = torch.empty(lay.hq, S, dtype=torch.float32, device="cuda")
+
     def backward():
-        bsm.bwd_ring(dp, hd, q, ks, vs, dout, o, lse, grads=(dq, dks, dvs))
+        # One rank's backward: delta, then the R steps.  Shard j's dK/dV
+        # accumulator travels the ring and arrives holding the other ranks'
+        # contributions; only the rank's own shard (j = r) starts from zero
+        # here, so the others keep accumulating across timed passes (their
+        # values are not checked; the kernels do the same work either way).
+        bsm.bwd_prep(hd, o, dout, delta)
+        dks[r].zero_()
+        dvs[r].zero_()
+        for s in range(R):
+            j = (r - s) % R
+            bsm.bwd_step(dp, s, hd, q, ks[j], vs[j], dout, lse, delta, dq, dks[j], dvs[j])
 
     for _ in range(args.warmup):
         forward()

@@ -162,6 +162,13 @@ def bwd_prep(hd, o, dout, delta=None):
     return delta
 
 
+def bwd_step(dp: DevicePlan, s, hd, q, k, v, dout, lse, delta, dq, dk, dv):
+    """One backward ring step against shard j = (r - s) mod R: dq carried
+    (first step with work overwrites), dk/dv of shard j added to."""
+    C.bsm_bwd_step(dp.handle, s, hd, _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(delta),
+                   _ptr(dq), _ptr(dk), _ptr(dv), _stream())
+
+
 def bwd_ring(dp: DevicePlan, hd, q, k_shards, v_shards, dout, o, lse, grads=None, steps=None):
     """Backward over ring steps s = 0..R-1.  Returns (dq, dk_shards, dv_shards) in fp32.
 
@@ -184,7 +191,5 @@ def bwd_ring(dp: DevicePlan, hd, q, k_shards, v_shards, dout, o, lse, grads=None
             t.zero_()
     for s in (range(dp.ranks) if steps is None else steps):
         j = (dp.rank - s) % dp.ranks
-        C.bsm_bwd_step(dp.handle, s, hd, _ptr(q), _ptr(k_shards[j]), _ptr(v_shards[j]),
-                       _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq), _ptr(dks[j]), _ptr(dvs[j]),
-                       _stream())
+        bwd_step(dp, s, hd, q, k_shards[j], v_shards[j], dout, lse, delta, dq, dks[j], dvs[j])
     return dq, dks, dvs

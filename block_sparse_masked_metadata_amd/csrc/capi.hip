@@ -54,8 +54,8 @@ struct Packed {
   std::vector<int2> entries;
   // byte offsets in the device buffer
   int64_t off_tracks = 0, off_items = 0, off_entries = 0, bytes = 0;
-  std::vector<int64_t> off_f, off_b;
-  int64_t off_s = 0;
+  std::vector<int64_t> off_f, off_b, off_ff;  // off_ff: first list entry of each forward item
+  int64_t off_s = 0, off_sf = 0;
 };
 
 static void pack(const Plan& p, int32_t r, Packed& pk) {
@@ -148,14 +148,19 @@ static void pack(const Plan& p, int32_t r, Packed& pk) {
   pk.off_items = off;
   pk.off_f.assign(R, 0);
   pk.off_b.assign(R, 0);
+  pk.off_ff.assign(R, 0);
   for (int32_t s = 0; s < R; ++s) {
     pk.off_f[s] = off;
     off = align256(off + (int64_t)pk.steps[s].fitems.size() * sizeof(int4));
+    pk.off_ff[s] = off;
+    off = align256(off + (int64_t)pk.steps[s].fitems.size() * sizeof(int2));
     pk.off_b[s] = off;
     off = align256(off + (int64_t)pk.steps[s].bitems.size() * sizeof(int4));
   }
   pk.off_s = off;
   off = align256(off + (int64_t)pk.sitems.size() * sizeof(int4));
+  pk.off_sf = off;
+  off = align256(off + (int64_t)pk.sitems.size() * sizeof(int2));
   pk.off_entries = off;
   off = align256(off + (int64_t)pk.entries.size() * sizeof(int2));
   pk.bytes = std::max<int64_t>(off, 256);
@@ -169,9 +174,11 @@ struct bsm_dplan {
   const int4* tracks = nullptr;
   const int2* entries = nullptr;
   const int4* fitems[64] = {};
+  const int2* ffirst[64] = {};
   const int4* bitems[64] = {};
   int64_t nf[64] = {}, nb[64] = {}, pairs[64] = {};
   const int4* sitems = nullptr;
+  const int2* sfirst = nullptr;
   int64_t ns = 0;
 };
 
@@ -320,9 +327,13 @@ int bsm_dplan_upload(const bsm_plan* plan, int32_t r, void* dev, int64_t bytes, 
     std::memcpy(img.data() + pk.off_tracks, pk.tracks.data(), pk.tracks.size() * sizeof(int4));
     for (int32_t s = 0; s < p.ranks; ++s) {
       std::memcpy(img.data() + pk.off_f[s], pk.steps[s].fitems.data(), pk.steps[s].fitems.size() * sizeof(int4));
+      int2* ff = (int2*)(img.data() + pk.off_ff[s]);
+      for (size_t i = 0; i < pk.steps[s].fitems.size(); ++i) ff[i] = pk.entries[pk.steps[s].fitems[i].z];
       std::memcpy(img.data() + pk.off_b[s], pk.steps[s].bitems.data(), pk.steps[s].bitems.size() * sizeof(int4));
     }
     std::memcpy(img.data() + pk.off_s, pk.sitems.data(), pk.sitems.size() * sizeof(int4));
+    int2* sf = (int2*)(img.data() + pk.off_sf);
+    for (size_t i = 0; i < pk.sitems.size(); ++i) sf[i] = pk.entries[pk.sitems[i].z];
     std::memcpy(img.data() + pk.off_entries, pk.entries.data(), pk.entries.size() * sizeof(int2));
     hipStream_t st = (hipStream_t)stream;
     int rc = hip_status(hipMemcpyAsync(dev, img.data(), pk.bytes, hipMemcpyHostToDevice, st),
@@ -342,12 +353,14 @@ int bsm_dplan_upload(const bsm_plan* plan, int32_t r, void* dev, int64_t bytes, 
     d->entries = (const int2*)(base + pk.off_entries);
     for (int32_t s = 0; s < p.ranks; ++s) {
       d->fitems[s] = (const int4*)(base + pk.off_f[s]);
+      d->ffirst[s] = (const int2*)(base + pk.off_ff[s]);
       d->bitems[s] = (const int4*)(base + pk.off_b[s]);
       d->nf[s] = (int64_t)pk.steps[s].fitems.size();
       d->nb[s] = (int64_t)pk.steps[s].bitems.size();
       d->pairs[s] = pk.steps[s].pairs;
     }
     d->sitems = (const int4*)(base + pk.off_s);
+    d->sfirst = (const int2*)(base + pk.off_sf);
     d->ns = (int64_t)pk.sitems.size();
     *out = d;
   } catch (const std::bad_alloc&) {
@@ -393,6 +406,7 @@ int bsm_fwd_step(const bsm_dplan* d, int32_t s, const bsm_heads* heads, const vo
   const int32_t j = ((d->r - s) % d->R + d->R) % d->R;
   FwdArgs a{};
   a.items = d->fitems[s];
+  a.first = d->ffirst[s];
   a.entries = d->entries;
   a.nitems = (int32_t)d->nf[s];
   a.hq = heads->hq;
@@ -432,6 +446,7 @@ int bsm_fwd_single(const bsm_dplan* d, const bsm_heads* heads, const void* q, co
   if (d->ns == 0) return BSM_OK;
   FwdArgs a{};
   a.items = d->sitems;
+  a.first = d->sfirst;
   a.entries = d->entries;
   a.nitems = (int32_t)d->ns;
   a.hq = heads->hq;

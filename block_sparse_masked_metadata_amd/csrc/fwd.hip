@@ -210,12 +210,19 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a) {
   int32_t item, h;
   map_block((int32_t)blockIdx.x, a.nitems, a.hq, a.heads_per_xcd, item, h);
   if (item < 0) return;
+  // Prologue in two memory round trips: the item record and its first list
+  // entry (scalar loads, side by side), then every other load at once: the
+  // list, the first K/V sub-tile, Q, the query tracks and the state.
   const int4 it = a.items[item];
+  int2 ent = a.first[item];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   // the item's list goes to LDS in chunks of kListCache entries, so the loop
-  // never waits on a memory load for it
-  for (int i = tid; i < it.w && i < kListCache; i += 256) sEnt[i] = a.entries[it.z + i];
+  // never waits on a memory load for it (two entries per thread)
+  const int nl = it.w < kListCache ? it.w : kListCache;
+  int2 le0 = make_int2(0, 0), le1 = make_int2(0, 0);
+  if (tid < nl) le0 = a.entries[it.z + tid];
+  if (tid + 256 < nl) le1 = a.entries[it.z + 256 + tid];
   const int l32 = lane & 31, hi = lane >> 5;
   const int64_t q0 = (int64_t)it.x * kTile;
   const int64_t qi = wave * 32 + l32;
@@ -230,7 +237,6 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a) {
   // prologue: fetch the first sub-tile, then Q and the state
   SubTile pf;
   const uint32_t lane_off = (uint32_t)(tid >> 4) * row_bytes + (uint32_t)(tid & 15) * 16u;
-  int2 ent = a.entries[it.z];
   ent.x = __builtin_amdgcn_readfirstlane(ent.x);
   ent.y = __builtin_amdgcn_readfirstlane(ent.y);
   {
@@ -276,6 +282,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a) {
         acc[db][4 * i + 3] = v4.w;
       }
   }
+  if (tid < nl) sEnt[tid] = le0;
+  if (tid + 256 < nl) sEnt[tid + 256] = le1;
   store_sub(pf, sK, sV, sKT, tid);
   // Drain every prologue load here, once: a register loaded before the loop
   // with a load still pending would make each iteration's first use of it

@@ -25,6 +25,7 @@ constexpr int32_t kPartialBit = 1 << 16;
 
 struct FwdArgs {
   const int4* items;
+  const int2* first;        // items[i]'s first list entry (entries[items[i].z])
   const int2* entries;
   int32_t nitems;
   int32_t hq, hkv;

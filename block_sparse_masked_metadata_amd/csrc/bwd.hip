@@ -205,11 +205,13 @@ struct RowStage {
 };
 
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
-  __shared__ __attribute__((aligned(1024))) char sQ[kSub * 256];
-  __shared__ __attribute__((aligned(1024))) char sO[kSub * 256];
-  __shared__ __attribute__((aligned(16))) float sL[kSub];
-  __shared__ __attribute__((aligned(16))) float sD[kSub];
-  __shared__ int4 sQT[kSub];
+  // two buffer sets: sub-tile m computes from set m % 2 while m + 1 is staged
+  // into the other, one barrier per sub-tile
+  __shared__ __attribute__((aligned(1024))) char sQ[2][kSub * 256];
+  __shared__ __attribute__((aligned(1024))) char sO[2][kSub * 256];
+  __shared__ __attribute__((aligned(16))) float sL[2][kSub];
+  __shared__ __attribute__((aligned(16))) float sD[2][kSub];
+  __shared__ int4 sQT[2][kSub];
   __shared__ int2 sEnt[kListCache];
 
   int32_t item, g;
@@ -250,13 +252,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
     pf.fetch((const char*)(a.q + (int64_t)h * kHeadDim), (const char*)(a.dout + (int64_t)h * kHeadDim),
              r0, nxt_len, row_bytes, tid);
   };
-  auto stage = [&]() {
-    pf.store(sQ, sO, tid);
-    if (tid < kSub) sL[tid] = rs.v;
-    else if (tid < 2 * kSub) sD[tid - kSub] = rs.v;
-    else if (tid < 3 * kSub) sQT[tid - 2 * kSub] = rs.t;
-    cur_len = nxt_len;
-    cur_partial = nxt_partial;
+  auto stage = [&](int buf) {
+    pf.store(sQ[buf], sO[buf], tid);
+    if (tid < kSub) sL[buf][tid] = rs.v;
+    else if (tid < 2 * kSub) sD[buf][tid - kSub] = rs.v;
+    else if (tid < 3 * kSub) sQT[buf][tid - 2 * kSub] = rs.t;
   };
 
   ent = a.entries[it.z];
@@ -281,7 +281,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
       dk[db][r] = 0.f;
       dv[db][r] = 0.f;
     }
-  stage();
+  stage(0);
+  cur_len = nxt_len;
+  cur_partial = nxt_partial;
   __builtin_amdgcn_s_waitcnt(0);  // no load is pending when the loop starts
   const TrLane tr(lane);
 
@@ -289,7 +291,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
   // 32 queries [q0, q0+32) of the staged sub-tile, as bf16 MFMA B operands
   // (lane: key; register r: query q0 + 8(r/4) + 4hi + r%4).  On partial
   // sub-tiles illegal pairs get P = 0; rows past len carry sample -2.
-  auto p_and_ds = [&](f32x16& s, f32x16& dp, bf16x8 (&pb)[2], bf16x8 (&dsb)[2], int q0, bool partial) {
+  auto p_and_ds = [&](f32x16& s, f32x16& dp, bf16x8 (&pb)[2], bf16x8 (&dsb)[2], int q0, bool partial,
+                      const float* sL, const float* sD, const int4* sQT) {
     if (partial) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -321,7 +324,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
       }
   };
   // dV^T += dO^T P^T and dK^T += Q^T dS^T over the queries [q0, q0+32).
-  auto accumulate = [&](const bf16x8 (&pb)[2], const bf16x8 (&dsb)[2], int q0) {
+  auto accumulate = [&](const bf16x8 (&pb)[2], const bf16x8 (&dsb)[2], int q0, const char* sQ, const char* sO) {
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
@@ -332,9 +335,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
   };
 
   for (int m = 0; m < total; ++m) {
-    const int len = cur_len;
     const bool partial = cur_partial;
-    __syncthreads();  // sub-tile m is in LDS
+    const int cb = m & 1;
+    __syncthreads();  // sub-tile m is in LDS; every wave is done with m - 1
     const bool more = m + 1 < total;
     if (more) {
       const int n1 = (m + 1) % nsub;
@@ -346,14 +349,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
     // half 0, and the dV/dK MFMAs of half 0 while it builds those of half 1.
     f32x16 s0, dp0, s1, dp1;
     bf16x8 pb0[2], ds0[2], pb1[2], ds1[2];
-    two_products(s0, dp0, sQ, sO, l32, kf, vf, hi);
-    two_products(s1, dp1, sQ, sO, 32 + l32, kf, vf, hi);
-    p_and_ds(s0, dp0, pb0, ds0, 0, partial);
-    accumulate(pb0, ds0, 0);
-    p_and_ds(s1, dp1, pb1, ds1, 32, partial);
-    accumulate(pb1, ds1, 32);
-    __syncthreads();  // every wave is done with sub-tile m
-    if (more) stage();
+    two_products(s0, dp0, sQ[cb], sO[cb], l32, kf, vf, hi);
+    two_products(s1, dp1, sQ[cb], sO[cb], 32 + l32, kf, vf, hi);
+    p_and_ds(s0, dp0, pb0, ds0, 0, partial, sL[cb], sD[cb], sQT[cb]);
+    accumulate(pb0, ds0, 0, sQ[cb], sO[cb]);
+    p_and_ds(s1, dp1, pb1, ds1, 32, partial, sL[cb], sD[cb], sQT[cb]);
+    accumulate(pb1, ds1, 32, sQ[cb], sO[cb]);
+    if (more) {
+      stage(cb ^ 1);  // the other set was last read in iteration m - 1
+      cur_len = nxt_len;
+      cur_partial = nxt_partial;
+    }
   }
 
   if (!kvalid) return;

@@ -40,6 +40,7 @@ ORDERS = {"contiguous": BSM_ORDER_CONTIGUOUS, "ptrr": BSM_ORDER_PTRR,
 EXPORTS = [
     "bsm_last_error", "bsm_version", "bsm_plan_build", "bsm_plan_free", "bsm_plan_get_info",
     "bsm_plan_permutation", "bsm_plan_block_cost", "bsm_plan_step_map", "bsm_plan_pairs",
+    "bsm_plan_key_intervals",
     "bsm_dplan_bytes", "bsm_dplan_upload", "bsm_dplan_free", "bsm_dplan_get_info",
     "bsm_fwd_step", "bsm_fwd_single", "bsm_bwd_prep", "bsm_bwd_step",
 ]
@@ -65,7 +66,7 @@ class bsm_plan_info(C.Structure):
                 ("busiest_rank", C.c_int32), ("reserved", C.c_int32),
                 ("total_pairs", C.c_int64), ("candidate_pairs", C.c_int64),
                 ("full_tiles", C.c_int64), ("partial_tiles", C.c_int64),
-                ("build_seconds", C.c_double)]
+                ("build_seconds", C.c_double), ("interval_keys", C.c_int64)]
 
 
 class bsm_dplan_info(C.Structure):
@@ -90,6 +91,7 @@ _sig = {
     "bsm_plan_block_cost": (C.c_int, [_P, _P, _P]),
     "bsm_plan_step_map": (C.c_int, [_P, C.c_int32, C.c_int32, _P, C.POINTER(C.c_int64)]),
     "bsm_plan_pairs": (C.c_int, [_P, _P]),
+    "bsm_plan_key_intervals": (C.c_int, [_P, _P, _P]),
     "bsm_dplan_bytes": (C.c_int, [_P, C.c_int32, C.POINTER(C.c_int64)]),
     "bsm_dplan_upload": (C.c_int, [_P, C.c_int32, _P, C.c_int64, _P, C.POINTER(_P)]),
     "bsm_dplan_free": (None, [_P]),
@@ -179,6 +181,14 @@ def bsm_plan_pairs(plan):
     out = np.empty((rk, rk), np.int64)
     _check(_lib.bsm_plan_pairs(plan, out.ctypes.data))
     return out
+
+
+def bsm_plan_key_intervals(plan):
+    n = bsm_plan_get_info(plan)["n"]
+    lo = np.empty(n, np.int32)
+    hi = np.empty(n, np.int32)
+    _check(_lib.bsm_plan_key_intervals(plan, lo.ctypes.data, hi.ctypes.data))
+    return lo, hi
 
 
 def bsm_dplan_bytes(plan, r) -> int:

@@ -101,7 +101,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
     int len;
     bool part;
     sub_bounds(ent, 0, r0, len, part);
-    if (part && tid < len) kt_pf = a.ktracks[r0 + tid];
+    if (part && tid < len) kt_pf = key_mask_data(a.ktracks, a.kint, r0 + tid, (ent.y & kIntervalBit) != 0);
     pf.fetch(kbase, vbase, r0, len, row_bytes, tid);
   }
   bf16x8 qf[8], df[8];
@@ -135,6 +135,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
     int len;
     bool partial;
     sub_bounds(ent, n, r0, len, partial);
+    const bool interval = (ent.y & kIntervalBit) != 0;
     __syncthreads();  // sub-tile n is in LDS
     const bool more = n + 1 < nsub;
     if (more) {
@@ -143,8 +144,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
       int nlen;
       bool npart;
       sub_bounds(ent, n + 1, nr0, nlen, npart);
-      kt_pf = make_int4(-1, -1, -1, 0);
-      if (npart && tid < nlen) kt_pf = a.ktracks[nr0 + tid];
+      kt_pf = make_int4(-1, -1, -1, 0);  // keys past len: sample -1, empty range
+      if (npart && tid < nlen) kt_pf = key_mask_data(a.ktracks, a.kint, nr0 + tid, (ent.y & kIntervalBit) != 0);
       pf.fetch(kbase, vbase, nr0, nlen, row_bytes, tid);
     }
 #pragma unroll
@@ -152,7 +153,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
       f32x16 s, dp;
       two_products(s, dp, sK, sV, kc * 32 + l32, qf, df, hi);
       // s[r] = S[query l32][key 32kc + 8(r/4) + 4hi + r%4]
-      if (partial) {
+      if (partial && interval) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kc * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+          const int2 iv = *(const int2*)&sKT[key];
+          s[r] = in_interval(qt.w, iv.x, iv.y) ? s[r] : kNegInf;
+        }
+      } else if (partial) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kc * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
@@ -241,7 +249,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
     int64_t r0;
     sub_bounds(e2, m % nsub, r0, nxt_len, nxt_partial);
     rs.v = 0.f;
-    rs.t = make_int4(-2, -1, -1, 0);
+    rs.t = make_int4(-2, -1, -1, -1);  // rows past len: no sample, no position
     if (tid < kSub) {
       rs.v = tid < nxt_len ? -a.lse[(int64_t)h * a.rows + r0 + tid] * kLog2e : kNegInf;
     } else if (tid < 2 * kSub) {
@@ -272,7 +280,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
       vf[kk] = kvalid ? as_bf16x8(*(const uint4*)(vp + kk * 16)) : as_bf16x8(make_uint4(0, 0, 0, 0));
     }
   }
-  const int4 kt = kvalid ? a.ktracks[key] : make_int4(-1, -1, -1, 0);
+  // this lane's key: its tracks, or its key interval when every key of the
+  // tile has one (kKeyInterval); invalid keys admit no query
+  const bool kin = (it.y & kKeyInterval) != 0;
+  const int4 kt = kvalid ? key_mask_data(a.ktracks, a.kint, key, kin) : make_int4(-1, -1, -1, 0);
   f32x16 dk[4], dv[4];  // dK^T / dV^T[d = 32db + 8(r/4) + 4hi + r%4][key]
 #pragma unroll
   for (int db = 0; db < 4; ++db)
@@ -293,7 +304,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
   // sub-tiles illegal pairs get P = 0; rows past len carry sample -2.
   auto p_and_ds = [&](f32x16& s, f32x16& dp, bf16x8 (&pb)[2], bf16x8 (&dsb)[2], int q0, bool partial,
                       const float* sL, const float* sD, const int4* sQT) {
-    if (partial) {
+    if (partial && kin) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qi = q0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+        s[r] = in_interval(sQT[qi].w, kt.x, kt.y) ? s[r] : kNegInf;
+      }
+    } else if (partial) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int qi = q0 + 8 * (r >> 2) + 4 * hi + (r & 3);

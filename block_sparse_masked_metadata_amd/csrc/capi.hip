@@ -51,9 +51,10 @@ struct Packed {
   std::vector<int4> tracks;
   std::vector<StepLists> steps;
   std::vector<int4> sitems;
+  std::vector<int2> kint;  // key intervals (lo, hi) in plan order
   std::vector<int2> entries;
   // byte offsets in the device buffer
-  int64_t off_tracks = 0, off_items = 0, off_entries = 0, bytes = 0;
+  int64_t off_tracks = 0, off_kint = 0, off_items = 0, off_entries = 0, bytes = 0;
   std::vector<int64_t> off_f, off_b, off_ff;  // off_ff: first list entry of each forward item
   int64_t off_s = 0, off_sf = 0;
 };
@@ -62,10 +63,14 @@ static void pack(const Plan& p, int32_t r, Packed& pk) {
   const int32_t R = p.ranks, T = p.tps;
   const int64_t S = p.shard;
   pk.tracks.resize(p.n);
+  pk.kint.resize(p.n);
   for (int64_t i = 0; i < p.n; ++i) {
     const int32_t t = p.perm[i];
     pk.tracks[i] = make_int4(p.sample[t], p.seg[t], p.noise[t], p.pos[t]);
+    pk.kint[i] = make_int2(p.klo[t], p.khi[t]);
   }
+  // a partner key tile (local tile b of shard j) whose keys all have intervals
+  auto kint_tile = [&](int32_t j, int32_t b) { return p.tile_kint[p.tiles_new[(int64_t)j * T + b]] != 0; };
   auto tlen = [&](int32_t a) { return (int32_t)std::min<int64_t>(kTile, S - (int64_t)a * kTile); };
   // per step row lists: rows[s][a] = (b, class) ascending b
   std::vector<std::vector<std::vector<std::pair<int32_t, uint8_t>>>> rows(
@@ -101,10 +106,12 @@ static void pack(const Plan& p, int32_t r, Packed& pk) {
       if (rows[s][a].empty()) continue;
       const int32_t flags = (first[a] == s ? kFirst : 0) | (last[a] == s ? kLast : 0);
       st.fitems.push_back(make_int4(a, flags, (int32_t)pk.entries.size(), (int32_t)rows[s][a].size()));
+      const int32_t j = ((r - s) % R + R) % R;
       for (auto& bc : rows[s][a]) {
         const int32_t kl = tlen(bc.first);
         const bool part = bc.second == BSM_TILE_PARTIAL || kl < kTile;
-        pk.entries.push_back(make_int2(bc.first * kTile, kl | (part ? kPartialBit : 0)));
+        const bool kin = part && kint_tile(j, bc.first);
+        pk.entries.push_back(make_int2(bc.first * kTile, kl | (part ? kPartialBit : 0) | (kin ? kIntervalBit : 0)));
       }
     }
     std::stable_sort(st.fitems.begin(), st.fitems.end(), by_len);
@@ -114,7 +121,9 @@ static void pack(const Plan& p, int32_t r, Packed& pk) {
       for (auto& bc : rows[s][a]) cols[bc.first].push_back({a, bc.second});
     for (int32_t b = 0; b < T; ++b) {
       if (cols[b].empty()) continue;
-      st.bitems.push_back(make_int4(b, 0, (int32_t)pk.entries.size(), (int32_t)cols[b].size()));
+      const int32_t jb = ((r - s) % R + R) % R;
+      st.bitems.push_back(make_int4(b, kint_tile(jb, b) ? kKeyInterval : 0, (int32_t)pk.entries.size(),
+                                    (int32_t)cols[b].size()));
       for (auto& ac : cols[b]) {
         const int32_t ql = tlen(ac.first);
         const bool part = ac.second == BSM_TILE_PARTIAL || ql < kTile;
@@ -132,8 +141,9 @@ static void pack(const Plan& p, int32_t r, Packed& pk) {
       for (auto& bc : rows[s][a]) {
         const int32_t kl = tlen(bc.first);
         const bool part = bc.second == BSM_TILE_PARTIAL || kl < kTile;
+        const bool kin = part && kint_tile(j, bc.first);
         pk.entries.push_back(make_int2((int32_t)(j * S + (int64_t)bc.first * kTile),
-                                       kl | (part ? kPartialBit : 0)));
+                                       kl | (part ? kPartialBit : 0) | (kin ? kIntervalBit : 0)));
       }
     }
     const int32_t cnt = (int32_t)pk.entries.size() - beg;
@@ -145,6 +155,8 @@ static void pack(const Plan& p, int32_t r, Packed& pk) {
   int64_t off = 0;
   pk.off_tracks = off;
   off = align256(off + p.n * (int64_t)sizeof(int4));
+  pk.off_kint = off;
+  off = align256(off + p.n * (int64_t)sizeof(int2));
   pk.off_items = off;
   pk.off_f.assign(R, 0);
   pk.off_b.assign(R, 0);
@@ -172,6 +184,7 @@ struct bsm_dplan {
   int32_t r = 0, R = 1, tps = 0, window = 0;
   int64_t S = 0, n = 0;
   const int4* tracks = nullptr;
+  const int2* kint = nullptr;
   const int2* entries = nullptr;
   const int4* fitems[64] = {};
   const int2* ffirst[64] = {};
@@ -259,6 +272,14 @@ int bsm_plan_get_info(const bsm_plan* plan, bsm_plan_info* out) {
   out->full_tiles = p.nfull;
   out->partial_tiles = p.npartial;
   out->build_seconds = p.seconds;
+  out->interval_keys = p.interval_keys;
+  return BSM_OK;
+}
+
+int bsm_plan_key_intervals(const bsm_plan* plan, int32_t* lo, int32_t* hi) {
+  if (!plan || !lo || !hi) { set_error("null argument"); return BSM_E_INVALID; }
+  std::memcpy(lo, plan->p.klo.data(), plan->p.n * sizeof(int32_t));
+  std::memcpy(hi, plan->p.khi.data(), plan->p.n * sizeof(int32_t));
   return BSM_OK;
 }
 
@@ -325,6 +346,7 @@ int bsm_dplan_upload(const bsm_plan* plan, int32_t r, void* dev, int64_t bytes, 
     }
     std::vector<char> img(pk.bytes, 0);
     std::memcpy(img.data() + pk.off_tracks, pk.tracks.data(), pk.tracks.size() * sizeof(int4));
+    std::memcpy(img.data() + pk.off_kint, pk.kint.data(), pk.kint.size() * sizeof(int2));
     for (int32_t s = 0; s < p.ranks; ++s) {
       std::memcpy(img.data() + pk.off_f[s], pk.steps[s].fitems.data(), pk.steps[s].fitems.size() * sizeof(int4));
       int2* ff = (int2*)(img.data() + pk.off_ff[s]);
@@ -350,6 +372,7 @@ int bsm_dplan_upload(const bsm_plan* plan, int32_t r, void* dev, int64_t bytes, 
     d->S = p.shard;
     d->n = p.n;
     d->tracks = (const int4*)(base + pk.off_tracks);
+    d->kint = (const int2*)(base + pk.off_kint);
     d->entries = (const int2*)(base + pk.off_entries);
     for (int32_t s = 0; s < p.ranks; ++s) {
       d->fitems[s] = (const int4*)(base + pk.off_f[s]);
@@ -417,6 +440,7 @@ int bsm_fwd_step(const bsm_dplan* d, int32_t s, const bsm_heads* heads, const vo
   a.v = bf(v);
   a.qtracks = d->tracks + (int64_t)d->r * d->S;
   a.ktracks = d->tracks + (int64_t)j * d->S;
+  a.kint = d->kint + (int64_t)j * d->S;
   a.rows = d->S;
   a.oacc = o_acc;
   a.m = m;
@@ -457,6 +481,7 @@ int bsm_fwd_single(const bsm_dplan* d, const bsm_heads* heads, const void* q, co
   a.v = bf(v_all);
   a.qtracks = d->tracks + (int64_t)d->r * d->S;
   a.ktracks = d->tracks;
+  a.kint = d->kint;
   a.rows = d->S;
   a.oacc = o_acc;
   a.m = m;
@@ -506,6 +531,7 @@ int bsm_bwd_step(const bsm_dplan* d, int32_t s, const bsm_heads* heads, const vo
   a.delta = delta;
   a.qtracks = d->tracks + (int64_t)d->r * d->S;
   a.ktracks = d->tracks + (int64_t)j * d->S;
+  a.kint = d->kint + (int64_t)j * d->S;
   a.rows = d->S;
   a.krows = d->S;
   a.dq = dq_acc;

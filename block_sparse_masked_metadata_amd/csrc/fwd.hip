@@ -101,11 +101,21 @@ struct SubTile {
 // the row base of a full sub-tile and the strides of its 4 loads are scalar;
 // `lane_off` = (t/16) * row_bytes + 16 (t%16) is loop-invariant.  Key-row byte
 // offsets stay below 2^32 (a key buffer holds fewer than 2^32 bytes).
+// On partial sub-tiles the key's mask data rides along: its tracks, or with
+// `interval` its key interval (lo, hi) in the first two fields.  Keys past len
+// keep (-1, -1, -1, 0): sample -1 and the empty range [-1, -1) admit no query.
 __device__ inline void fetch_sub(SubTile& t, const char* kbase, const char* vbase,
-                                 const int4* ktracks, int32_t k0, int len, bool partial,
-                                 uint32_t row_bytes, uint32_t lane_off, int tid) {
-  t.kt = make_int4(-1, -1, -1, 0);  // sample -1: no query is legal against it
-  if (partial && tid < len) t.kt = ktracks[k0 + tid];
+                                 const int4* ktracks, const int2* kint, int32_t k0, int len, bool partial,
+                                 bool interval, uint32_t row_bytes, uint32_t lane_off, int tid) {
+  t.kt = make_int4(-1, -1, -1, 0);
+  if (partial && tid < len) {
+    if (interval) {
+      const int2 iv = kint[k0 + tid];
+      t.kt = make_int4(iv.x, iv.y, 0, 0);
+    } else {
+      t.kt = ktracks[k0 + tid];
+    }
+  }
   const uint32_t r0 = (uint32_t)k0 * row_bytes;
   if (len == kSub) {
 #pragma unroll
@@ -141,20 +151,21 @@ __device__ inline void store_sub(const SubTile& t, char* sK, char* sV, int4* sKT
 }
 
 // Sub-tile n of an item: half n%2 of list entry n/2.
-__device__ inline void sub_bounds(const int2 ent, int n, int32_t& k0, int& len, bool& partial) {
+__device__ inline void sub_bounds(const int2 ent, int n, int32_t& k0, int& len, bool& partial, bool& interval) {
   const int half = n & 1;
   const int klen = ent.y & 0xffff;
   k0 = ent.x + half * kSub;
   len = klen - half * kSub;
   len = len < 0 ? 0 : (len > kSub ? kSub : len);
   partial = (ent.y & kPartialBit) != 0;
+  interval = (ent.y & kIntervalBit) != 0;
 }
 
 // S^T = K Q^T for one 64-key sub-tile: s[kb][r] = S[query l32][key 32kb + 8(r/4) + 4hi + r%4],
 // operand reads issued 4 at a time ahead of their MFMAs; on partial sub-tiles
 // illegal pairs (and keys past len) become -inf.
 __device__ inline void scores(f32x16 (&s)[2], const char* sK, const bf16x8 (&qf)[8], const int4* sKT,
-                              const int4 qt, bool partial, int len, int32_t window, int l32, int hi) {
+                              const int4 qt, bool partial, bool interval, int32_t window, int l32, int hi) {
   __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
@@ -174,7 +185,17 @@ __device__ inline void scores(f32x16 (&s)[2], const char* sK, const bf16x8 (&qf)
     }
   }
   __builtin_amdgcn_s_setprio(0);
-  if (partial) {
+  if (partial && interval) {
+    // Key intervals: legal iff lo <= pos_q < hi, one unsigned compare.
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+        const int2 iv = *(const int2*)&sKT[key];
+        s[kb][r] = (uint32_t)(qt.w - iv.x) < (uint32_t)(iv.y - iv.x) ? s[kb][r] : kNegInf;
+      }
+  } else if (partial) {
     // Keys past len carry sample -1 and fail the sample test.  Every lane of
     // a half-wave reads the same key track (an LDS broadcast); no branches.
 #pragma unroll
@@ -242,9 +263,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a) {
   {
     int32_t k0;
     int len;
-    bool part;
-    sub_bounds(ent, 0, k0, len, part);
-    fetch_sub(pf, kbase, vbase, a.ktracks, k0, len, part, row_bytes, lane_off, tid);
+    bool part, kin;
+    sub_bounds(ent, 0, k0, len, part, kin);
+    fetch_sub(pf, kbase, vbase, a.ktracks, a.kint, k0, len, part, kin, row_bytes, lane_off, tid);
   }
 
   // Q^T as the B operand: lane holds query l32, channels [16kk + 8hi, +8).
@@ -299,8 +320,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a) {
   for (int n = 0; n < nsub; ++n) {
     int32_t k0;
     int len;
-    bool partial;
-    sub_bounds(ent, n, k0, len, partial);
+    bool partial, interval;
+    sub_bounds(ent, n, k0, len, partial, interval);
     __syncthreads();  // sub-tile n is in LDS
     const bool more = n + 1 < nsub;
     if (more) {
@@ -316,13 +337,13 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a) {
       }
       int32_t nk0;
       int nlen;
-      bool npart;
-      sub_bounds(ent, n + 1, nk0, nlen, npart);
-      fetch_sub(pf, kbase, vbase, a.ktracks, nk0, nlen, npart, row_bytes, lane_off, tid);
+      bool npart, nkin;
+      sub_bounds(ent, n + 1, nk0, nlen, npart, nkin);
+      fetch_sub(pf, kbase, vbase, a.ktracks, a.kint, nk0, nlen, npart, nkin, row_bytes, lane_off, tid);
     }
 
     f32x16 s[2];
-    scores(s, sK, qf, sKT, qt, partial, len, a.window, l32, hi);
+    scores(s, sK, qf, sKT, qt, partial, interval, a.window, l32, hi);
 
     // Online softmax in base-2 units against a lazily updated reference mref.
     // Common case: exponentiate against the current reference; every p stays
@@ -337,7 +358,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a) {
       ls = exp_sum(s, a.scale_log2, -mref);
       if (__any(!(ls < kSumCap))) {
         fast = false;
-        scores(s, sK, qf, sKT, qt, partial, len, a.window, l32, hi);
+        scores(s, sK, qf, sKT, qt, partial, interval, a.window, l32, hi);
       }
     }
     if (!fast) {

@@ -13,12 +13,20 @@ constexpr int kTile = 128;      // query and key tile tokens
 //   x = tile index (query tile for forward / dQ, key tile for dK/dV)
 //   y = flags (kFirst: the tile's first step with work, kLast: its last)
 //   z = first entry of the tile's list, w = number of entries
-enum : int32_t { kFirst = 1, kLast = 2 };
+//   kKeyInterval (backward column items): every key of the tile has a key
+//   interval, so partial pairs test lo <= pos_q < hi
+enum : int32_t { kFirst = 1, kLast = 2, kKeyInterval = 4 };
 
 // List entry (int2): x = first row of the partner tile in the partner buffer,
 //                    y = valid rows of the partner tile | (partial << 16)
 // A partner tile with fewer than 128 valid rows is always marked partial.
+// kIntervalBit (with the partial bit, forward and dQ lists): every key of the
+// partner tile has a key interval.
 constexpr int32_t kPartialBit = 1 << 16;
+constexpr int32_t kIntervalBit = 1 << 17;
+
+// Key interval of a token (int2): the queries it is legal for are exactly
+// those with x <= pos < y; y < x when it has none (the planner's key_interval).
 
 // Per-token tracks in plan order (int4): sample, seg, noise, pos.
 // bf16 tensors are passed as raw 16-bit patterns (uint16_t).
@@ -35,6 +43,7 @@ struct FwdArgs {
   const uint16_t* v;
   const int4* qtracks;      // tracks of the query shard rows
   const int4* ktracks;      // tracks of the key buffer rows
+  const int2* kint;         // key intervals of the key buffer rows
   int64_t rows;             // S: query shard rows (state stride / ragged bound)
   float* oacc;              // [S, Hq, d] fp32
   float* m;                 // [Hq, S]
@@ -60,6 +69,7 @@ struct BwdArgs {
   const float* delta;         // [Hq, S]
   const int4* qtracks;
   const int4* ktracks;
+  const int2* kint;           // key intervals of the key buffer rows
   int64_t rows;               // S (query rows)
   int64_t krows;              // key rows of the k/v buffers
   float* dq;                  // [S, Hq, d]

@@ -9,6 +9,11 @@
 //                                         each rank's blocks in sequence order
 //   section 04, "Planning cost"        - built once per batch on CPU threads
 //
+// Key intervals: for each key the planner also derives the set of queries it
+// is legal for from the track structure (its causal window, the runs of its
+// seg id, the run of its noise id, its sample); when that set is one range of
+// positions the kernels test partial tiles with two compares per pair.
+//
 // Classification is exact: a tile pair is FULL when every valid token pair is
 // legal, EMPTY when none is, PARTIAL otherwise.  Per-tile summaries (min/max of
 // every track) decide a pair only when they prove it; every other candidate
@@ -24,6 +29,8 @@
 #include <chrono>
 #include <numeric>
 #include <thread>
+#include <unordered_map>
+#include <utility>
 
 namespace bsm {
 
@@ -121,6 +128,74 @@ int validate(const bsm_plan_desc& d) {
     }
   }
   return BSM_OK;
+}
+
+using Run = std::pair<int64_t, int64_t>;  // token index range [first, second)
+
+// Maximal runs of each id >= 0 of a track, in index order.
+std::unordered_map<int32_t, std::vector<Run>> id_runs(const std::vector<int32_t>& t) {
+  std::unordered_map<int32_t, std::vector<Run>> runs;
+  const int64_t n = (int64_t)t.size();
+  for (int64_t i = 0; i < n;) {
+    int64_t j = i + 1;
+    while (j < n && t[j] == t[i]) ++j;
+    if (t[i] >= 0) runs[t[i]].push_back({i, j});
+    i = j;
+  }
+  return runs;
+}
+
+// Sorted, merged union of ranges (touching ranges join).
+void merge_runs(std::vector<Run>& v) {
+  std::sort(v.begin(), v.end());
+  size_t k = 0;
+  for (size_t i = 0; i < v.size(); ++i) {
+    if (k && v[i].first <= v[k - 1].second)
+      v[k - 1].second = std::max(v[k - 1].second, v[i].second);
+    else
+      v[k++] = v[i];
+  }
+  v.resize(k);
+}
+
+// The legal query set of key k as index ranges: (causal window U span of its
+// seg id) within its sample, restricted to the noise span of its noise id.
+// It is one range of positions whenever it is one range of indices, since
+// pos rises strictly with the index.
+void key_interval(const Plan& p, int64_t k, int64_t s0, int64_t s1,
+                  const std::unordered_map<int32_t, std::vector<Run>>& seg_runs,
+                  const std::unordered_map<int32_t, std::vector<Run>>& noise_runs, std::vector<Run>& u,
+                  int32_t& lo, int32_t& hi) {
+  u.clear();
+  // causal: 0 <= pos_q - pos_k < W  <=>  q in [k, first index with pos >= pos_k + W)
+  const int64_t lim = (int64_t)p.pos[k] + p.window;
+  const int64_t c1 = std::lower_bound(p.pos.begin() + k, p.pos.begin() + s1, lim,
+                                      [](int32_t a, int64_t b) { return (int64_t)a < b; }) -
+                     p.pos.begin();
+  u.push_back({k, c1});
+  if (p.seg[k] >= 0)
+    for (const Run& r : seg_runs.at(p.seg[k])) {
+      const int64_t a = std::max(r.first, s0), b = std::min(r.second, s1);
+      if (a < b) u.push_back({a, b});
+    }
+  merge_runs(u);
+  if (p.noise[k] >= 0) {
+    std::vector<Run> w;
+    for (const Run& r : noise_runs.at(p.noise[k]))
+      for (const Run& x : u) {
+        const int64_t a = std::max(r.first, x.first), b = std::min(r.second, x.second);
+        if (a < b) w.push_back({a, b});
+      }
+    merge_runs(w);
+    u.swap(w);
+  }
+  if (u.size() == 1) {
+    lo = p.pos[u[0].first];
+    hi = p.pos[u[0].second - 1] + 1;
+  } else {
+    lo = 0;
+    hi = -1;
+  }
 }
 
 template <class F>
@@ -273,6 +348,39 @@ int build_plan(const bsm_plan_desc& d, Plan& p) {
   p.perm.reserve(d.n);
   for (int32_t i = 0; i < nt; ++i)
     for (int64_t x = p.tstart[p.tiles_new[i]]; x < p.tend[p.tiles_new[i]]; ++x) p.perm.push_back((int32_t)x);
+
+  // key intervals (MARBLE section 03, "Block classification": a partial tile
+  // can test one position range per key instead of the full predicate)
+  {
+    const auto seg_runs = id_runs(p.seg), noise_runs = id_runs(p.noise);
+    p.klo.assign(d.n, 0);
+    p.khi.assign(d.n, -1);
+    std::vector<int64_t> s0(d.n), s1(d.n);
+    for (int64_t i = 0; i < d.n;) {
+      int64_t j = i + 1;
+      while (j < d.n && p.sample[j] == p.sample[i]) ++j;
+      for (int64_t x = i; x < j; ++x) {
+        s0[x] = i;
+        s1[x] = j;
+      }
+      i = j;
+    }
+    const int64_t chunk = 4096, nchunks = (d.n + chunk - 1) / chunk;
+    parallel_for(nchunks, threads, [&](int64_t c) {
+      std::vector<Run> u;
+      const int64_t b = std::min(d.n, (c + 1) * chunk);
+      for (int64_t k = c * chunk; k < b; ++k)
+        key_interval(p, k, s0[k], s1[k], seg_runs, noise_runs, u, p.klo[k], p.khi[k]);
+    });
+    p.tile_kint.assign(nt, 1);
+    p.interval_keys = 0;
+    for (int32_t t = 0; t < nt; ++t)
+      for (int64_t x = p.tstart[t]; x < p.tend[t]; ++x) {
+        const bool ok = p.khi[x] >= p.klo[x];
+        p.interval_keys += ok;
+        if (!ok) p.tile_kint[t] = 0;
+      }
+  }
 
   // busiest rank: most legal pairs over all keys, ties -> lowest rank
   int64_t best = -1;

@@ -32,6 +32,11 @@ struct Plan {
   std::vector<int32_t> perm;       // new token -> original token
   // tracks, original order
   std::vector<int32_t> sample, seg, noise, pos;
+  // Key intervals, original order: the queries key k is legal for are exactly
+  // the positions [klo[k], khi[k]), or the key has no such range (khi < klo).
+  std::vector<int32_t> klo, khi;
+  std::vector<uint8_t> tile_kint;  // original tile: every key has an interval
+  int64_t interval_keys = 0;
   int32_t busiest = 0;
   int64_t total_pairs = 0, candidates = 0, nfull = 0, npartial = 0;
   double seconds = 0;

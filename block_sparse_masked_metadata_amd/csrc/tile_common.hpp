@@ -143,5 +143,20 @@ __device__ inline void sub_bounds(const int2 ent, int n, int64_t& r0, int& len, 
   partial = (ent.y & kPartialBit) != 0;
 }
 
+// Mask data of a key for a partial sub-tile: its tracks, or (lo, hi, 0, 0)
+// when the entry marks key intervals.
+__device__ inline int4 key_mask_data(const int4* ktracks, const int2* kint, int64_t row, bool interval) {
+  if (interval) {
+    const int2 iv = kint[row];
+    return make_int4(iv.x, iv.y, 0, 0);
+  }
+  return ktracks[row];
+}
+
+// lo <= pos < hi as one unsigned compare (positions and bounds are int32 >= -1).
+__device__ inline bool in_interval(int32_t pos, int32_t lo, int32_t hi) {
+  return (uint32_t)(pos - lo) < (uint32_t)(hi - lo);
+}
+
 }  // namespace dev
 }  // namespace bsm

@@ -54,6 +54,10 @@ class Plan:
     def block_cost(self):
         return C.bsm_plan_block_cost(self.handle)
 
+    def key_intervals(self):
+        """(lo, hi) per key in the original order; hi < lo: no single range."""
+        return C.bsm_plan_key_intervals(self.handle)
+
     def close(self):
         if self.handle:
             C.bsm_plan_free(self.handle)

@@ -143,6 +143,7 @@ typedef struct {
   int64_t full_tiles;        /* tile pairs classified FULL (all ranks/steps)   */
   int64_t partial_tiles;     /* tile pairs classified PARTIAL                  */
   double build_seconds;      /* wall time of bsm_plan_build                    */
+  int64_t interval_keys;     /* keys whose legal queries form one pos range    */
 } bsm_plan_info;
 
 int bsm_plan_get_info(const bsm_plan* plan, bsm_plan_info* out);
@@ -162,6 +163,17 @@ int bsm_plan_step_map(const bsm_plan* plan, int32_t r, int32_t s, uint8_t* map,
 
 /* pairs[r * R + s] = legal pairs of rank r at step s (host int64[R*R]). */
 int bsm_plan_pairs(const bsm_plan* plan, int64_t* pairs);
+
+/*
+ * Key intervals (MARBLE section 03, "Block classification": a partial tile can
+ * test one range per key in a chosen coordinate).  For every key k in the
+ * ORIGINAL order, when the queries k is legal for are exactly those with
+ * lo[k] <= pos < hi[k] (the union of its causal window and the spans of its
+ * seg id, within its sample and the span of its noise id, is one run of
+ * tokens), lo/hi receive that range; otherwise lo[k] = 0, hi[k] = -1 and the
+ * kernels keep the four-track predicate for its tiles.  Host int32[n] each.
+ */
+int bsm_plan_key_intervals(const bsm_plan* plan, int32_t* lo, int32_t* hi);
 
 /* ====================================================================== *
  *  Device plan: one rank's lists, packed into caller-owned device memory. *

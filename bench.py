@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--fwd-only", action="store_true", help="time only the forward pass")
     ap.add_argument("--single", action="store_true",
                     help="diagnostic: time the one-launch single pass instead of the ring steps")
+    ap.add_argument("--merge", choices=["carry", "fp32", "bf16"], default="carry",
+                    help="accuracy controls: time per-step merges instead of the fp32 carry "
+                         "(forward only; no roofline)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
     return ap.parse_args()
@@ -188,9 +191,18 @@ def main():
     dks = [torch.zeros(S, lay.hkv, d, dtype=torch.float32, device="cuda") for _ in range(R)]
     dvs = [torch.zeros(S, lay.hkv, d, dtype=torch.float32, device="cuda") for _ in range(R)]
     fwd_steps = [s for s in range(R) if dp.info["fwd_items"][s] > 0]
-    do_bwd = not args.fwd_only
+    do_bwd = not args.fwd_only and args.merge == "carry"
 
     def forward(events=None):
+        if args.merge != "carry":
+            if events is not None:
+                events.append(torch.cuda.Event(enable_timing=True))
+                events[-1].record()
+            bsm.fwd_ring_merged(dp, hd, q, ks, vs, args.merge)
+            if events is not None:
+                events.append(torch.cuda.Event(enable_timing=True))
+                events[-1].record()
+            return
         if args.single:
             if events is not None:
                 events.append(torch.cuda.Event(enable_timing=True))
@@ -260,7 +272,7 @@ def main():
     fwd_flops = 4 * d * lay.hq * total_pairs
     bwd_flops = 10 * d * lay.hq * total_pairs
     fwd_tflops = fwd_flops / (fwd_ms * 1e-3) / 1e12
-    nlaunch = 1 if args.single else len(fwd_steps)
+    nlaunch = 1 if args.single or args.merge != "carry" else len(fwd_steps)
     per_launch_flops = fwd_flops / nlaunch
     per_launch_bytes = sum(fwd_algorithmic_bytes(plan, r, R, S, lay.hq, lay.hkv, d, args.single)) / nlaunch
     # roofline of the forward kernel: whichever of the MFMA and HBM times of its
@@ -320,10 +332,13 @@ def main():
                      "hbm_frac": round(hbm_gbs / PEAK_HBM_GBS, 4),
                      "avg_launch_us": round(avg_launch_ms * 1e3, 2),
                      "launches_per_step": nlaunch},
-        "mode": "single-pass diagnostic" if args.single else "ring",
+        "mode": ("single-pass diagnostic" if args.single else
+                 "ring" if args.merge == "carry" else f"ring, per-step {args.merge} merge (accuracy control)"),
         "planner_s": round(plan_s, 4),
         "wall_s": round(wall, 3),
     }
+    if args.merge != "carry":
+        out["roofline"] = None  # the timed forward includes fills and merge kernels
     if not args.no_cpu_baseline:
         qc, kc, vc = (t.cpu() for t in full[:3])
         out["cpu_baseline"] = cpu_baseline(lay, None, rows, qc, kc, vc, args.cpu_seconds)

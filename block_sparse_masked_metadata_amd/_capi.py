@@ -33,6 +33,7 @@ BSM_WINDOW_INF = 0x7FFFFFFF
 BSM_ORDER_CONTIGUOUS, BSM_ORDER_PTRR, BSM_ORDER_EXPLICIT = 0, 1, 2
 BSM_TILE_EMPTY, BSM_TILE_PARTIAL, BSM_TILE_FULL = 0, 1, 2
 BSM_FWD_KEEP_STATE = 1
+BSM_FWD_STEP_ONLY = 2
 
 ORDERS = {"contiguous": BSM_ORDER_CONTIGUOUS, "ptrr": BSM_ORDER_PTRR,
           "explicit": BSM_ORDER_EXPLICIT}
@@ -42,7 +43,8 @@ EXPORTS = [
     "bsm_plan_permutation", "bsm_plan_block_cost", "bsm_plan_step_map", "bsm_plan_pairs",
     "bsm_plan_key_intervals",
     "bsm_dplan_bytes", "bsm_dplan_upload", "bsm_dplan_free", "bsm_dplan_get_info",
-    "bsm_fwd_step", "bsm_fwd_single", "bsm_bwd_prep", "bsm_bwd_step",
+    "bsm_fwd_step", "bsm_fwd_single", "bsm_fwd_merge_bf16", "bsm_fwd_merge_fp32",
+    "bsm_bwd_prep", "bsm_bwd_step",
 ]
 
 
@@ -100,6 +102,8 @@ _sig = {
                                _P, _P, C.c_int32, _P]),
     "bsm_fwd_single": (C.c_int, [_P, C.POINTER(bsm_heads), _P, _P, _P, _P, _P, _P, _P, _P,
                                  C.c_int32, _P]),
+    "bsm_fwd_merge_bf16": (C.c_int, [C.POINTER(bsm_heads), C.c_int64, _P, _P, _P, _P, _P]),
+    "bsm_fwd_merge_fp32": (C.c_int, [C.POINTER(bsm_heads), C.c_int64, _P, _P, _P, _P, _P, _P, _P]),
     "bsm_bwd_prep": (C.c_int, [C.POINTER(bsm_heads), C.c_int64, _P, _P, _P, _P]),
     "bsm_bwd_step": (C.c_int, [_P, C.c_int32, C.POINTER(bsm_heads), _P, _P, _P, _P, _P, _P,
                                _P, _P, _P, _P]),
@@ -229,6 +233,14 @@ def bsm_fwd_step(dplan, s, heads, q, k, v, o_acc, m, l, o, lse, flags, stream):
 def bsm_fwd_single(dplan, heads, q, k_all, v_all, o_acc, m, l, o, lse, flags, stream):
     _check(_lib.bsm_fwd_single(dplan, C.byref(heads), q, k_all, v_all, o_acc, m, l, o, lse,
                                int(flags), stream))
+
+
+def bsm_fwd_merge_bf16(heads, rows, o_run, lse_run, o_s, lse_s, stream):
+    _check(_lib.bsm_fwd_merge_bf16(C.byref(heads), int(rows), o_run, lse_run, o_s, lse_s, stream))
+
+
+def bsm_fwd_merge_fp32(heads, rows, o_run, lse_run, acc_s, m_s, l_s, o_bf16, stream):
+    _check(_lib.bsm_fwd_merge_fp32(C.byref(heads), int(rows), o_run, lse_run, acc_s, m_s, l_s, o_bf16, stream))
 
 
 def bsm_bwd_prep(heads, rows, o, dout, delta, stream):

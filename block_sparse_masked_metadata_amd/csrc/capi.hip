@@ -450,6 +450,7 @@ int bsm_fwd_step(const bsm_dplan* d, int32_t s, const bsm_heads* heads, const vo
   a.scale_log2 = heads->scale * 1.44269504088896340736f;
   a.window = d->window;
   a.keep_state = keep ? 1 : 0;
+  a.step_only = (flags & BSM_FWD_STEP_ONLY) != 0 ? 1 : 0;
   hipStream_t st = (hipStream_t)stream;
   return hip_status(launch_fwd(a, st), "forward step launch", st);
 }
@@ -491,8 +492,31 @@ int bsm_fwd_single(const bsm_dplan* d, const bsm_heads* heads, const void* q, co
   a.scale_log2 = heads->scale * 1.44269504088896340736f;
   a.window = d->window;
   a.keep_state = keep ? 1 : 0;
+  a.step_only = (flags & BSM_FWD_STEP_ONLY) != 0 ? 1 : 0;
   hipStream_t st = (hipStream_t)stream;
   return hip_status(launch_fwd(a, st), "forward single launch", st);
+}
+
+int bsm_fwd_merge_bf16(const bsm_heads* heads, int64_t rows, void* o_run, float* lse_run, const void* o_s,
+                       const float* lse_s, void* stream) {
+  int rc = check_heads(heads);
+  if (rc) return rc;
+  if (rows < 1) { set_error("rows must be >= 1"); return BSM_E_INVALID; }
+  if (!o_run || !lse_run || !o_s || !lse_s) { set_error("null tensor pointer"); return BSM_E_INVALID; }
+  hipStream_t st = (hipStream_t)stream;
+  return hip_status(launch_merge_bf16(rows, heads->hq, (uint16_t*)o_run, lse_run, bf(o_s), lse_s, st),
+                    "bf16 merge launch", st);
+}
+
+int bsm_fwd_merge_fp32(const bsm_heads* heads, int64_t rows, float* o_run, float* lse_run, const float* acc_s,
+                       const float* m_s, const float* l_s, void* o_bf16, void* stream) {
+  int rc = check_heads(heads);
+  if (rc) return rc;
+  if (rows < 1) { set_error("rows must be >= 1"); return BSM_E_INVALID; }
+  if (!o_run || !lse_run || !acc_s || !m_s || !l_s) { set_error("null tensor pointer"); return BSM_E_INVALID; }
+  hipStream_t st = (hipStream_t)stream;
+  return hip_status(launch_merge_fp32(rows, heads->hq, o_run, lse_run, acc_s, m_s, l_s, (uint16_t*)o_bf16, st),
+                    "fp32 merge launch", st);
 }
 
 int bsm_bwd_prep(const bsm_heads* heads, int64_t rows, const void* o, const void* dout,

@@ -234,7 +234,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a) {
   // Prologue in two memory round trips: the item record and its first list
   // entry (scalar loads, side by side), then every other load at once: the
   // list, the first K/V sub-tile, Q, the query tracks and the state.
-  const int4 it = a.items[item];
+  int4 it = a.items[item];
+  if (a.step_only) it.y = kFirst | kLast;  // this step's keys alone
   int2 ent = a.first[item];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -438,6 +439,72 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a) {
   }
 }
 
+// ---- Accuracy controls (MARBLE section 03, "Exact ring attention
+// accumulation", against the per-step merges it compares with) ----
+// One step's partial result merged into a running one, per (row, head):
+//   lse = log(e^lse_run + e^lse_s),  O = O_run e^(lse_run - lse) + O_s e^(lse_s - lse).
+// Threads own 8 channels; 16 lanes cover one (row, head).  Rows the step did
+// not reach (lse_s = -inf, or l = 0) keep the running values.
+__device__ inline void merge_weights(float lr, float ls, float& wr, float& ws, float& lnew) {
+  const float mx = fmaxf(lr, ls);
+  const float er = expf(lr - mx), es = expf(ls - mx);  // lr = -inf -> er = 0
+  lnew = mx + logf(er + es);
+  wr = expf(lr - lnew);
+  ws = expf(ls - lnew);
+}
+
+__global__ __launch_bounds__(256) void merge_bf16_kernel(int64_t pairs, int64_t rows, int32_t hq,
+                                                         unsigned short* o_run, float* lse_run,
+                                                         const unsigned short* o_s, const float* lse_s) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t pair = gid >> 4;
+  if (pair >= pairs) return;
+  const int64_t row = pair / hq;
+  const int32_t h = (int32_t)(pair % hq);
+  const int64_t li = (int64_t)h * rows + row;
+  const float ls = lse_s[li];
+  if (ls == kNegInf) return;
+  const float lr = lse_run[li];
+  float wr, ws, lnew;
+  merge_weights(lr, ls, wr, ws, lnew);
+  const bf16x8 a8 = as_bf16x8(*(const uint4*)(o_run + gid * 8));
+  const bf16x8 b8 = as_bf16x8(*(const uint4*)(o_s + gid * 8));
+  bf16x8 r8;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r8[i] = (__bf16)((lr == kNegInf ? 0.f : wr * (float)a8[i]) + ws * (float)b8[i]);
+  *(uint4*)(o_run + gid * 8) = __builtin_bit_cast(uint4, r8);
+  if ((gid & 15) == 0) lse_run[li] = lnew;
+}
+
+__global__ __launch_bounds__(256) void merge_fp32_kernel(int64_t pairs, int64_t rows, int32_t hq, float* o_run,
+                                                         float* lse_run, const float* acc_s, const float* m_s,
+                                                         const float* l_s, unsigned short* o_bf16) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t pair = gid >> 4;
+  if (pair >= pairs) return;
+  const int64_t row = pair / hq;
+  const int32_t h = (int32_t)(pair % hq);
+  const int64_t li = (int64_t)h * rows + row;
+  const float l = l_s[li];
+  float* orp = o_run + gid * 8;
+  if (l > 0.f) {
+    const float ls = (m_s[li] + log2f(l)) * kLn2;  // the step's LSE (m in base-2 units)
+    const float lr = lse_run[li];
+    float wr, ws, lnew;
+    merge_weights(lr, ls, wr, ws, lnew);
+    const float* ap = acc_s + gid * 8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) orp[i] = (lr == kNegInf ? 0.f : wr * orp[i]) + ws * (ap[i] / l);
+    if ((gid & 15) == 0) lse_run[li] = lnew;
+  }
+  if (o_bf16) {
+    bf16x8 r8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r8[i] = (__bf16)orp[i];
+    *(uint4*)(o_bf16 + gid * 8) = __builtin_bit_cast(uint4, r8);
+  }
+}
+
 __global__ __launch_bounds__(256) void bwd_prep_kernel(int64_t pairs, int64_t rows, int32_t hq,
                                                        const unsigned short* o,
                                                        const unsigned short* dout, float* delta) {
@@ -469,6 +536,24 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   const int64_t blocks = (int64_t)a.nitems * a.hq;
   if (blocks <= 0) return hipSuccess;
   hipLaunchKernelGGL(fwd_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_bf16(int64_t rows, int32_t hq, uint16_t* o_run, float* lse_run, const uint16_t* o_s,
+                             const float* lse_s, hipStream_t stream) {
+  const int64_t pairs = rows * hq;
+  const int64_t blocks = (pairs * 16 + 255) / 256;
+  hipLaunchKernelGGL(merge_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, pairs, rows, hq,
+                     (unsigned short*)o_run, lse_run, (const unsigned short*)o_s, lse_s);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_fp32(int64_t rows, int32_t hq, float* o_run, float* lse_run, const float* acc_s,
+                             const float* m_s, const float* l_s, uint16_t* o_bf16, hipStream_t stream) {
+  const int64_t pairs = rows * hq;
+  const int64_t blocks = (pairs * 16 + 255) / 256;
+  hipLaunchKernelGGL(merge_fp32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, pairs, rows, hq, o_run,
+                     lse_run, acc_s, m_s, l_s, (unsigned short*)o_bf16);
   return hipGetLastError();
 }
 

@@ -53,6 +53,7 @@ struct FwdArgs {
   float scale_log2;         // scale * log2(e)
   int32_t window;
   int32_t keep_state;
+  int32_t step_only;        // ignore the carried state and finalize every item
 };
 
 struct BwdArgs {
@@ -81,6 +82,11 @@ struct BwdArgs {
 };
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+// Accuracy controls: merge one step's partial result into a running one.
+hipError_t launch_merge_bf16(int64_t rows, int32_t hq, uint16_t* o_run, float* lse_run, const uint16_t* o_s,
+                             const float* lse_s, hipStream_t stream);
+hipError_t launch_merge_fp32(int64_t rows, int32_t hq, float* o_run, float* lse_run, const float* acc_s,
+                             const float* m_s, const float* l_s, uint16_t* o_bf16, hipStream_t stream);
 hipError_t launch_bwd_prep(int64_t rows, int32_t hq, const uint16_t* o,
                            const uint16_t* dout, float* delta, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);

@@ -136,6 +136,44 @@ def fwd_ring(dp: DevicePlan, hd, q, k_shards, v_shards, state=None, out=None, ke
     return o, lse, state
 
 
+def fwd_ring_merged(dp: DevicePlan, hd, q, k_shards, v_shards, mode="bf16", steps=None):
+    """Accuracy controls: each ring step finishes its own keys (BSM_FWD_STEP_ONLY)
+    and is merged into a running result, instead of carrying (O_acc, m, l).
+
+    mode "bf16": per-step normalized bf16 O_s and LSE_s, merged into a bf16 O.
+    mode "fp32": per-step unnormalized fp32 partials, merged into an fp32 O.
+    Returns (o bf16 [S, Hq, d], lse fp32 [Hq, S])."""
+    import torch
+    rows, dev = dp.rows, q.device
+    shape = (rows, hd.hq, hd.d)
+    lse_run = torch.full((hd.hq, rows), -math.inf, dtype=torch.float32, device=dev)
+    acc, m, l = new_state(rows, hd.hq, hd.d, dev)
+    todo = [s for s in (range(dp.ranks) if steps is None else steps) if dp.info["fwd_items"][s] > 0]
+    if mode == "bf16":
+        o_run = torch.zeros(shape, dtype=torch.bfloat16, device=dev)
+        o_s = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+        lse_s = torch.empty(hd.hq, rows, dtype=torch.float32, device=dev)
+        for s in todo:
+            j = (dp.rank - s) % dp.ranks
+            lse_s.fill_(-math.inf)  # rows this step does not reach
+            C.bsm_fwd_step(dp.handle, s, hd, _ptr(q), _ptr(k_shards[j]), _ptr(v_shards[j]), _ptr(acc),
+                           _ptr(m), _ptr(l), _ptr(o_s), _ptr(lse_s), C.BSM_FWD_STEP_ONLY, _stream())
+            C.bsm_fwd_merge_bf16(hd, rows, _ptr(o_run), _ptr(lse_run), _ptr(o_s), _ptr(lse_s), _stream())
+        return o_run, lse_run
+    if mode != "fp32":
+        raise ValueError("mode must be 'bf16' or 'fp32'")
+    o_run = torch.zeros(shape, dtype=torch.float32, device=dev)
+    o = torch.zeros(shape, dtype=torch.bfloat16, device=dev)
+    for i, s in enumerate(todo):
+        j = (dp.rank - s) % dp.ranks
+        l.fill_(0.0)  # rows this step does not reach
+        C.bsm_fwd_step(dp.handle, s, hd, _ptr(q), _ptr(k_shards[j]), _ptr(v_shards[j]), _ptr(acc), _ptr(m),
+                       _ptr(l), None, None, C.BSM_FWD_STEP_ONLY | C.BSM_FWD_KEEP_STATE, _stream())
+        C.bsm_fwd_merge_fp32(hd, rows, _ptr(o_run), _ptr(lse_run), _ptr(acc), _ptr(m), _ptr(l),
+                             _ptr(o) if i == len(todo) - 1 else None, _stream())
+    return o, lse_run
+
+
 def fwd_single(dp: DevicePlan, hd, q, k_all, v_all, keep_state=False, out=None):
     """Single pass over all shards (k_all/v_all = shards concatenated in plan order)."""
     import torch

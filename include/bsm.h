@@ -64,8 +64,13 @@ enum { BSM_TILE_EMPTY = 0, BSM_TILE_PARTIAL = 1, BSM_TILE_FULL = 2 };
 
 /* Flags of the forward entry points. */
 enum {
-  BSM_FWD_KEEP_STATE = 1   /* never finalize: always store (O_acc, m, l),
+  BSM_FWD_KEEP_STATE = 1,  /* never finalize: always store (O_acc, m, l),
                               even on a tile's last step; O and LSE untouched */
+  BSM_FWD_STEP_ONLY = 2    /* accuracy controls: ignore the carried state and
+                              treat every tile as on its first and last step,
+                              so the call's result covers this step's keys
+                              only (with KEEP_STATE: their unnormalized
+                              O_acc, m, l; without: normalized bf16 O, LSE) */
 };
 
 /* Thread-local text of the last failure on the calling thread ("" if none). */
@@ -266,6 +271,28 @@ int bsm_fwd_single(const bsm_dplan* dplan, const bsm_heads* heads,
                    const void* q, const void* k_all, const void* v_all,
                    float* o_acc, float* m, float* l, void* o, float* lse,
                    int32_t flags, void* stream);
+
+/*
+ * Accuracy controls (MARBLE section 03, "Exact ring attention accumulation":
+ * the fp32 carry of (O_acc, m, l) against per-step merges).  A ring can also
+ * finish every step (BSM_FWD_STEP_ONLY) and merge the step's normalized
+ * partial into a running result:
+ *   lse = ln(e^lse_run + e^lse_s),  O = O_run e^(lse_run - lse) + O_s e^(lse_s - lse).
+ * bsm_fwd_merge_bf16: o_run, o_s bf16 [rows, Hq, d]; lse_run, lse_s fp32
+ *   [Hq, rows] (natural log); the merged O is rounded to bf16 every step.
+ * bsm_fwd_merge_fp32: o_run fp32 [rows, Hq, d] normalized; the step is given
+ *   as its unnormalized fp32 (acc_s, m_s, l_s) from BSM_FWD_STEP_ONLY |
+ *   BSM_FWD_KEEP_STATE; o_bf16 (may be NULL) receives RNE bf16 of the merged O.
+ * Rows the step did not reach must read lse_s = -inf (bf16) or l_s = 0
+ * (fp32): the caller fills them before the step; they keep the running values.
+ * Start from lse_run = -inf (o_run is then ignored).  Stream-ordered on
+ * `stream`; rows >= 1; heads as for the forward.
+ */
+int bsm_fwd_merge_bf16(const bsm_heads* heads, int64_t rows, void* o_run, float* lse_run,
+                       const void* o_s, const float* lse_s, void* stream);
+int bsm_fwd_merge_fp32(const bsm_heads* heads, int64_t rows, float* o_run, float* lse_run,
+                       const float* acc_s, const float* m_s, const float* l_s, void* o_bf16,
+                       void* stream);
 
 /* ====================================================================== *
  *  Backward.                                                              *

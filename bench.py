@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--merge", choices=["carry", "fp32", "bf16"], default="carry",
                     help="accuracy controls: time per-step merges instead of the fp32 carry "
                          "(forward only; no roofline)")
+    ap.add_argument("--fetch", action="store_true",
+                    help="sparse fetch: contiguous chunks, one pass over the rank's shard and its "
+                         "fetched remote tiles (forward only; the fetch itself is not timed)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
     return ap.parse_args()
@@ -117,6 +120,23 @@ def fwd_algorithmic_bytes(plan, r, R, S, hq, hkv, d, single=False):
     return out
 
 
+def sparse_fetch_summary(lay, plan, r):
+    """Remote key tiles the measured rank needs under this plan's order and
+    under contiguous chunks (MARBLE section 04: the sparse all-to-all moves only
+    those; the ring moves all R - 1 remote shards)."""
+    import dataclasses
+    import block_sparse_masked_metadata_amd as bsm
+    R, T = plan.info["ranks"], plan.info["tiles_per_shard"]
+    out = {"remote_tiles": (R - 1) * T}
+    _, out[f"needed_{lay.order}"] = plan.fetch_set(r)
+    if lay.order != "contiguous":
+        cp = bsm.Plan.from_layout(dataclasses.replace(lay, order="contiguous"))
+        _, out["needed_contiguous"] = cp.fetch_set(cp.info["busiest_rank"])
+    out["bytes_avoided_contiguous"] = round(1 - out["needed_contiguous"] / out["remote_tiles"], 4) \
+        if out["remote_tiles"] else 0.0
+    return out
+
+
 def cpu_baseline(lay, plan_pairs_fn, rows_all, q, k, v, target_s):
     """Time the fp64 oracle on whole samples of the measured rank's share."""
     from oracle import attention as oatt
@@ -163,6 +183,9 @@ def main():
     from workloads import config, qkv
 
     lay = config(args.config)
+    if args.fetch:
+        import dataclasses
+        lay = dataclasses.replace(lay, order="contiguous")
     t0 = time.perf_counter()
     plan = bsm.Plan.from_layout(lay)
     plan_s = time.perf_counter() - t0
@@ -191,9 +214,21 @@ def main():
     dks = [torch.zeros(S, lay.hkv, d, dtype=torch.float32, device="cuda") for _ in range(R)]
     dvs = [torch.zeros(S, lay.hkv, d, dtype=torch.float32, device="cuda") for _ in range(R)]
     fwd_steps = [s for s in range(R) if dp.info["fwd_items"][s] > 0]
-    do_bwd = not args.fwd_only and args.merge == "carry"
+    do_bwd = not args.fwd_only and args.merge == "carry" and not args.fetch
+
+    if args.fetch:
+        kf, vf = bsm.gather_fetched(plan, r, k_all, v_all)
 
     def forward(events=None):
+        if args.fetch:
+            if events is not None:
+                events.append(torch.cuda.Event(enable_timing=True))
+                events[-1].record()
+            bsm.fwd_fetched(dp, hd, q, kf, vf, out=(o, lse))
+            if events is not None:
+                events.append(torch.cuda.Event(enable_timing=True))
+                events[-1].record()
+            return
         if args.merge != "carry":
             if events is not None:
                 events.append(torch.cuda.Event(enable_timing=True))
@@ -272,9 +307,10 @@ def main():
     fwd_flops = 4 * d * lay.hq * total_pairs
     bwd_flops = 10 * d * lay.hq * total_pairs
     fwd_tflops = fwd_flops / (fwd_ms * 1e-3) / 1e12
-    nlaunch = 1 if args.single or args.merge != "carry" else len(fwd_steps)
+    nlaunch = 1 if args.single or args.fetch or args.merge != "carry" else len(fwd_steps)
     per_launch_flops = fwd_flops / nlaunch
-    per_launch_bytes = sum(fwd_algorithmic_bytes(plan, r, R, S, lay.hq, lay.hkv, d, args.single)) / nlaunch
+    per_launch_bytes = sum(fwd_algorithmic_bytes(plan, r, R, S, lay.hq, lay.hkv, d,
+                                                 args.single or args.fetch)) / nlaunch
     # roofline of the forward kernel: whichever of the MFMA and HBM times of its
     # algorithmic work is longer bounds it
     t_mfma = per_launch_flops / (PEAK_BF16_TFLOPS * 1e12)
@@ -333,7 +369,9 @@ def main():
                      "avg_launch_us": round(avg_launch_ms * 1e3, 2),
                      "launches_per_step": nlaunch},
         "mode": ("single-pass diagnostic" if args.single else
+                 "sparse fetch: one pass over the shard and fetched tiles (contiguous chunks)" if args.fetch else
                  "ring" if args.merge == "carry" else f"ring, per-step {args.merge} merge (accuracy control)"),
+        "sparse_fetch": sparse_fetch_summary(lay, plan, r),
         "planner_s": round(plan_s, 4),
         "wall_s": round(wall, 3),
     }

@@ -41,7 +41,7 @@ ORDERS = {"contiguous": BSM_ORDER_CONTIGUOUS, "ptrr": BSM_ORDER_PTRR,
 EXPORTS = [
     "bsm_last_error", "bsm_version", "bsm_plan_build", "bsm_plan_free", "bsm_plan_get_info",
     "bsm_plan_permutation", "bsm_plan_block_cost", "bsm_plan_step_map", "bsm_plan_pairs",
-    "bsm_plan_key_intervals",
+    "bsm_plan_key_intervals", "bsm_plan_fetch_set", "bsm_fwd_fetched",
     "bsm_dplan_bytes", "bsm_dplan_upload", "bsm_dplan_free", "bsm_dplan_get_info",
     "bsm_fwd_step", "bsm_fwd_single", "bsm_fwd_merge_bf16", "bsm_fwd_merge_fp32",
     "bsm_bwd_prep", "bsm_bwd_step",
@@ -75,7 +75,8 @@ class bsm_dplan_info(C.Structure):
     _fields_ = [("rank", C.c_int32), ("ranks", C.c_int32), ("shard_tokens", C.c_int64),
                 ("tiles_per_shard", C.c_int32), ("window", C.c_int32),
                 ("fwd_items", C.c_int64 * 64), ("bwd_items", C.c_int64 * 64),
-                ("step_pairs", C.c_int64 * 64), ("single_items", C.c_int64)]
+                ("step_pairs", C.c_int64 * 64), ("single_items", C.c_int64),
+                ("fetch_tiles", C.c_int64), ("fetch_rows", C.c_int64)]
 
 
 class bsm_heads(C.Structure):
@@ -94,6 +95,9 @@ _sig = {
     "bsm_plan_step_map": (C.c_int, [_P, C.c_int32, C.c_int32, _P, C.POINTER(C.c_int64)]),
     "bsm_plan_pairs": (C.c_int, [_P, _P]),
     "bsm_plan_key_intervals": (C.c_int, [_P, _P, _P]),
+    "bsm_plan_fetch_set": (C.c_int, [_P, C.c_int32, _P, C.POINTER(C.c_int64)]),
+    "bsm_fwd_fetched": (C.c_int, [_P, C.POINTER(bsm_heads), _P, _P, _P, _P, _P, _P, _P, _P,
+                                  C.c_int32, _P]),
     "bsm_dplan_bytes": (C.c_int, [_P, C.c_int32, C.POINTER(C.c_int64)]),
     "bsm_dplan_upload": (C.c_int, [_P, C.c_int32, _P, C.c_int64, _P, C.POINTER(_P)]),
     "bsm_dplan_free": (None, [_P]),
@@ -195,6 +199,19 @@ def bsm_plan_key_intervals(plan):
     return lo, hi
 
 
+def bsm_plan_fetch_set(plan, r):
+    info = bsm_plan_get_info(plan)
+    need = np.empty(info["ranks"] * info["tiles_per_shard"], np.uint8)
+    tiles = C.c_int64()
+    _check(_lib.bsm_plan_fetch_set(plan, int(r), need.ctypes.data, C.byref(tiles)))
+    return need.reshape(info["ranks"], info["tiles_per_shard"]), tiles.value
+
+
+def bsm_fwd_fetched(dplan, heads, q, k_fetch, v_fetch, o_acc, m, l, o, lse, flags, stream):
+    _check(_lib.bsm_fwd_fetched(dplan, C.byref(heads), q, k_fetch, v_fetch, o_acc, m, l, o, lse,
+                                int(flags), stream))
+
+
 def bsm_dplan_bytes(plan, r) -> int:
     b = C.c_int64()
     _check(_lib.bsm_dplan_bytes(plan, int(r), C.byref(b)))
@@ -218,7 +235,8 @@ def bsm_dplan_get_info(dplan) -> dict:
     return {"rank": info.rank, "ranks": rk, "shard_tokens": info.shard_tokens,
             "tiles_per_shard": info.tiles_per_shard, "window": info.window,
             "fwd_items": list(info.fwd_items[:rk]), "bwd_items": list(info.bwd_items[:rk]),
-            "step_pairs": list(info.step_pairs[:rk]), "single_items": info.single_items}
+            "step_pairs": list(info.step_pairs[:rk]), "single_items": info.single_items,
+            "fetch_tiles": info.fetch_tiles, "fetch_rows": info.fetch_rows}
 
 
 def _heads(hq, hkv, d, scale):

@@ -52,11 +52,15 @@ struct Packed {
   std::vector<StepLists> steps;
   std::vector<int4> sitems;
   std::vector<int2> kint;  // key intervals (lo, hi) in plan order
+  // sparse fetch: one pass over [local shard | needed remote tiles]
+  std::vector<int4> xitems, xtracks;
+  std::vector<int2> xkint;
+  int64_t fetch_tiles = 0, fetch_rows = 0;
   std::vector<int2> entries;
   // byte offsets in the device buffer
   int64_t off_tracks = 0, off_kint = 0, off_items = 0, off_entries = 0, bytes = 0;
   std::vector<int64_t> off_f, off_b, off_ff;  // off_ff: first list entry of each forward item
-  int64_t off_s = 0, off_sf = 0;
+  int64_t off_s = 0, off_sf = 0, off_x = 0, off_xf = 0, off_xtracks = 0, off_xkint = 0;
 };
 
 static void pack(const Plan& p, int32_t r, Packed& pk) {
@@ -151,6 +155,53 @@ static void pack(const Plan& p, int32_t r, Packed& pk) {
   }
   std::stable_sort(pk.sitems.begin(), pk.sitems.end(), by_len);
 
+  // sparse fetch: the local shard, then the needed remote key tiles in ring
+  // step order (s = 1 .. R-1), ascending tile; each remote tile takes 128 rows
+  {
+    std::vector<uint8_t> need((size_t)R * T);
+    pk.fetch_tiles = fetch_set(p, r, need.data());
+    std::vector<int64_t> slot((size_t)R * T, -1);
+    for (int32_t b = 0; b < T; ++b) slot[(size_t)r * T + b] = (int64_t)b * kTile;
+    int64_t next = S;
+    for (int32_t s = 1; s < R; ++s) {
+      const int32_t j = ((r - s) % R + R) % R;
+      for (int32_t b = 0; b < T; ++b)
+        if (need[(size_t)j * T + b]) {
+          slot[(size_t)j * T + b] = next;
+          next += kTile;
+        }
+    }
+    pk.fetch_rows = next;
+    pk.xtracks.assign(next, make_int4(-1, -1, -1, 0));
+    pk.xkint.assign(next, make_int2(0, -1));
+    for (int32_t j = 0; j < R; ++j)
+      for (int32_t b = 0; b < T; ++b) {
+        const int64_t base = slot[(size_t)j * T + b];
+        if (base < 0) continue;
+        for (int32_t i = 0; i < tlen(b); ++i) {
+          pk.xtracks[base + i] = pk.tracks[(int64_t)j * S + (int64_t)b * kTile + i];
+          pk.xkint[base + i] = pk.kint[(int64_t)j * S + (int64_t)b * kTile + i];
+        }
+      }
+    pk.xitems.clear();
+    for (int32_t a = 0; a < T; ++a) {
+      const int32_t beg = (int32_t)pk.entries.size();
+      for (int32_t s = 0; s < R; ++s) {
+        const int32_t j = ((r - s) % R + R) % R;
+        for (auto& bc : rows[s][a]) {
+          const int32_t kl = tlen(bc.first);
+          const bool part = bc.second == BSM_TILE_PARTIAL || kl < kTile;
+          const bool kin = part && kint_tile(j, bc.first);
+          pk.entries.push_back(make_int2((int32_t)slot[(size_t)j * T + bc.first],
+                                         kl | (part ? kPartialBit : 0) | (kin ? kIntervalBit : 0)));
+        }
+      }
+      const int32_t cnt = (int32_t)pk.entries.size() - beg;
+      if (cnt) pk.xitems.push_back(make_int4(a, kFirst | kLast, beg, cnt));
+    }
+    std::stable_sort(pk.xitems.begin(), pk.xitems.end(), by_len);
+  }
+
   // byte layout
   int64_t off = 0;
   pk.off_tracks = off;
@@ -173,6 +224,14 @@ static void pack(const Plan& p, int32_t r, Packed& pk) {
   off = align256(off + (int64_t)pk.sitems.size() * sizeof(int4));
   pk.off_sf = off;
   off = align256(off + (int64_t)pk.sitems.size() * sizeof(int2));
+  pk.off_x = off;
+  off = align256(off + (int64_t)pk.xitems.size() * sizeof(int4));
+  pk.off_xf = off;
+  off = align256(off + (int64_t)pk.xitems.size() * sizeof(int2));
+  pk.off_xtracks = off;
+  off = align256(off + pk.fetch_rows * (int64_t)sizeof(int4));
+  pk.off_xkint = off;
+  off = align256(off + pk.fetch_rows * (int64_t)sizeof(int2));
   pk.off_entries = off;
   off = align256(off + (int64_t)pk.entries.size() * sizeof(int2));
   pk.bytes = std::max<int64_t>(off, 256);
@@ -193,6 +252,11 @@ struct bsm_dplan {
   const int4* sitems = nullptr;
   const int2* sfirst = nullptr;
   int64_t ns = 0;
+  const int4* xitems = nullptr;
+  const int2* xfirst = nullptr;
+  const int4* xtracks = nullptr;
+  const int2* xkint = nullptr;
+  int64_t nx = 0, fetch_tiles = 0, fetch_rows = 0;
 };
 
 using namespace bsm;
@@ -356,6 +420,11 @@ int bsm_dplan_upload(const bsm_plan* plan, int32_t r, void* dev, int64_t bytes, 
     std::memcpy(img.data() + pk.off_s, pk.sitems.data(), pk.sitems.size() * sizeof(int4));
     int2* sf = (int2*)(img.data() + pk.off_sf);
     for (size_t i = 0; i < pk.sitems.size(); ++i) sf[i] = pk.entries[pk.sitems[i].z];
+    std::memcpy(img.data() + pk.off_x, pk.xitems.data(), pk.xitems.size() * sizeof(int4));
+    int2* xf = (int2*)(img.data() + pk.off_xf);
+    for (size_t i = 0; i < pk.xitems.size(); ++i) xf[i] = pk.entries[pk.xitems[i].z];
+    std::memcpy(img.data() + pk.off_xtracks, pk.xtracks.data(), pk.xtracks.size() * sizeof(int4));
+    std::memcpy(img.data() + pk.off_xkint, pk.xkint.data(), pk.xkint.size() * sizeof(int2));
     std::memcpy(img.data() + pk.off_entries, pk.entries.data(), pk.entries.size() * sizeof(int2));
     hipStream_t st = (hipStream_t)stream;
     int rc = hip_status(hipMemcpyAsync(dev, img.data(), pk.bytes, hipMemcpyHostToDevice, st),
@@ -385,6 +454,13 @@ int bsm_dplan_upload(const bsm_plan* plan, int32_t r, void* dev, int64_t bytes, 
     d->sitems = (const int4*)(base + pk.off_s);
     d->sfirst = (const int2*)(base + pk.off_sf);
     d->ns = (int64_t)pk.sitems.size();
+    d->xitems = (const int4*)(base + pk.off_x);
+    d->xfirst = (const int2*)(base + pk.off_xf);
+    d->xtracks = (const int4*)(base + pk.off_xtracks);
+    d->xkint = (const int2*)(base + pk.off_xkint);
+    d->nx = (int64_t)pk.xitems.size();
+    d->fetch_tiles = pk.fetch_tiles;
+    d->fetch_rows = pk.fetch_rows;
     *out = d;
   } catch (const std::bad_alloc&) {
     set_error("out of host memory");
@@ -409,6 +485,8 @@ int bsm_dplan_get_info(const bsm_dplan* d, bsm_dplan_info* out) {
     out->step_pairs[s] = d->pairs[s];
   }
   out->single_items = d->ns;
+  out->fetch_tiles = d->fetch_tiles;
+  out->fetch_rows = d->fetch_rows;
   return BSM_OK;
 }
 
@@ -455,9 +533,12 @@ int bsm_fwd_step(const bsm_dplan* d, int32_t s, const bsm_heads* heads, const vo
   return hip_status(launch_fwd(a, st), "forward step launch", st);
 }
 
-int bsm_fwd_single(const bsm_dplan* d, const bsm_heads* heads, const void* q, const void* k_all,
-                   const void* v_all, float* o_acc, float* m, float* l, void* o, float* lse,
-                   int32_t flags, void* stream) {
+namespace {
+// One pass over merged lists (`fetched`: the sparse-fetch lists over the
+// compact buffer; otherwise the single-pass lists over all shards).
+int fwd_pass(const bsm_dplan* d, bool fetched, const bsm_heads* heads, const void* q, const void* k_all,
+             const void* v_all, float* o_acc, float* m, float* l, void* o, float* lse, int32_t flags,
+             void* stream) {
   if (!d) { set_error("null device plan"); return BSM_E_INVALID; }
   int rc = check_heads(heads);
   if (rc) return rc;
@@ -466,14 +547,16 @@ int bsm_fwd_single(const bsm_dplan* d, const bsm_heads* heads, const void* q, co
     set_error("null tensor pointer");
     return BSM_E_INVALID;
   }
-  if ((rc = check_rows(d->S, heads->hq, "q")) || (rc = check_rows((int64_t)d->S * d->R, heads->hkv, "k_all/v_all")))
+  const int64_t krows = fetched ? d->fetch_rows : (int64_t)d->S * d->R;
+  if ((rc = check_rows(d->S, heads->hq, "q")) || (rc = check_rows(krows, heads->hkv, "keys/values")))
     return rc;
-  if (d->ns == 0) return BSM_OK;
+  const int64_t nitems = fetched ? d->nx : d->ns;
+  if (nitems == 0) return BSM_OK;
   FwdArgs a{};
-  a.items = d->sitems;
-  a.first = d->sfirst;
+  a.items = fetched ? d->xitems : d->sitems;
+  a.first = fetched ? d->xfirst : d->sfirst;
   a.entries = d->entries;
-  a.nitems = (int32_t)d->ns;
+  a.nitems = (int32_t)nitems;
   a.hq = heads->hq;
   a.hkv = heads->hkv;
   a.heads_per_xcd = heads_per_xcd(heads->hq);
@@ -481,8 +564,8 @@ int bsm_fwd_single(const bsm_dplan* d, const bsm_heads* heads, const void* q, co
   a.k = bf(k_all);
   a.v = bf(v_all);
   a.qtracks = d->tracks + (int64_t)d->r * d->S;
-  a.ktracks = d->tracks;
-  a.kint = d->kint;
+  a.ktracks = fetched ? d->xtracks : d->tracks;
+  a.kint = fetched ? d->xkint : d->kint;
   a.rows = d->S;
   a.oacc = o_acc;
   a.m = m;
@@ -494,7 +577,28 @@ int bsm_fwd_single(const bsm_dplan* d, const bsm_heads* heads, const void* q, co
   a.keep_state = keep ? 1 : 0;
   a.step_only = (flags & BSM_FWD_STEP_ONLY) != 0 ? 1 : 0;
   hipStream_t st = (hipStream_t)stream;
-  return hip_status(launch_fwd(a, st), "forward single launch", st);
+  return hip_status(launch_fwd(a, st), fetched ? "forward fetched launch" : "forward single launch", st);
+}
+}  // namespace
+
+int bsm_fwd_single(const bsm_dplan* d, const bsm_heads* heads, const void* q, const void* k_all,
+                   const void* v_all, float* o_acc, float* m, float* l, void* o, float* lse,
+                   int32_t flags, void* stream) {
+  return fwd_pass(d, false, heads, q, k_all, v_all, o_acc, m, l, o, lse, flags, stream);
+}
+
+int bsm_fwd_fetched(const bsm_dplan* d, const bsm_heads* heads, const void* q, const void* k_fetch,
+                    const void* v_fetch, float* o_acc, float* m, float* l, void* o, float* lse,
+                    int32_t flags, void* stream) {
+  return fwd_pass(d, true, heads, q, k_fetch, v_fetch, o_acc, m, l, o, lse, flags, stream);
+}
+
+int bsm_plan_fetch_set(const bsm_plan* plan, int32_t r, uint8_t* needed, int64_t* tiles) {
+  if (!plan || !needed) { set_error("null argument"); return BSM_E_INVALID; }
+  if (r < 0 || r >= plan->p.ranks) { set_error("rank out of range"); return BSM_E_INVALID; }
+  const int64_t c = fetch_set(plan->p, r, needed);
+  if (tiles) *tiles = c;
+  return BSM_OK;
 }
 
 int bsm_fwd_merge_bf16(const bsm_heads* heads, int64_t rows, void* o_run, float* lse_run, const void* o_s,

@@ -412,4 +412,21 @@ int64_t step_map(const Plan& p, int32_t r, int32_t s, uint8_t* map) {
   return total;
 }
 
+int64_t fetch_set(const Plan& p, int32_t r, uint8_t* needed) {
+  std::fill(needed, needed + (int64_t)p.ranks * p.tps, (uint8_t)0);
+  int64_t count = 0;
+  for (int32_t a = 0; a < p.tps; ++a) {
+    const int32_t tq = p.tiles_new[r * p.tps + a];
+    for (int64_t e = p.pptr[tq]; e < p.pptr[tq + 1]; ++e) {
+      const int32_t tk = p.pkey[e];
+      const int32_t j = p.owner[tk];
+      if (j == r) continue;
+      uint8_t& x = needed[(int64_t)j * p.tps + p.local[tk]];
+      count += x == 0;
+      x = 1;
+    }
+  }
+  return count;
+}
+
 }  // namespace bsm

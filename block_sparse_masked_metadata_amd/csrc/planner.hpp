@@ -50,6 +50,11 @@ int build_plan(const bsm_plan_desc& desc, Plan& out);
 // Legal pairs of rank r at step s and optional tile map.
 int64_t step_map(const Plan& p, int32_t r, int32_t s, uint8_t* map);
 
+// Sparse fetch: needed[j * tps + b] = 1 when some query tile of rank r has a
+// non-empty pair with key tile b of shard j != r; returns the number of such
+// remote tiles.
+int64_t fetch_set(const Plan& p, int32_t r, uint8_t* needed);
+
 }  // namespace bsm
 
 struct bsm_plan {

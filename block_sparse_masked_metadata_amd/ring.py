@@ -54,6 +54,10 @@ class Plan:
     def block_cost(self):
         return C.bsm_plan_block_cost(self.handle)
 
+    def fetch_set(self, r):
+        """(needed [R, tiles_per_shard] uint8, count): remote key tiles rank r needs."""
+        return C.bsm_plan_fetch_set(self.handle, r)
+
     def key_intervals(self):
         """(lo, hi) per key in the original order; hi < lo: no single range."""
         return C.bsm_plan_key_intervals(self.handle)
@@ -172,6 +176,49 @@ def fwd_ring_merged(dp: DevicePlan, hd, q, k_shards, v_shards, mode="bf16", step
         C.bsm_fwd_merge_fp32(hd, rows, _ptr(o_run), _ptr(lse_run), _ptr(acc), _ptr(m), _ptr(l),
                              _ptr(o) if i == len(todo) - 1 else None, _stream())
     return o, lse_run
+
+
+def fetch_rows(plan: Plan, r: int):
+    """Source row (into the shards concatenated in plan order) of every row of
+    rank r's compact sparse-fetch buffer: its own shard, then each needed
+    remote tile (128 rows, ring step order, ascending tile); -1 pads a ragged
+    tile."""
+    need, _ = plan.fetch_set(r)
+    R, T = need.shape
+    S = plan.info["shard_tokens"]
+    out = [np.arange(r * S, (r + 1) * S, dtype=np.int64)]
+    for s in range(1, R):
+        j = (r - s) % R
+        for b in np.flatnonzero(need[j]):
+            src = np.arange(j * S + b * 128, j * S + b * 128 + 128, dtype=np.int64)
+            src[src >= (j + 1) * S] = -1
+            out.append(src)
+    return np.concatenate(out)
+
+
+def gather_fetched(plan: Plan, r: int, k_all, v_all):
+    """The compact key/value buffers of rank r from all shards (what one
+    variable-sized all-to-all would deliver); pad rows copy row 0."""
+    import torch
+    src = torch.from_numpy(np.maximum(fetch_rows(plan, r), 0)).to(k_all.device)
+    return k_all.index_select(0, src), v_all.index_select(0, src)
+
+
+def fwd_fetched(dp: DevicePlan, hd, q, k_fetch, v_fetch, out=None):
+    """One pass over the rank's shard and its fetched remote tiles."""
+    import torch
+    rows = dp.rows
+    _need(q, torch.bfloat16, (rows, hd.hq, hd.d), "q")
+    fr = dp.info["fetch_rows"]
+    _need(k_fetch, torch.bfloat16, (fr, hd.hkv, hd.d), "k_fetch")
+    _need(v_fetch, torch.bfloat16, (fr, hd.hkv, hd.d), "v_fetch")
+    if out is None:
+        out = (torch.empty(rows, hd.hq, hd.d, dtype=torch.bfloat16, device=q.device),
+               torch.empty(hd.hq, rows, dtype=torch.float32, device=q.device))
+    o, lse = out
+    C.bsm_fwd_fetched(dp.handle, hd, _ptr(q), _ptr(k_fetch), _ptr(v_fetch), None, None, None, _ptr(o),
+                      _ptr(lse), 0, _stream())
+    return o, lse
 
 
 def fwd_single(dp: DevicePlan, hd, q, k_all, v_all, keep_state=False, out=None):

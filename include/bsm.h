@@ -170,6 +170,17 @@ int bsm_plan_step_map(const bsm_plan* plan, int32_t r, int32_t s, uint8_t* map,
 int bsm_plan_pairs(const bsm_plan* plan, int64_t* pairs);
 
 /*
+ * Sparse fetch (MARBLE section 04, "Sparse all-to-all and strategy selection":
+ * instead of the ring, each rank pulls only the remote 128-token key/value
+ * blocks its queries can see, then runs one pass over its local and fetched
+ * keys): needed[j * tps + b] = 1
+ * when some query tile of rank r has a legal pair with key tile b of shard
+ * j != r (host uint8[ranks * tiles_per_shard]); *tiles (may be NULL) = their
+ * count.  The bytes a rank avoids are the remote tiles with needed = 0.
+ */
+int bsm_plan_fetch_set(const bsm_plan* plan, int32_t r, uint8_t* needed, int64_t* tiles);
+
+/*
  * Key intervals (MARBLE section 03, "Block classification": a partial tile can
  * test one range per key in a chosen coordinate).  For every key k in the
  * ORIGINAL order, when the queries k is legal for are exactly those with
@@ -212,6 +223,8 @@ typedef struct {
   int64_t bwd_items[64];     /* key tiles with work at step s                 */
   int64_t step_pairs[64];    /* legal pairs at step s                         */
   int64_t single_items;      /* query tiles with work in the merged list      */
+  int64_t fetch_tiles;       /* remote key tiles the rank needs (sparse fetch) */
+  int64_t fetch_rows;        /* rows of the compact key/value buffer          */
 } bsm_dplan_info;
 
 int bsm_dplan_get_info(const bsm_dplan* dplan, bsm_dplan_info* out);
@@ -271,6 +284,20 @@ int bsm_fwd_single(const bsm_dplan* dplan, const bsm_heads* heads,
                    const void* q, const void* k_all, const void* v_all,
                    float* o_acc, float* m, float* l, void* o, float* lse,
                    int32_t flags, void* stream);
+
+/*
+ * One pass over the rank's local shard and the fetched remote tiles (sparse
+ * fetch).  k_fetch, v_fetch bf16 [fetch_rows, Hkv, d] hold the compact
+ * buffer: rows [0, S) = the rank's own shard j = r in plan order, then every
+ * needed remote tile (bsm_plan_fetch_set) at 128 rows each, in ring step
+ * order s = 1..R-1 (shard j = (r - s) mod R), ascending tile b; rows of a
+ * ragged tile past its valid rows are never read.  Tiles are visited in the
+ * single pass's order, so the result is bitwise that of bsm_fwd_single.
+ * Other arguments and flags as for bsm_fwd_single.
+ */
+int bsm_fwd_fetched(const bsm_dplan* dplan, const bsm_heads* heads, const void* q,
+                    const void* k_fetch, const void* v_fetch, float* o_acc, float* m, float* l,
+                    void* o, float* lse, int32_t flags, void* stream);
 
 /*
  * Accuracy controls (MARBLE section 03, "Exact ring attention accumulation":

@@ -50,6 +50,15 @@ def parse():
     ap.add_argument("--fetch", action="store_true",
                     help="sparse fetch: contiguous chunks, one pass over the rank's shard and its "
                          "fetched remote tiles (forward only; the fetch itself is not timed)")
+    ap.add_argument("--order", choices=["ptrr", "contiguous"], default=None,
+                    help="token order of the ring layout (default: the workload's own)")
+    ap.add_argument("--chunks", type=int, default=0,
+                    help="chunked ring layout: search 1..K contiguous chunks per rank")
+    ap.add_argument("--tau", type=float, default=0.0,
+                    help="chunk search: cost of one extra key range per rank and step, in pairs")
+    ap.add_argument("--ring-estimate", action="store_true",
+                    help="also time every rank's forward steps and report the ring's critical "
+                         "path (sum over steps of the slowest rank), untimed by the headline")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
     return ap.parse_args()
@@ -172,6 +181,44 @@ def cpu_baseline(lay, plan_pairs_fn, rows_all, q, k, v, target_s):
                       f"host {platform.processor() or platform.machine()}"}
 
 
+def ring_estimate(bsm, torch, plan, hd, full, perm, k_all, v_all, lay, d, passes):
+    """Every rank's forward steps on this one GPU, each launch timed with
+    events: the ring's forward critical path is the sum over steps of the
+    slowest rank's launch (communication and overlap not included)."""
+    R, S = lay.ranks, plan.info["shard_tokens"]
+    ks = [k_all[j * S:(j + 1) * S] for j in range(R)]
+    vs = [v_all[j * S:(j + 1) * S] for j in range(R)]
+    t = np.zeros((R, R))
+    for rr in range(R):
+        dpr = bsm.DevicePlan(plan, rr)
+        q = full[0][torch.from_numpy(perm[rr * S:(rr + 1) * S]).cuda()].contiguous()
+        state = bsm.new_state(S, lay.hq, d)
+        o = torch.empty(S, lay.hq, d, dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty(lay.hq, S, dtype=torch.float32, device="cuda")
+        steps = [s for s in range(R) if dpr.info["fwd_items"][s] > 0]
+        for it in range(passes + 1):
+            ev = []
+            for s in steps:
+                j = (rr - s) % R
+                ev.append(torch.cuda.Event(enable_timing=True))
+                ev[-1].record()
+                bsm.fwd_step(dpr, s, hd, q, ks[j], vs[j], state, o, lse)
+                ev.append(torch.cuda.Event(enable_timing=True))
+                ev[-1].record()
+            torch.cuda.synchronize()
+            if it:  # the first pass warms up
+                for i, s in enumerate(steps):
+                    t[rr, s] += ev[2 * i].elapsed_time(ev[2 * i + 1]) / passes
+        del dpr, q, state, o, lse
+    pairs = plan.pairs()
+    return {"critical_path_ms": round(float(t.max(axis=0).sum()), 4),
+            "busiest_rank_ms": round(float(t.sum(axis=1).max()), 4),
+            "mean_rank_ms": round(float(t.sum(axis=1).mean()), 4),
+            "step_max_pairs_sum": int(pairs.max(axis=0).sum()),
+            "busiest_rank_pairs": int(pairs.sum(axis=1).max()),
+            "passes": passes}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -182,11 +229,18 @@ def main():
     import block_sparse_masked_metadata_amd as bsm
     from workloads import config, qkv
 
+    import dataclasses
     lay = config(args.config)
+    if args.order:
+        lay = dataclasses.replace(lay, order=args.order)
     if args.fetch:
-        import dataclasses
         lay = dataclasses.replace(lay, order="contiguous")
+    chunk_info = None
     t0 = time.perf_counter()
+    if args.chunks:
+        base = bsm.Plan.from_layout(dataclasses.replace(lay, order="contiguous"))
+        bperm, chunk_info = base.chunk_order(1, args.chunks, args.tau, 4)
+        lay = dataclasses.replace(lay, order="explicit", block_perm=bperm)
     plan = bsm.Plan.from_layout(lay)
     plan_s = time.perf_counter() - t0
     r = plan.info["busiest_rank"]
@@ -377,6 +431,11 @@ def main():
     }
     if args.merge != "carry":
         out["roofline"] = None  # the timed forward includes fills and merge kernels
+    if chunk_info is not None:
+        out["chunking"] = chunk_info
+    if args.ring_estimate:
+        out["ring_estimate"] = ring_estimate(bsm, torch, plan, hd, full, perm, k_all, v_all,
+                                             lay, d, max(1, args.steps // 4))
     if not args.no_cpu_baseline:
         qc, kc, vc = (t.cpu() for t in full[:3])
         out["cpu_baseline"] = cpu_baseline(lay, None, rows, qc, kc, vc, args.cpu_seconds)

@@ -41,7 +41,7 @@ ORDERS = {"contiguous": BSM_ORDER_CONTIGUOUS, "ptrr": BSM_ORDER_PTRR,
 EXPORTS = [
     "bsm_last_error", "bsm_version", "bsm_plan_build", "bsm_plan_free", "bsm_plan_get_info",
     "bsm_plan_permutation", "bsm_plan_block_cost", "bsm_plan_step_map", "bsm_plan_pairs",
-    "bsm_plan_key_intervals", "bsm_plan_fetch_set", "bsm_fwd_fetched",
+    "bsm_plan_key_intervals", "bsm_plan_fetch_set", "bsm_plan_chunk_order", "bsm_fwd_fetched",
     "bsm_dplan_bytes", "bsm_dplan_upload", "bsm_dplan_free", "bsm_dplan_get_info",
     "bsm_fwd_step", "bsm_fwd_single", "bsm_fwd_merge_bf16", "bsm_fwd_merge_fp32",
     "bsm_bwd_prep", "bsm_bwd_step",
@@ -79,6 +79,11 @@ class bsm_dplan_info(C.Structure):
                 ("fetch_tiles", C.c_int64), ("fetch_rows", C.c_int64)]
 
 
+class bsm_chunk_info(C.Structure):
+    _fields_ = [("chunks_per_rank", C.c_int32), ("strategy", C.c_int32), ("cost", C.c_double),
+                ("step_max_sum", C.c_double), ("range_term", C.c_double)]
+
+
 class bsm_heads(C.Structure):
     _fields_ = [("hq", C.c_int32), ("hkv", C.c_int32), ("d", C.c_int32), ("scale", C.c_float)]
 
@@ -96,6 +101,8 @@ _sig = {
     "bsm_plan_pairs": (C.c_int, [_P, _P]),
     "bsm_plan_key_intervals": (C.c_int, [_P, _P, _P]),
     "bsm_plan_fetch_set": (C.c_int, [_P, C.c_int32, _P, C.POINTER(C.c_int64)]),
+    "bsm_plan_chunk_order": (C.c_int, [_P, C.c_int32, C.c_int32, C.c_double, C.c_int32, _P,
+                                       C.POINTER(bsm_chunk_info)]),
     "bsm_fwd_fetched": (C.c_int, [_P, C.POINTER(bsm_heads), _P, _P, _P, _P, _P, _P, _P, _P,
                                   C.c_int32, _P]),
     "bsm_dplan_bytes": (C.c_int, [_P, C.c_int32, C.POINTER(C.c_int64)]),
@@ -205,6 +212,16 @@ def bsm_plan_fetch_set(plan, r):
     tiles = C.c_int64()
     _check(_lib.bsm_plan_fetch_set(plan, int(r), need.ctypes.data, C.byref(tiles)))
     return need.reshape(info["ranks"], info["tiles_per_shard"]), tiles.value
+
+
+def bsm_plan_chunk_order(plan, min_chunks=1, max_chunks=64, tau=0.0, swaps=4):
+    nt = bsm_plan_get_info(plan)["tiles_total"]
+    perm = np.empty(nt, np.int32)
+    info = bsm_chunk_info()
+    _check(_lib.bsm_plan_chunk_order(plan, int(min_chunks), int(max_chunks), float(tau), int(swaps),
+                                     perm.ctypes.data, C.byref(info)))
+    return perm, {"chunks_per_rank": info.chunks_per_rank, "strategy": info.strategy,
+                  "cost": info.cost, "step_max_sum": info.step_max_sum, "range_term": info.range_term}
 
 
 def bsm_fwd_fetched(dplan, heads, q, k_fetch, v_fetch, o_acc, m, l, o, lse, flags, stream):

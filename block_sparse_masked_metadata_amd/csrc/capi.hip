@@ -593,6 +593,20 @@ int bsm_fwd_fetched(const bsm_dplan* d, const bsm_heads* heads, const void* q, c
   return fwd_pass(d, true, heads, q, k_fetch, v_fetch, o_acc, m, l, o, lse, flags, stream);
 }
 
+int bsm_plan_chunk_order(const bsm_plan* plan, int32_t min_chunks, int32_t max_chunks, double tau,
+                         int32_t swaps, int32_t* block_perm, bsm_chunk_info* out) {
+  if (!plan || !block_perm || !out) { set_error("null argument"); return BSM_E_INVALID; }
+  ChunkResult res;
+  const int rc = chunk_order(plan->p, min_chunks, max_chunks, tau, swaps, block_perm, res);
+  if (rc) return rc;
+  out->chunks_per_rank = res.chunks_per_rank;
+  out->strategy = res.strategy;
+  out->cost = res.cost;
+  out->step_max_sum = res.step_max_sum;
+  out->range_term = res.range_term;
+  return BSM_OK;
+}
+
 int bsm_plan_fetch_set(const bsm_plan* plan, int32_t r, uint8_t* needed, int64_t* tiles) {
   if (!plan || !needed) { set_error("null argument"); return BSM_E_INVALID; }
   if (r < 0 || r >= plan->p.ranks) { set_error("rank out of range"); return BSM_E_INVALID; }

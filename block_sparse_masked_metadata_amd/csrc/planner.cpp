@@ -429,4 +429,134 @@ int64_t fetch_set(const Plan& p, int32_t r, uint8_t* needed) {
   return count;
 }
 
+// Chunked ring attention (MARBLE section 03, "Chunked ring attention"): the
+// sequence is cut into R*k contiguous chunks of whole tiles, k a power of two
+// in [min_chunks, max_chunks] dividing the tiles per shard; chunks
+// are dealt to ranks by the PTRR rule (sort, rounds of R, every other round
+// reversed) once in the order of work and once in sequence order, optionally
+// improved by greedy pairwise swaps of chunks between ranks; each rank keeps
+// its tiles in sequence order.  The cost of a layout is
+//   C = sum_s max_r W[r][(r - s) mod R] + tau * R * k,
+// with W[r][j] the legal pairs between rank r's queries and rank j's keys
+// (from the exact tile-pair counts) and tau the fixed cost of one range in one
+// step, in pairs.  The cheapest candidate wins (ties: fewer chunks, then work
+// order).
+namespace {
+
+struct ChunkEval {
+  const Plan& p;
+  int32_t R, k, nchunks, ctiles;
+  std::vector<int32_t> tile_chunk;  // original tile -> chunk
+  std::vector<int64_t> cpair;       // chunk x chunk legal pairs
+  ChunkEval(const Plan& p_, int32_t k_) : p(p_), R(p_.ranks), k(k_) {
+    nchunks = R * k;
+    ctiles = p.ntiles / nchunks;
+    tile_chunk.resize(p.ntiles);
+    for (int32_t t = 0; t < p.ntiles; ++t) tile_chunk[t] = t / ctiles;
+    cpair.assign((size_t)nchunks * nchunks, 0);
+    for (int32_t tq = 0; tq < p.ntiles; ++tq)
+      for (int64_t e = p.pptr[tq]; e < p.pptr[tq + 1]; ++e)
+        cpair[(size_t)tile_chunk[tq] * nchunks + tile_chunk[p.pkey[e]]] += p.pcount[e];
+  }
+  // sum over steps of the slowest rank, for chunk -> rank assignment `own`
+  double step_max_sum(const std::vector<int32_t>& own) const {
+    std::vector<int64_t> w((size_t)R * R, 0);
+    for (int32_t a = 0; a < nchunks; ++a)
+      for (int32_t b = 0; b < nchunks; ++b) w[(size_t)own[a] * R + own[b]] += cpair[(size_t)a * nchunks + b];
+    double tot = 0;
+    for (int32_t s = 0; s < R; ++s) {
+      int64_t mx = 0;
+      for (int32_t r = 0; r < R; ++r) mx = std::max(mx, w[(size_t)r * R + ((r - s) % R + R) % R]);
+      tot += (double)mx;
+    }
+    return tot;
+  }
+};
+
+// PTRR dealing of chunks given in `order` (rounds of R, odd rounds reversed).
+std::vector<int32_t> deal(const std::vector<int32_t>& order, int32_t R) {
+  std::vector<int32_t> own(order.size());
+  for (size_t i = 0; i < order.size(); ++i) {
+    const int32_t round = (int32_t)(i / R), slot = (int32_t)(i % R);
+    own[order[i]] = (round % 2 == 0) ? slot : R - 1 - slot;
+  }
+  return own;
+}
+
+}  // namespace
+
+int chunk_order(const Plan& p, int32_t min_chunks, int32_t max_chunks, double tau, int32_t swaps,
+                int32_t* block_perm, ChunkResult& out) {
+  const int32_t R = p.ranks;
+  if (p.n % ((int64_t)p.block * R)) {  // an explicit block order needs whole blocks per rank
+    set_error("chunked layouts need n % (block * ranks) == 0");
+    return BSM_E_INVALID;
+  }
+  if (min_chunks < 1 || max_chunks < min_chunks || swaps < 0 || !(tau >= 0)) {
+    set_error("need 1 <= min_chunks <= max_chunks, swaps >= 0, tau >= 0");
+    return BSM_E_INVALID;
+  }
+  const int32_t tps = p.ntiles / R;
+  bool found = false;
+  std::vector<int32_t> best_own;
+  int32_t best_k = 0;
+  for (int32_t k = 1; k <= max_chunks && k <= tps; k *= 2) {
+    if (k < min_chunks || tps % k) continue;
+    ChunkEval ev(p, k);
+    std::vector<int64_t> work(ev.nchunks, 0);
+    for (int32_t a = 0; a < ev.nchunks; ++a)
+      for (int32_t b = 0; b < ev.nchunks; ++b) work[a] += ev.cpair[(size_t)a * ev.nchunks + b];
+    for (int32_t strategy = 0; strategy < 2; ++strategy) {
+      std::vector<int32_t> order(ev.nchunks);
+      std::iota(order.begin(), order.end(), 0);
+      if (strategy == 0)
+        std::stable_sort(order.begin(), order.end(),
+                         [&](int32_t a, int32_t b) { return work[a] != work[b] ? work[a] > work[b] : a < b; });
+      std::vector<int32_t> own = deal(order, R);
+      double cur = ev.step_max_sum(own);
+      // greedy pairwise swaps of chunks on different ranks, first improvement
+      // (quartic in the chunk count: only for up to 64 chunks)
+      for (int32_t pass = 0; pass < (ev.nchunks <= 64 ? swaps : 0); ++pass) {
+        bool improved = false;
+        for (int32_t a = 0; a < ev.nchunks && !improved; ++a)
+          for (int32_t b = a + 1; b < ev.nchunks && !improved; ++b) {
+            if (own[a] == own[b]) continue;
+            std::swap(own[a], own[b]);
+            const double c = ev.step_max_sum(own);
+            if (c < cur) {
+              cur = c;
+              improved = true;
+            } else {
+              std::swap(own[a], own[b]);
+            }
+          }
+        if (!improved) break;
+      }
+      const double range_term = tau * R * k;
+      const double cost = cur + range_term;
+      if (!found || cost < out.cost) {
+        found = true;
+        out.cost = cost;
+        out.step_max_sum = cur;
+        out.range_term = range_term;
+        out.chunks_per_rank = k;
+        out.strategy = strategy;
+        best_own = own;
+        best_k = k;
+      }
+    }
+  }
+  if (!found) {
+    set_error("no chunk count divides the tiles per shard");
+    return BSM_E_INVALID;
+  }
+  // explicit block order: ranks in order, each rank's tiles ascending
+  const int32_t ctiles = p.ntiles / (R * best_k);
+  int32_t pos = 0;
+  for (int32_t r = 0; r < R; ++r)
+    for (int32_t t = 0; t < p.ntiles; ++t)
+      if (best_own[t / ctiles] == r) block_perm[pos++] = t;
+  return BSM_OK;
+}
+
 }  // namespace bsm

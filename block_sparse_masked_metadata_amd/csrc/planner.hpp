@@ -55,6 +55,15 @@ int64_t step_map(const Plan& p, int32_t r, int32_t s, uint8_t* map);
 // remote tiles.
 int64_t fetch_set(const Plan& p, int32_t r, uint8_t* needed);
 
+// Chunked ring layout (see planner.cpp): the explicit block order of the
+// cheapest candidate and its cost terms.
+struct ChunkResult {
+  int32_t chunks_per_rank = 0, strategy = 0;
+  double cost = 0, step_max_sum = 0, range_term = 0;
+};
+int chunk_order(const Plan& p, int32_t min_chunks, int32_t max_chunks, double tau, int32_t swaps,
+                int32_t* block_perm, ChunkResult& out);
+
 }  // namespace bsm
 
 struct bsm_plan {

@@ -40,7 +40,7 @@ class Plan:
     @classmethod
     def from_layout(cls, layout, threads=0):
         return cls(layout.tracks(), layout.window, layout.ranks, layout.block, layout.order,
-                   threads=threads)
+                   explicit_block_perm=getattr(layout, "block_perm", None), threads=threads)
 
     def permutation(self):
         return C.bsm_plan_permutation(self.handle)
@@ -53,6 +53,10 @@ class Plan:
 
     def block_cost(self):
         return C.bsm_plan_block_cost(self.handle)
+
+    def chunk_order(self, min_chunks=1, max_chunks=64, tau=0.0, swaps=4):
+        """Chunked ring layout: (explicit block order, cost terms)."""
+        return C.bsm_plan_chunk_order(self.handle, min_chunks, max_chunks, tau, swaps)
 
     def fetch_set(self, r):
         """(needed [R, tiles_per_shard] uint8, count): remote key tiles rank r needs."""

@@ -170,6 +170,32 @@ int bsm_plan_step_map(const bsm_plan* plan, int32_t r, int32_t s, uint8_t* map,
 int bsm_plan_pairs(const bsm_plan* plan, int64_t* pairs);
 
 /*
+ * Chunked ring layout (MARBLE section 03, "Chunked ring attention").  The
+ * sequence (the plan's tiles in the original order) is cut into R*k
+ * contiguous chunks, k a power of two in [min_chunks, max_chunks] dividing
+ * the tiles per shard.  Chunks are dealt to ranks by the PTRR rule once in the
+ * order of work (strategy 0) and once in sequence order (strategy 1), then
+ * improved by up to `swaps` rounds of greedy pairwise swaps (only when
+ * R*k <= 64).  The layout minimizing
+ *   C = sum_s max_r W[r][(r - s) mod R] + tau * R * k
+ * wins; W[r][j] is the legal pairs between rank r's queries and rank j's keys
+ * and tau the fixed cost of one range in one step, in pairs.  block_perm
+ * (host int32[tiles_total]) receives its explicit block order (new position ->
+ * original block; ranks in order, each rank's blocks ascending), to rebuild the
+ * plan with BSM_ORDER_EXPLICIT.  Needs n % (block * ranks) == 0.
+ */
+typedef struct {
+  int32_t chunks_per_rank;   /* k of the chosen layout                        */
+  int32_t strategy;          /* 0: dealt in order of work, 1: sequence order  */
+  double cost;               /* C                                             */
+  double step_max_sum;       /* sum over steps of the slowest rank's pairs    */
+  double range_term;         /* tau * R * k                                   */
+} bsm_chunk_info;
+
+int bsm_plan_chunk_order(const bsm_plan* plan, int32_t min_chunks, int32_t max_chunks, double tau,
+                         int32_t swaps, int32_t* block_perm, bsm_chunk_info* out);
+
+/*
  * Sparse fetch (MARBLE section 04, "Sparse all-to-all and strategy selection":
  * instead of the ring, each rank pulls only the remote 128-token key/value
  * blocks its queries can see, then runs one pass over its local and fetched

@@ -46,6 +46,8 @@ class Layout:
     backward: bool = False
     # human-readable span list: (start, end, mode, sample) for docs / tests
     spans: list = field(default_factory=list)
+    # order "explicit": new block position -> original block
+    block_perm: object = None
 
     @property
     def n(self) -> int:

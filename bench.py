@@ -56,9 +56,15 @@ def parse():
                     help="chunked ring layout: search 1..K contiguous chunks per rank")
     ap.add_argument("--tau", type=float, default=0.0,
                     help="chunk search: cost of one extra key range per rank and step, in pairs")
+    ap.add_argument("--dense", action="store_true",
+                    help="dense-call mode: every ring step as full / causal / reverse calls "
+                         "(forward only)")
     ap.add_argument("--ring-estimate", action="store_true",
                     help="also time every rank's forward steps and report the ring's critical "
                          "path (sum over steps of the slowest rank), untimed by the headline")
+    ap.add_argument("--fit-tau", action="store_true",
+                    help="fit the chunk cost's per-range term: time the ring critical path at "
+                         "1, 2, 4, ..., 64 chunks per rank and print one JSON line with the fit")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
     return ap.parse_args()
@@ -181,7 +187,7 @@ def cpu_baseline(lay, plan_pairs_fn, rows_all, q, k, v, target_s):
                       f"host {platform.processor() or platform.machine()}"}
 
 
-def ring_estimate(bsm, torch, plan, hd, full, perm, k_all, v_all, lay, d, passes):
+def ring_estimate(bsm, torch, plan, hd, full, perm, k_all, v_all, lay, d, passes, dense=False):
     """Every rank's forward steps on this one GPU, each launch timed with
     events: the ring's forward critical path is the sum over steps of the
     slowest rank's launch (communication and overlap not included)."""
@@ -190,7 +196,7 @@ def ring_estimate(bsm, torch, plan, hd, full, perm, k_all, v_all, lay, d, passes
     vs = [v_all[j * S:(j + 1) * S] for j in range(R)]
     t = np.zeros((R, R))
     for rr in range(R):
-        dpr = bsm.DevicePlan(plan, rr)
+        dpr = bsm.DevicePlan(plan, rr, dense=dense)
         q = full[0][torch.from_numpy(perm[rr * S:(rr + 1) * S]).cuda()].contiguous()
         state = bsm.new_state(S, lay.hq, d)
         o = torch.empty(S, lay.hq, d, dtype=torch.bfloat16, device="cuda")
@@ -219,6 +225,47 @@ def ring_estimate(bsm, torch, plan, hd, full, perm, k_all, v_all, lay, d, passes
             "passes": passes}
 
 
+def fit_tau(args, bsm, torch, lay, config_qkv):
+    """Chunk cost C = sum_s max_r W[r][(r - s) mod R] + tau * R * k: least squares
+    of the measured forward critical path t_k = a * P_k + c * R * k + b over chunk
+    counts k (P_k the planner's step-max sum), tau = c / a in pairs."""
+    import dataclasses
+    d = 128
+    hd = bsm.heads(lay.hq, lay.hkv, d, 1.0 / np.sqrt(lay.d))
+    full = config_qkv(lay.n, lay.hq, lay.hkv, d, lay.seed, "cuda")
+    base = bsm.Plan.from_layout(dataclasses.replace(lay, order="contiguous"))
+    R = lay.ranks
+    rows = []
+    for k in (1, 2, 4, 8, 16, 32, 64):
+        try:
+            bperm, ci = base.chunk_order(k, k, 0.0, 4)
+        except bsm.BsmError:
+            break  # fewer blocks than chunks
+        chl = dataclasses.replace(lay, order="explicit", block_perm=bperm)
+        plan = bsm.Plan.from_layout(chl)
+        perm = plan.permutation().astype(np.int64)
+        pidx = torch.from_numpy(perm).cuda()
+        k_all = full[1][pidx].contiguous()
+        v_all = full[2][pidx].contiguous()
+        est = ring_estimate(bsm, torch, plan, hd, full, perm, k_all, v_all, lay, d,
+                            max(1, args.steps // 4), args.dense)
+        rows.append({"k": k, "strategy": ci["strategy"], "step_max_pairs": int(ci["step_max_sum"]),
+                     "critical_path_ms": est["critical_path_ms"]})
+        del k_all, v_all
+    P = np.array([r_["step_max_pairs"] for r_ in rows], float)
+    K = np.array([R * r_["k"] for r_ in rows], float)
+    t = np.array([r_["critical_path_ms"] for r_ in rows], float)
+    A = np.stack([P, K, np.ones_like(P)], axis=1)
+    (a, c, b), *_ = np.linalg.lstsq(A, t, rcond=None)
+    pred = A @ np.array([a, c, b])
+    for r_, p_ in zip(rows, pred):
+        r_["predicted_ms"] = round(float(p_), 4)
+    return {"metric": "chunk cost fit", "workload": lay.name, "mode": "dense calls" if args.dense else "block-sparse",
+            "ranks": R, "ms_per_pair": float(a), "ms_per_range": float(c), "ms_fixed": float(b),
+            "tau_pairs": float(c / a) if a > 0 else None,
+            "max_rel_err": round(float(np.max(np.abs(pred - t) / t)), 4), "points": rows}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -231,6 +278,9 @@ def main():
 
     import dataclasses
     lay = config(args.config)
+    if args.fit_tau:
+        print(json.dumps(fit_tau(args, bsm, torch, lay, qkv)), flush=True)
+        return
     if args.order:
         lay = dataclasses.replace(lay, order=args.order)
     if args.fetch:
@@ -245,7 +295,7 @@ def main():
     plan_s = time.perf_counter() - t0
     r = plan.info["busiest_rank"]
     R, S = lay.ranks, plan.info["shard_tokens"]
-    dp = bsm.DevicePlan(plan, r)
+    dp = bsm.DevicePlan(plan, r, dense=args.dense)
     perm = plan.permutation().astype(np.int64)
     rows = perm[r * S:(r + 1) * S]
     pairs = plan.pairs()[r]
@@ -268,7 +318,10 @@ def main():
     dks = [torch.zeros(S, lay.hkv, d, dtype=torch.float32, device="cuda") for _ in range(R)]
     dvs = [torch.zeros(S, lay.hkv, d, dtype=torch.float32, device="cuda") for _ in range(R)]
     fwd_steps = [s for s in range(R) if dp.info["fwd_items"][s] > 0]
-    do_bwd = not args.fwd_only and args.merge == "carry" and not args.fetch
+    do_bwd = not args.fwd_only and args.merge == "carry" and not args.fetch and not args.dense
+    if args.dense and args.fetch:
+        print(json.dumps({"error": "--dense and --fetch exclude each other"}))
+        sys.exit(2)
 
     if args.fetch:
         kf, vf = bsm.gather_fetched(plan, r, k_all, v_all)
@@ -411,7 +464,7 @@ def main():
         "roofline": {"bound": bound, "kernel": "fwd_kernel", "achieved": round(achieved, 2),
                      "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4),
-                     "traffic": None if args.single else measured_traffic(lay.name),
+                     "traffic": None if args.single or args.dense else measured_traffic(lay.name),
                      "algorithmic_bytes": int(per_launch_bytes),
                      "algorithmic_flops": int(per_launch_flops),
                      "flop_per_byte": round(per_launch_flops / per_launch_bytes, 1),
@@ -422,7 +475,8 @@ def main():
                      "hbm_frac": round(hbm_gbs / PEAK_HBM_GBS, 4),
                      "avg_launch_us": round(avg_launch_ms * 1e3, 2),
                      "launches_per_step": nlaunch},
-        "mode": ("single-pass diagnostic" if args.single else
+        "mode": ("dense calls" + (" (single pass)" if args.single else "") if args.dense else
+                 "single-pass diagnostic" if args.single else
                  "sparse fetch: one pass over the shard and fetched tiles (contiguous chunks)" if args.fetch else
                  "ring" if args.merge == "carry" else f"ring, per-step {args.merge} merge (accuracy control)"),
         "sparse_fetch": sparse_fetch_summary(lay, plan, r),
@@ -435,7 +489,7 @@ def main():
         out["chunking"] = chunk_info
     if args.ring_estimate:
         out["ring_estimate"] = ring_estimate(bsm, torch, plan, hd, full, perm, k_all, v_all,
-                                             lay, d, max(1, args.steps // 4))
+                                             lay, d, max(1, args.steps // 4), args.dense)
     if not args.no_cpu_baseline:
         qc, kc, vc = (t.cpu() for t in full[:3])
         out["cpu_baseline"] = cpu_baseline(lay, None, rows, qc, kc, vc, args.cpu_seconds)

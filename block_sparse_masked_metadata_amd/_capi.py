@@ -34,6 +34,7 @@ BSM_ORDER_CONTIGUOUS, BSM_ORDER_PTRR, BSM_ORDER_EXPLICIT = 0, 1, 2
 BSM_TILE_EMPTY, BSM_TILE_PARTIAL, BSM_TILE_FULL = 0, 1, 2
 BSM_FWD_KEEP_STATE = 1
 BSM_FWD_STEP_ONLY = 2
+BSM_CALL_FULL, BSM_CALL_CAUSAL, BSM_CALL_REVERSE, BSM_CALL_PAST_WINDOW = 0, 1, 2, 3
 
 ORDERS = {"contiguous": BSM_ORDER_CONTIGUOUS, "ptrr": BSM_ORDER_PTRR,
           "explicit": BSM_ORDER_EXPLICIT}
@@ -44,7 +45,8 @@ EXPORTS = [
     "bsm_plan_key_intervals", "bsm_plan_fetch_set", "bsm_plan_chunk_order", "bsm_fwd_fetched",
     "bsm_dplan_bytes", "bsm_dplan_upload", "bsm_dplan_free", "bsm_dplan_get_info",
     "bsm_fwd_step", "bsm_fwd_single", "bsm_fwd_merge_bf16", "bsm_fwd_merge_fp32",
-    "bsm_bwd_prep", "bsm_bwd_step",
+    "bsm_bwd_prep", "bsm_bwd_step", "bsm_plan_dense_calls", "bsm_dplan_calls_bytes",
+    "bsm_dplan_calls_upload",
 ]
 
 
@@ -76,7 +78,12 @@ class bsm_dplan_info(C.Structure):
                 ("tiles_per_shard", C.c_int32), ("window", C.c_int32),
                 ("fwd_items", C.c_int64 * 64), ("bwd_items", C.c_int64 * 64),
                 ("step_pairs", C.c_int64 * 64), ("single_items", C.c_int64),
-                ("fetch_tiles", C.c_int64), ("fetch_rows", C.c_int64)]
+                ("fetch_tiles", C.c_int64), ("fetch_rows", C.c_int64), ("dense_calls", C.c_int32)]
+
+
+class bsm_call(C.Structure):
+    _fields_ = [("q0", C.c_int32), ("q_len", C.c_int32), ("k0", C.c_int32), ("k_len", C.c_int32),
+                ("kind", C.c_int32)]
 
 
 class bsm_chunk_info(C.Structure):
@@ -108,6 +115,9 @@ _sig = {
     "bsm_dplan_bytes": (C.c_int, [_P, C.c_int32, C.POINTER(C.c_int64)]),
     "bsm_dplan_upload": (C.c_int, [_P, C.c_int32, _P, C.c_int64, _P, C.POINTER(_P)]),
     "bsm_dplan_free": (None, [_P]),
+    "bsm_dplan_calls_bytes": (C.c_int, [_P, C.c_int32, C.POINTER(C.c_int64)]),
+    "bsm_dplan_calls_upload": (C.c_int, [_P, C.c_int32, _P, C.c_int64, _P, C.POINTER(_P)]),
+    "bsm_plan_dense_calls": (C.c_int, [_P, C.c_int32, C.c_int32, _P, C.c_int64, C.POINTER(C.c_int64)]),
     "bsm_dplan_get_info": (C.c_int, [_P, C.POINTER(bsm_dplan_info)]),
     "bsm_fwd_step": (C.c_int, [_P, C.c_int32, C.POINTER(bsm_heads), _P, _P, _P, _P, _P, _P,
                                _P, _P, C.c_int32, _P]),
@@ -241,6 +251,28 @@ def bsm_dplan_upload(plan, r, dev_ptr, nbytes, stream):
     return out.value
 
 
+def bsm_dplan_calls_bytes(plan, r) -> int:
+    b = C.c_int64()
+    _check(_lib.bsm_dplan_calls_bytes(plan, int(r), C.byref(b)))
+    return b.value
+
+
+def bsm_dplan_calls_upload(plan, r, dev_ptr, nbytes, stream):
+    out = _P()
+    _check(_lib.bsm_dplan_calls_upload(plan, int(r), dev_ptr, int(nbytes), stream, C.byref(out)))
+    return out.value
+
+
+def bsm_plan_dense_calls(plan, r, s):
+    """int32 array [count, 5]: q0, q_len, k0, k_len, kind per call."""
+    cnt = C.c_int64()
+    _check(_lib.bsm_plan_dense_calls(plan, int(r), int(s), None, 0, C.byref(cnt)))
+    buf = (bsm_call * max(1, cnt.value))()
+    _check(_lib.bsm_plan_dense_calls(plan, int(r), int(s), buf, cnt.value, C.byref(cnt)))
+    return np.ctypeslib.as_array(C.cast(buf, C.POINTER(C.c_int32)), (max(1, cnt.value) * 5,)).reshape(
+        -1, 5)[:cnt.value].copy()
+
+
 def bsm_dplan_free(dplan):
     _lib.bsm_dplan_free(dplan)
 
@@ -253,7 +285,8 @@ def bsm_dplan_get_info(dplan) -> dict:
             "tiles_per_shard": info.tiles_per_shard, "window": info.window,
             "fwd_items": list(info.fwd_items[:rk]), "bwd_items": list(info.bwd_items[:rk]),
             "step_pairs": list(info.step_pairs[:rk]), "single_items": info.single_items,
-            "fetch_tiles": info.fetch_tiles, "fetch_rows": info.fetch_rows}
+            "fetch_tiles": info.fetch_tiles, "fetch_rows": info.fetch_rows,
+            "dense_calls": bool(info.dense_calls)}
 
 
 def _heads(hq, hkv, d, scale):

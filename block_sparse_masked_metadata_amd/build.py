@@ -25,7 +25,7 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
 HOST_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-pthread", "-Wall", "-I", INCLUDE, "-I", CSRC]
 
 HIP_SOURCES = ["fwd.hip", "bwd.hip", "capi.hip"]
-HOST_SOURCES = ["planner.cpp"]
+HOST_SOURCES = ["planner.cpp", "calls.cpp"]
 
 
 def _run(cmds):

@@ -9,6 +9,7 @@
 #include <cstring>
 #include <new>
 #include <string>
+#include <tuple>
 #include <vector>
 
 #include "kernels.hpp"
@@ -62,6 +63,8 @@ struct Packed {
   std::vector<int64_t> off_f, off_b, off_ff;  // off_ff: first list entry of each forward item
   int64_t off_s = 0, off_sf = 0, off_x = 0, off_xf = 0, off_xtracks = 0, off_xkint = 0;
 };
+
+static void layout(const Plan& p, Packed& pk);
 
 static void pack(const Plan& p, int32_t r, Packed& pk) {
   const int32_t R = p.ranks, T = p.tps;
@@ -202,7 +205,12 @@ static void pack(const Plan& p, int32_t r, Packed& pk) {
     std::stable_sort(pk.xitems.begin(), pk.xitems.end(), by_len);
   }
 
-  // byte layout
+  layout(p, pk);
+}
+
+// Byte layout of the device image.
+static void layout(const Plan& p, Packed& pk) {
+  const int32_t R = p.ranks;
   int64_t off = 0;
   pk.off_tracks = off;
   off = align256(off + p.n * (int64_t)sizeof(int4));
@@ -237,9 +245,160 @@ static void pack(const Plan& p, int32_t r, Packed& pk) {
   pk.bytes = std::max<int64_t>(off, 256);
 }
 
+// Position bounds of local rows [a, b) of the shard at plan row `base`;
+// positions rise within each 128-row tile of a shard.
+static void row_bounds(const Plan& p, int64_t base, int64_t a, int64_t b, int64_t& mn, int64_t& mx) {
+  mn = INT64_MAX;
+  mx = INT64_MIN;
+  for (int64_t x = a; x < b;) {
+    const int64_t y = std::min<int64_t>(b, (x / kTile + 1) * kTile);
+    mn = std::min<int64_t>(mn, p.pos[p.perm[base + x]]);
+    mx = std::max<int64_t>(mx, p.pos[p.perm[base + y - 1]]);
+    x = y;
+  }
+}
+
+namespace {
+struct DenseEnt {
+  int32_t k0, kl, qlo, qhi, kind;
+  int64_t qmin, qmax, kmin, kmax;
+};
+}  // namespace
+
+// Dense-call lists of rank r (MARBLE section 03, "Chunked ring attention"):
+// each call of a step becomes, per query tile it meets, one list entry per
+// 128-key piece of its key run, carrying the call's relation and the tile rows
+// it applies to; pieces no pair of which satisfies the relation are dropped,
+// pieces every pair of which does become full.  Entries of one tile with the
+// same rows and keys whose relations leave no pair out merge into one full
+// entry.  Returns BSM_OK or an error code.
+static int pack_calls(const Plan& p, int32_t r, Packed& pk) {
+  const int32_t R = p.ranks, T = p.tps;
+  const int64_t S = p.shard;
+  if (p.pos[p.n - 1] >= INT32_MAX) {
+    set_error("dense calls need positions below 2^31 - 1");
+    return BSM_E_UNSUPPORTED;
+  }
+  pk.tracks.resize(p.n);
+  pk.kint.assign(p.n, make_int2(0, -1));
+  for (int64_t i = 0; i < p.n; ++i) {
+    const int32_t t = p.perm[i];
+    pk.tracks[i] = make_int4(p.sample[t], p.seg[t], p.noise[t], p.pos[t]);
+  }
+  std::vector<std::vector<std::vector<int2>>> lists(R, std::vector<std::vector<int2>>(T));
+  std::vector<Call> calls;
+  std::vector<std::vector<DenseEnt>> per_tile(T);
+  pk.steps.assign(R, StepLists());
+  for (int32_t s = 0; s < R; ++s) {
+    const int32_t j = ((r - s) % R + R) % R;
+    const int64_t qbase = (int64_t)r * S, kbase = (int64_t)j * S;
+    int rc = dense_calls(p, r, s, calls);
+    if (rc) return rc;
+    for (auto& v : per_tile) v.clear();
+    for (const Call& c : calls) {
+      // bounds of the call's key pieces
+      std::vector<std::pair<int64_t, int64_t>> kb;
+      for (int32_t k = c.k0; k < c.k0 + c.kn; k += kTile) {
+        int64_t mn, mx;
+        row_bounds(p, kbase, k, std::min<int64_t>(k + kTile, c.k0 + c.kn), mn, mx);
+        kb.push_back({mn, mx});
+      }
+      for (int32_t a = c.q0 / kTile; a <= (c.q0 + c.qn - 1) / kTile; ++a) {
+        const int32_t ra = std::max(c.q0, a * kTile), rb = std::min(c.q0 + c.qn, (a + 1) * kTile);
+        int64_t qmn, qmx;
+        row_bounds(p, qbase, ra, rb, qmn, qmx);
+        for (size_t i = 0; i < kb.size(); ++i) {
+          const int32_t k = c.k0 + (int32_t)i * kTile;
+          const int cls = relation_bounds(c.kind, qmn, qmx, kb[i].first, kb[i].second, p.window);
+          if (cls == 0) continue;
+          per_tile[a].push_back({k, std::min(kTile, c.k0 + c.kn - k), ra - a * kTile, rb - a * kTile,
+                                 cls == 2 ? (int32_t)kCallFull : c.kind, qmn, qmx, kb[i].first, kb[i].second});
+        }
+      }
+    }
+    for (int32_t a = 0; a < T; ++a) {
+      auto& v = per_tile[a];
+      std::sort(v.begin(), v.end(), [](const DenseEnt& x, const DenseEnt& y) {
+        return std::tie(x.k0, x.kl, x.qlo, x.qhi, x.kind) < std::tie(y.k0, y.kl, y.qlo, y.qhi, y.kind);
+      });
+      const int32_t tile_rows = (int32_t)std::min<int64_t>(kTile, S - (int64_t)a * kTile);
+      for (size_t g = 0; g < v.size();) {
+        size_t h = g + 1;
+        while (h < v.size() && v[h].k0 == v[g].k0 && v[h].kl == v[g].kl && v[h].qlo == v[g].qlo &&
+               v[h].qhi == v[g].qhi)
+          ++h;
+        // relations present; the group is full when every absent one has no pair
+        bool full = h - g > 1;
+        if (full) {
+          uint32_t mask = 0;
+          for (size_t i = g; i < h; ++i) mask |= 1u << v[i].kind;
+          if (mask & (1u << kCallFull)) full = false;
+          for (int32_t kd : {(int32_t)kCallCausal, (int32_t)kCallReverse, (int32_t)kCallPastWindow})
+            if (full && !(mask & (1u << kd)) &&
+                relation_bounds(kd, v[g].qmin, v[g].qmax, v[g].kmin, v[g].kmax, p.window) != 0)
+              full = false;
+        }
+        for (size_t i = g; i < (full ? g + 1 : h); ++i) {
+          const DenseEnt& e = v[i];
+          const int32_t kind = full ? (int32_t)kCallFull : e.kind;
+          const bool whole = e.qlo == 0 && e.qhi == tile_rows;
+          const bool part = !(kind == kCallFull && whole && e.kl == kTile);
+          lists[s][a].push_back(make_int2(e.k0, e.kl | (e.qlo << kRowLoShift) | ((e.qhi - 1) << kRowHiShift) |
+                                                    (kind << kKindShift) | (part ? kPartialBit : 0)));
+        }
+        g = h;
+      }
+    }
+  }
+  std::vector<int32_t> first(T, -1), last(T, -1);
+  for (int32_t s = 0; s < R; ++s)
+    for (int32_t a = 0; a < T; ++a)
+      if (!lists[s][a].empty()) {
+        if (first[a] < 0) first[a] = s;
+        last[a] = s;
+      }
+  auto by_len = [](const int4& x, const int4& y) { return x.w != y.w ? x.w > y.w : x.x < y.x; };
+  pk.entries.clear();
+  for (int32_t s = 0; s < R; ++s) {
+    StepLists& st = pk.steps[s];
+    st.pairs = step_map(p, r, s, nullptr);
+    for (int32_t a = 0; a < T; ++a) {
+      if (lists[s][a].empty()) continue;
+      const int32_t flags = (first[a] == s ? kFirst : 0) | (last[a] == s ? kLast : 0);
+      st.fitems.push_back(make_int4(a, flags, (int32_t)pk.entries.size(), (int32_t)lists[s][a].size()));
+      pk.entries.insert(pk.entries.end(), lists[s][a].begin(), lists[s][a].end());
+    }
+    std::stable_sort(st.fitems.begin(), st.fitems.end(), by_len);
+  }
+  pk.sitems.clear();
+  for (int32_t a = 0; a < T; ++a) {
+    const int32_t beg = (int32_t)pk.entries.size();
+    for (int32_t s = 0; s < R; ++s) {
+      const int32_t j = ((r - s) % R + R) % R;
+      for (const int2& e : lists[s][a]) pk.entries.push_back(make_int2((int32_t)(j * S + e.x), e.y));
+    }
+    const int32_t cnt = (int32_t)pk.entries.size() - beg;
+    if (cnt) pk.sitems.push_back(make_int4(a, kFirst | kLast, beg, cnt));
+  }
+  std::stable_sort(pk.sitems.begin(), pk.sitems.end(), by_len);
+  pk.xitems.clear();
+  pk.xtracks.clear();
+  pk.xkint.clear();
+  pk.fetch_tiles = pk.fetch_rows = 0;
+  layout(p, pk);
+  return BSM_OK;
+}
+
 }  // namespace bsm
 
+static_assert(bsm::kCallFull == bsm::kRelFull && bsm::kCallCausal == bsm::kRelCausal &&
+                  bsm::kCallReverse == bsm::kRelReverse && bsm::kCallPastWindow == bsm::kRelPastWindow &&
+                  bsm::kCallFull == BSM_CALL_FULL && bsm::kCallCausal == BSM_CALL_CAUSAL &&
+                  bsm::kCallReverse == BSM_CALL_REVERSE && bsm::kCallPastWindow == BSM_CALL_PAST_WINDOW,
+              "planner relations and kernel entry relations agree");
+
 struct bsm_dplan {
+  int32_t dense = 0;  // forward lists from dense calls (no backward or fetch lists)
   int32_t r = 0, R = 1, tps = 0, window = 0;
   int64_t S = 0, n = 0;
   const int4* tracks = nullptr;
@@ -379,13 +538,21 @@ int bsm_plan_pairs(const bsm_plan* plan, int64_t* pairs) {
   return BSM_OK;
 }
 
-int bsm_dplan_bytes(const bsm_plan* plan, int32_t r, int64_t* bytes) {
+}  // extern "C"
+
+namespace {
+int dplan_bytes(const bsm_plan* plan, int32_t r, bool dense, int64_t* bytes) {
   if (!plan || !bytes) { set_error("null argument"); return BSM_E_INVALID; }
   if (r < 0 || r >= plan->p.ranks) { set_error("rank out of range"); return BSM_E_INVALID; }
   if (plan->p.block != kTile) { set_error("device plans need block == 128"); return BSM_E_UNSUPPORTED; }
   try {
     Packed pk;
-    pack(plan->p, r, pk);
+    if (dense) {
+      const int rc = pack_calls(plan->p, r, pk);
+      if (rc) return rc;
+    } else {
+      pack(plan->p, r, pk);
+    }
     *bytes = pk.bytes;
   } catch (const std::bad_alloc&) {
     set_error("out of host memory");
@@ -394,8 +561,8 @@ int bsm_dplan_bytes(const bsm_plan* plan, int32_t r, int64_t* bytes) {
   return BSM_OK;
 }
 
-int bsm_dplan_upload(const bsm_plan* plan, int32_t r, void* dev, int64_t bytes, void* stream,
-                     bsm_dplan** out) {
+int dplan_upload(const bsm_plan* plan, int32_t r, bool dense, void* dev, int64_t bytes, void* stream,
+                 bsm_dplan** out) {
   if (!plan || !dev || !out) { set_error("null argument"); return BSM_E_INVALID; }
   *out = nullptr;
   if (r < 0 || r >= plan->p.ranks) { set_error("rank out of range"); return BSM_E_INVALID; }
@@ -403,7 +570,12 @@ int bsm_dplan_upload(const bsm_plan* plan, int32_t r, void* dev, int64_t bytes, 
   const Plan& p = plan->p;
   try {
     Packed pk;
-    pack(p, r, pk);
+    if (dense) {
+      const int rc = pack_calls(p, r, pk);
+      if (rc) return rc;
+    } else {
+      pack(p, r, pk);
+    }
     if (bytes < pk.bytes) {
       set_error("device plan buffer too small: need " + std::to_string(pk.bytes) + " bytes");
       return BSM_E_NOMEM;
@@ -434,6 +606,7 @@ int bsm_dplan_upload(const bsm_plan* plan, int32_t r, void* dev, int64_t bytes, 
     if (rc) return rc;
     bsm_dplan* d = new bsm_dplan();
     char* base = (char*)dev;
+    d->dense = dense ? 1 : 0;
     d->r = r;
     d->R = p.ranks;
     d->tps = p.tps;
@@ -468,6 +641,52 @@ int bsm_dplan_upload(const bsm_plan* plan, int32_t r, void* dev, int64_t bytes, 
   }
   return BSM_OK;
 }
+}  // namespace
+
+extern "C" {
+
+int bsm_dplan_bytes(const bsm_plan* plan, int32_t r, int64_t* bytes) {
+  return dplan_bytes(plan, r, false, bytes);
+}
+
+int bsm_dplan_upload(const bsm_plan* plan, int32_t r, void* dev, int64_t bytes, void* stream,
+                     bsm_dplan** out) {
+  return dplan_upload(plan, r, false, dev, bytes, stream, out);
+}
+
+int bsm_dplan_calls_bytes(const bsm_plan* plan, int32_t r, int64_t* bytes) {
+  return dplan_bytes(plan, r, true, bytes);
+}
+
+int bsm_dplan_calls_upload(const bsm_plan* plan, int32_t r, void* dev, int64_t bytes, void* stream,
+                           bsm_dplan** out) {
+  return dplan_upload(plan, r, true, dev, bytes, stream, out);
+}
+
+int bsm_plan_dense_calls(const bsm_plan* plan, int32_t r, int32_t s, bsm_call* calls, int64_t capacity,
+                         int64_t* count) {
+  if (!plan || !count) { set_error("null argument"); return BSM_E_INVALID; }
+  if (r < 0 || r >= plan->p.ranks || s < 0 || s >= plan->p.ranks) {
+    set_error("rank or step out of range");
+    return BSM_E_INVALID;
+  }
+  try {
+    std::vector<Call> v;
+    const int rc = dense_calls(plan->p, r, s, v);
+    if (rc) return rc;
+    *count = (int64_t)v.size();
+    if (!calls) return BSM_OK;
+    if (capacity < (int64_t)v.size()) {
+      set_error("call buffer too small: need " + std::to_string(v.size()) + " calls");
+      return BSM_E_NOMEM;
+    }
+    for (size_t i = 0; i < v.size(); ++i) calls[i] = bsm_call{v[i].q0, v[i].qn, v[i].k0, v[i].kn, v[i].kind};
+  } catch (const std::bad_alloc&) {
+    set_error("out of host memory");
+    return BSM_E_NOMEM;
+  }
+  return BSM_OK;
+}
 
 void bsm_dplan_free(bsm_dplan* dplan) { delete dplan; }
 
@@ -487,6 +706,7 @@ int bsm_dplan_get_info(const bsm_dplan* d, bsm_dplan_info* out) {
   out->single_items = d->ns;
   out->fetch_tiles = d->fetch_tiles;
   out->fetch_rows = d->fetch_rows;
+  out->dense_calls = d->dense;
   return BSM_OK;
 }
 
@@ -529,6 +749,7 @@ int bsm_fwd_step(const bsm_dplan* d, int32_t s, const bsm_heads* heads, const vo
   a.window = d->window;
   a.keep_state = keep ? 1 : 0;
   a.step_only = (flags & BSM_FWD_STEP_ONLY) != 0 ? 1 : 0;
+  a.dense = d->dense;
   hipStream_t st = (hipStream_t)stream;
   return hip_status(launch_fwd(a, st), "forward step launch", st);
 }
@@ -546,6 +767,10 @@ int fwd_pass(const bsm_dplan* d, bool fetched, const bsm_heads* heads, const voi
   if (!q || !k_all || !v_all || (keep && (!o_acc || !m || !l)) || (!keep && (!o || !lse))) {
     set_error("null tensor pointer");
     return BSM_E_INVALID;
+  }
+  if (fetched && d->dense) {
+    set_error("a dense-call device plan has no sparse-fetch lists");
+    return BSM_E_UNSUPPORTED;
   }
   const int64_t krows = fetched ? d->fetch_rows : (int64_t)d->S * d->R;
   if ((rc = check_rows(d->S, heads->hq, "q")) || (rc = check_rows(krows, heads->hkv, "keys/values")))
@@ -576,6 +801,7 @@ int fwd_pass(const bsm_dplan* d, bool fetched, const bsm_heads* heads, const voi
   a.window = d->window;
   a.keep_state = keep ? 1 : 0;
   a.step_only = (flags & BSM_FWD_STEP_ONLY) != 0 ? 1 : 0;
+  a.dense = d->dense;
   hipStream_t st = (hipStream_t)stream;
   return hip_status(launch_fwd(a, st), fetched ? "forward fetched launch" : "forward single launch", st);
 }
@@ -654,6 +880,10 @@ int bsm_bwd_step(const bsm_dplan* d, int32_t s, const bsm_heads* heads, const vo
   int rc = check_heads(heads);
   if (rc) return rc;
   if (s < 0 || s >= d->R) { set_error("step out of range"); return BSM_E_INVALID; }
+  if (d->dense) {
+    set_error("a dense-call device plan has no backward lists");
+    return BSM_E_UNSUPPORTED;
+  }
   if (!q || !k || !v || !dout || !lse || !delta || !dq_acc || !dk || !dv) {
     set_error("null tensor pointer");
     return BSM_E_INVALID;

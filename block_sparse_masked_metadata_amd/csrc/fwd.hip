@@ -104,12 +104,17 @@ struct SubTile {
 // On partial sub-tiles the key's mask data rides along: its tracks, or with
 // `interval` its key interval (lo, hi) in the first two fields.  Keys past len
 // keep (-1, -1, -1, 0): sample -1 and the empty range [-1, -1) admit no query.
+// With kDense (dense-call lists) a partial sub-tile carries only the key's
+// position, and keys past len take position 2^31 - 1, outside every range.
+template <bool kDense>
 __device__ inline void fetch_sub(SubTile& t, const char* kbase, const char* vbase,
                                  const int4* ktracks, const int2* kint, int32_t k0, int len, bool partial,
                                  bool interval, uint32_t row_bytes, uint32_t lane_off, int tid) {
-  t.kt = make_int4(-1, -1, -1, 0);
+  t.kt = make_int4(kDense ? INT32_MAX : -1, -1, -1, 0);
   if (partial && tid < len) {
-    if (interval) {
+    if (kDense) {
+      t.kt.x = ktracks[k0 + tid].w;
+    } else if (interval) {
       const int2 iv = kint[k0 + tid];
       t.kt = make_int4(iv.x, iv.y, 0, 0);
     } else {
@@ -153,7 +158,7 @@ __device__ inline void store_sub(const SubTile& t, char* sK, char* sV, int4* sKT
 // Sub-tile n of an item: half n%2 of list entry n/2.
 __device__ inline void sub_bounds(const int2 ent, int n, int32_t& k0, int& len, bool& partial, bool& interval) {
   const int half = n & 1;
-  const int klen = ent.y & 0xffff;
+  const int klen = ent.y & kLenMask;
   k0 = ent.x + half * kSub;
   len = klen - half * kSub;
   len = len < 0 ? 0 : (len > kSub ? kSub : len);
@@ -161,11 +166,27 @@ __device__ inline void sub_bounds(const int2 ent, int n, int32_t& k0, int& len, 
   interval = (ent.y & kIntervalBit) != 0;
 }
 
+// Key positions legal for query row `row` of its tile (position pq) under a
+// dense-call entry: [lo, lo + span), span 0 for rows outside the entry.
+__device__ inline void dense_range(int32_t y, int row, int32_t pq, int32_t window, int32_t& lo, uint32_t& span) {
+  const int kind = (y >> kKindShift) & 3;
+  const int rlo = (y >> kRowLoShift) & 127, rhi = ((y >> kRowHiShift) & 127) + 1;
+  // pq >= 0 and 1 <= window <= 2^31 - 1: no overflow below
+  const int32_t below = pq - window + 1;
+  lo = kind == kRelCausal ? below : kind == kRelReverse ? pq + 1 : INT32_MIN;
+  const int32_t hi = kind == kRelCausal ? pq + 1 : kind == kRelPastWindow ? below : INT32_MAX;
+  span = (uint32_t)(row - rlo) < (uint32_t)(rhi - rlo) ? (uint32_t)hi - (uint32_t)lo : 0u;
+}
+
 // S^T = K Q^T for one 64-key sub-tile: s[kb][r] = S[query l32][key 32kb + 8(r/4) + 4hi + r%4],
 // operand reads issued 4 at a time ahead of their MFMAs; on partial sub-tiles
 // illegal pairs (and keys past len) become -inf.
+// With kDense, a partial sub-tile keeps the pairs whose key position lies in
+// the range dense_range gives the lane's query for entry word `ey`.
+template <bool kDense>
 __device__ inline void scores(f32x16 (&s)[2], const char* sK, const bf16x8 (&qf)[8], const int4* sKT,
-                              const int4 qt, bool partial, bool interval, int32_t window, int l32, int hi) {
+                              const int4 qt, bool partial, bool interval, int32_t window, int l32, int hi,
+                              int32_t ey, int row) {
   __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
@@ -185,7 +206,20 @@ __device__ inline void scores(f32x16 (&s)[2], const char* sK, const bf16x8 (&qf)
     }
   }
   __builtin_amdgcn_s_setprio(0);
-  if (partial && interval) {
+  if (kDense) {
+    if (partial) {
+      int32_t dlo;
+      uint32_t dspan;
+      dense_range(ey, row, qt.w, window, dlo, dspan);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+          s[kb][r] = (uint32_t)(sKT[key].x - dlo) < dspan ? s[kb][r] : kNegInf;
+        }
+    }
+  } else if (partial && interval) {
     // Key intervals: legal iff lo <= pos_q < hi, one unsigned compare.
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -222,6 +256,7 @@ __device__ inline float exp_sum(f32x16 (&s)[2], float scale_log2, float nbase) {
   return ls;
 }
 
+template <bool kDense>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char sK[kSub * 256];
   __shared__ __attribute__((aligned(1024))) char sV[kSub * 256];
@@ -266,7 +301,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a) {
     int len;
     bool part, kin;
     sub_bounds(ent, 0, k0, len, part, kin);
-    fetch_sub(pf, kbase, vbase, a.ktracks, a.kint, k0, len, part, kin, row_bytes, lane_off, tid);
+    fetch_sub<kDense>(pf, kbase, vbase, a.ktracks, a.kint, k0, len, part, kin, row_bytes, lane_off, tid);
   }
 
   // Q^T as the B operand: lane holds query l32, channels [16kk + 8hi, +8).
@@ -323,6 +358,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a) {
     int len;
     bool partial, interval;
     sub_bounds(ent, n, k0, len, partial, interval);
+    const int32_t ey = ent.y;
     __syncthreads();  // sub-tile n is in LDS
     const bool more = n + 1 < nsub;
     if (more) {
@@ -340,11 +376,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a) {
       int nlen;
       bool npart, nkin;
       sub_bounds(ent, n + 1, nk0, nlen, npart, nkin);
-      fetch_sub(pf, kbase, vbase, a.ktracks, a.kint, nk0, nlen, npart, nkin, row_bytes, lane_off, tid);
+      fetch_sub<kDense>(pf, kbase, vbase, a.ktracks, a.kint, nk0, nlen, npart, nkin, row_bytes, lane_off, tid);
     }
 
     f32x16 s[2];
-    scores(s, sK, qf, sKT, qt, partial, interval, a.window, l32, hi);
+    scores<kDense>(s, sK, qf, sKT, qt, partial, interval, a.window, l32, hi, ey, (int)qi);
 
     // Online softmax in base-2 units against a lazily updated reference mref.
     // Common case: exponentiate against the current reference; every p stays
@@ -359,7 +395,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a) {
       ls = exp_sum(s, a.scale_log2, -mref);
       if (__any(!(ls < kSumCap))) {
         fast = false;
-        scores(s, sK, qf, sKT, qt, partial, interval, a.window, l32, hi);
+        scores<kDense>(s, sK, qf, sKT, qt, partial, interval, a.window, l32, hi, ey, (int)qi);
       }
     }
     if (!fast) {
@@ -535,7 +571,10 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(int64_t pairs, int64_t ro
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   const int64_t blocks = (int64_t)a.nitems * a.hq;
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fwd_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  if (a.dense)
+    hipLaunchKernelGGL(fwd_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(fwd_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

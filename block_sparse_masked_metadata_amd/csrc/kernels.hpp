@@ -24,6 +24,15 @@ enum : int32_t { kFirst = 1, kLast = 2, kKeyInterval = 4 };
 // partner tile has a key interval.
 constexpr int32_t kPartialBit = 1 << 16;
 constexpr int32_t kIntervalBit = 1 << 17;
+constexpr int32_t kLenMask = 0xff;  // valid rows: at most 128
+// Dense-call entries (forward lists of a dense-call device plan): the entry
+// applies to query rows [lo, hi] of its tile, lo in bits 8-14 and hi in bits
+// 24-30, and bits 19-20 hold the relation its pairs satisfy (kCallFull,
+// kCallCausal, kCallReverse or kCallPastWindow of the planner).  With the
+// partial bit the kernel tests row range and relation (one compare per pair),
+// and masks keys past the valid rows.
+constexpr int kRowLoShift = 8, kRowHiShift = 24, kKindShift = 19;
+enum : int32_t { kRelFull = 0, kRelCausal = 1, kRelReverse = 2, kRelPastWindow = 3 };
 
 // Key interval of a token (int2): the queries it is legal for are exactly
 // those with x <= pos < y; y < x when it has none (the planner's key_interval).
@@ -54,6 +63,7 @@ struct FwdArgs {
   int32_t window;
   int32_t keep_state;
   int32_t step_only;        // ignore the carried state and finalize every item
+  int32_t dense;            // the lists hold dense-call entries
 };
 
 struct BwdArgs {

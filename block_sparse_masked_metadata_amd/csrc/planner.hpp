@@ -64,6 +64,18 @@ struct ChunkResult {
 int chunk_order(const Plan& p, int32_t min_chunks, int32_t max_chunks, double tau, int32_t swaps,
                 int32_t* block_perm, ChunkResult& out);
 
+// Dense calls of rank r at step s (see calls.cpp): query rows [q0, q0 + qn)
+// of rank r's shard against key rows [k0, k0 + kn) of shard (r - s) mod R,
+// every pair of whose positions satisfies the relation `kind` computed.
+enum : int32_t { kCallFull = 0, kCallCausal = 1, kCallReverse = 2, kCallPastWindow = 3 };
+struct Call {
+  int32_t q0, qn, k0, kn, kind;
+};
+int dense_calls(const Plan& p, int32_t r, int32_t s, std::vector<Call>& out);
+// 0: no pair of the position bounds satisfies relation `kind`, 2: every
+// pair does, 1: some may.
+int relation_bounds(int32_t kind, int64_t qmin, int64_t qmax, int64_t kmin, int64_t kmax, int64_t w);
+
 }  // namespace bsm
 
 struct bsm_plan {

@@ -58,6 +58,10 @@ class Plan:
         """Chunked ring layout: (explicit block order, cost terms)."""
         return C.bsm_plan_chunk_order(self.handle, min_chunks, max_chunks, tau, swaps)
 
+    def dense_calls(self, r, s):
+        """int32 [count, 5] (q0, q_len, k0, k_len, kind): rank r's dense calls at step s."""
+        return C.bsm_plan_dense_calls(self.handle, r, s)
+
     def fetch_set(self, r):
         """(needed [R, tiles_per_shard] uint8, count): remote key tiles rank r needs."""
         return C.bsm_plan_fetch_set(self.handle, r)
@@ -81,11 +85,14 @@ class Plan:
 class DevicePlan:
     """Rank r's device plan in a torch uint8 buffer (the library allocates nothing)."""
 
-    def __init__(self, plan: Plan, r: int, device="cuda"):
+    def __init__(self, plan: Plan, r: int, device="cuda", dense=False):
+        """dense: forward lists from the plan's dense calls (forward steps and
+        the single pass only)."""
         import torch
-        nbytes = C.bsm_dplan_bytes(plan.handle, r)
+        nbytes = (C.bsm_dplan_calls_bytes if dense else C.bsm_dplan_bytes)(plan.handle, r)
         self.buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
-        self.handle = C.bsm_dplan_upload(plan.handle, r, self.buf.data_ptr(), nbytes, _stream())
+        upload = C.bsm_dplan_calls_upload if dense else C.bsm_dplan_upload
+        self.handle = upload(plan.handle, r, self.buf.data_ptr(), nbytes, _stream())
         self.info = C.bsm_dplan_get_info(self.handle)
         self.rank = r
         self.ranks = plan.info["ranks"]

@@ -217,6 +217,44 @@ int bsm_plan_fetch_set(const bsm_plan* plan, int32_t r, uint8_t* needed, int64_t
  */
 int bsm_plan_key_intervals(const bsm_plan* plan, int32_t* lo, int32_t* hi);
 
+/*
+ * Dense calls (MARBLE section 03, "Chunked ring attention": for long, mostly
+ * dense samples each ring step runs as a few dense calls, full, causal or
+ * reverse causal over runs of tokens, instead of one masked block-sparse
+ * call).  The calls of rank r at step s cover every legal pair between rank
+ * r's query shard and key shard (r - s) mod R exactly once and no illegal one.
+ * A call pairs query rows [q0, q0 + q_len) of the query shard with key rows
+ * [k0, k0 + k_len) of the key shard (plan order, local to each shard) and
+ * computes the pairs whose positions satisfy `kind`:
+ *   BSM_CALL_FULL         every pair
+ *   BSM_CALL_CAUSAL       0 <= pos_q - pos_k < W (W: the plan's window)
+ *   BSM_CALL_REVERSE      pos_k > pos_q
+ *   BSM_CALL_PAST_WINDOW  pos_q - pos_k >= W (finite windows only)
+ * The families behind them: each sample's queries against its clean
+ * (noise < 0) keys, causal; each seg's queries against the seg's clean keys,
+ * the rest of the seg (reverse, past window); each noise span's queries
+ * against the span's keys, full when the whole span has one seg >= 0, else
+ * causal plus the per-seg rest.
+ * *count receives the number of calls; with calls != NULL and capacity >=
+ * *count they are written to calls (host memory), with a smaller capacity the
+ * call fails with BSM_E_NOMEM.
+ */
+typedef enum {
+  BSM_CALL_FULL = 0,
+  BSM_CALL_CAUSAL = 1,
+  BSM_CALL_REVERSE = 2,
+  BSM_CALL_PAST_WINDOW = 3
+} bsm_call_kind;
+
+typedef struct {
+  int32_t q0, q_len;         /* query rows of rank r's shard                  */
+  int32_t k0, k_len;         /* key rows of shard (r - s) mod R               */
+  int32_t kind;              /* bsm_call_kind                                 */
+} bsm_call;
+
+int bsm_plan_dense_calls(const bsm_plan* plan, int32_t r, int32_t s, bsm_call* calls,
+                         int64_t capacity, int64_t* count);
+
 /* ====================================================================== *
  *  Device plan: one rank's lists, packed into caller-owned device memory. *
  * ====================================================================== */
@@ -239,6 +277,20 @@ int bsm_dplan_upload(const bsm_plan* plan, int32_t r, void* dev, int64_t bytes,
                      void* stream, bsm_dplan** out);
 void bsm_dplan_free(bsm_dplan* dplan);
 
+/*
+ * Dense-call device plan of rank r (MARBLE section 03, "Chunked ring
+ * attention"): its forward lists run the calls of bsm_plan_dense_calls, each
+ * as 128-key pieces of its key run for every query tile it meets, tested by
+ * row range and one position compare (pieces every pair of which satisfies the
+ * relation run unmasked).  Same memory rules as bsm_dplan_bytes /
+ * bsm_dplan_upload.  bsm_fwd_step and bsm_fwd_single accept the handle with the
+ * same arguments and results; bsm_fwd_fetched and bsm_bwd_step refuse it with
+ * BSM_E_UNSUPPORTED.  Needs every position below 2^31 - 1 (BSM_E_UNSUPPORTED).
+ */
+int bsm_dplan_calls_bytes(const bsm_plan* plan, int32_t r, int64_t* bytes);
+int bsm_dplan_calls_upload(const bsm_plan* plan, int32_t r, void* dev, int64_t bytes,
+                           void* stream, bsm_dplan** out);
+
 typedef struct {
   int32_t rank;
   int32_t ranks;
@@ -251,6 +303,7 @@ typedef struct {
   int64_t single_items;      /* query tiles with work in the merged list      */
   int64_t fetch_tiles;       /* remote key tiles the rank needs (sparse fetch) */
   int64_t fetch_rows;        /* rows of the compact key/value buffer          */
+  int32_t dense_calls;       /* 1: a dense-call device plan                   */
 } bsm_dplan_info;
 
 int bsm_dplan_get_info(const bsm_dplan* dplan, bsm_dplan_info* out);

@@ -6,6 +6,7 @@ import torch
 
 import block_sparse_masked_metadata_amd as bsm
 from workloads import qkv
+from oracle import attention as oatt
 
 O_TOL = 1e-2      # max |O - O_ref| for bf16 inputs
 LSE_TOL = 1e-3    # max |LSE - LSE_ref|
@@ -17,14 +18,14 @@ needs_gpu = torch.cuda.is_available()
 class Case:
     """One rank's share of a layout on the GPU."""
 
-    def __init__(self, lay, rank=None, with_do=False, tensors=None, hq=None, hkv=None):
+    def __init__(self, lay, rank=None, with_do=False, tensors=None, hq=None, hkv=None, dense=False):
         self.lay = lay
         self.hq = hq or lay.hq
         self.hkv = hkv or lay.hkv
         self.d = 128
         self.plan = bsm.Plan.from_layout(lay)
         self.r = self.plan.info["busiest_rank"] if rank is None else rank
-        self.dp = bsm.DevicePlan(self.plan, self.r)
+        self.dp = bsm.DevicePlan(self.plan, self.r, dense=dense)
         self.R = lay.ranks
         self.S = self.plan.info["shard_tokens"]
         self.perm = self.plan.permutation().astype(np.int64)
@@ -65,3 +66,30 @@ def grad_ok(g, ref, name):
     err = float(np.abs(np.asarray(g, np.float64) - ref).max())
     assert err <= tol, f"{name}: max err {err:.3e} > {tol:.3e}"
     return err
+
+
+def check_rows(case, o, lse, sel=None, tol_o=O_TOL, tol_lse=LSE_TOL, single=False):
+    """Compare GPU rows (indices into the rank's shard) with the oracle.
+
+    The O bar applies to the value the kernel rounds to bf16 (O_acc / l from a
+    KEEP_STATE run of the same launches); the bf16 output must be exactly that
+    value rounded to nearest even.  LSE is compared as written."""
+    sel = np.arange(case.S) if sel is None else np.asarray(sel)
+    q, k, v = case.cpu(0), case.cpu(1), case.cpu(2)
+    o_ref, lse_ref = oatt.forward_rows(case.lay.tracks(), case.lay.window, q, k, v,
+                                       case.rows[sel], 1.0 / np.sqrt(case.lay.d))
+    tsel = torch.from_numpy(sel).cuda()
+    acc, m, l = case.single(keep_state=True) if single else case.ring(keep_state=True)[2]
+    acc = acc[tsel].cpu()
+    l = l[:, tsel].cpu().T[:, :, None]
+    o32 = torch.where(l > 0, acc / torch.where(l > 0, l, torch.ones_like(l)), torch.zeros_like(acc))
+    og = o[tsel].cpu()
+    assert torch.equal(og, o32.to(torch.bfloat16)), "bf16 O is not RNE(O_acc / l)"
+    lg = lse[:, tsel].cpu().numpy()
+    eo = max_err(o32.numpy(), o_ref)
+    eob = max_err(og.float().numpy(), o_ref)
+    el = max_err(lg, lse_ref)
+    print(f"  rank={case.r} rows={len(sel)} max|dO32|={eo:.3e} max|dO_bf16|={eob:.3e} "
+          f"max|dLSE|={el:.3e}", flush=True)
+    assert eo <= tol_o and el <= tol_lse
+    return eo, el

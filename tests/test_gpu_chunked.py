@@ -1,6 +1,7 @@
-"""GPU parity on chunked ring layouts (MARBLE section 03, "Chunked ring
-attention"): each rank owns k contiguous chunks chosen by the planner's
-search; every rank's ring steps must still match the fp64 oracle."""
+"""GPU parity on chunked ring layouts and of the dense-call mode (MARBLE
+section 03, "Chunked ring attention"): each rank owns k contiguous chunks
+chosen by the planner's search, and each ring step can run as dense calls;
+every rank's ring steps must still match the fp64 oracle."""
 import dataclasses
 
 import numpy as np
@@ -8,9 +9,8 @@ import pytest
 import torch
 
 import block_sparse_masked_metadata_amd as bsm
-from workloads import random_small, packed_multimodal
-from oracle import attention as oatt
-from gpu_common import Case, O_TOL, LSE_TOL, max_err, needs_gpu
+from workloads import random_small, packed_multimodal, long_mixed, packed_text
+from gpu_common import Case, check_rows, needs_gpu
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not needs_gpu, reason="needs a GPU")]
 
@@ -21,17 +21,10 @@ def _chunked(lay, min_chunks, max_chunks, tau=0.0, swaps=2):
     return dataclasses.replace(lay, order="explicit", block_perm=perm), info
 
 
-def _check(case, sel):
-    o, lse, _ = case.ring()
+def _check(case, sel, single=False):
+    o, lse = case.single() if single else case.ring()[:2]
     torch.cuda.synchronize()
-    o_ref, lse_ref = oatt.forward_rows(case.lay.tracks(), case.lay.window, case.cpu(0),
-                                       case.cpu(1), case.cpu(2), case.rows[sel],
-                                       1.0 / np.sqrt(case.lay.d))
-    tsel = torch.from_numpy(sel).cuda()
-    eo = max_err(o[tsel].float().cpu().numpy(), o_ref)
-    el = max_err(lse[:, tsel].cpu().numpy(), lse_ref)
-    print(f"  rank={case.r} rows={len(sel)} max|dO|={eo:.3e} max|dLSE|={el:.3e}", flush=True)
-    assert eo <= O_TOL and el <= LSE_TOL
+    check_rows(case, o, lse, sel, single=single)
 
 
 @pytest.mark.parametrize("seed", range(3))
@@ -55,3 +48,53 @@ def test_chunked_packed_multimodal_sampled():
     case = Case(lay)
     rng = np.random.default_rng(3)
     _check(case, np.sort(rng.choice(case.S, 512, replace=False)))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_dense_calls_random_every_rank(seed):
+    """All five span modes, noise spans and finite windows, every rank."""
+    rng = np.random.default_rng(1300 + seed)
+    R = [1, 2, 4, 3, 2, 4][seed]
+    lay = random_small(rng, 128 * R * [2, 3, 1, 2, 4, 2][seed], max_span=[300, 40, 500, 120, 60, 900][seed])
+    lay.ranks, lay.seed = R, 80 + seed
+    lay.order = ["ptrr", "contiguous"][seed % 2]
+    lay.hq, lay.hkv = [(4, 2), (2, 1), (8, 8), (4, 1), (6, 2), (2, 2)][seed]
+    lay.d = 128
+    print(f"  window={lay.window} order={lay.order}", flush=True)
+    for r in range(R):
+        case = Case(lay, rank=r, dense=True)
+        assert case.dp.info["dense_calls"]
+        _check(case, np.arange(case.S))
+
+
+def test_dense_calls_single_pass_matches_oracle():
+    rng = np.random.default_rng(1400)
+    lay = random_small(rng, 128 * 3 * 2, max_span=200)
+    lay.ranks, lay.seed, lay.order = 3, 91, "ptrr"
+    lay.hq, lay.hkv, lay.d = 4, 2, 128
+    for r in range(3):
+        _check(Case(lay, rank=r, dense=True), np.arange(128 * 2), single=True)
+
+
+def test_dense_calls_packed_text_full_share():
+    case = Case(packed_text(), dense=True)
+    _check(case, np.arange(case.S))
+
+
+def test_dense_calls_long_mixed_chunked_sampled():
+    lay, info = _chunked(long_mixed(), 1, 8)
+    case = Case(lay, dense=True)
+    rng = np.random.default_rng(4)
+    _check(case, np.sort(rng.choice(case.S, 256, replace=False)))
+
+
+def test_dense_calls_refuse_backward_and_fetch():
+    case = Case(packed_text(), dense=True)
+    C = bsm._capi
+    z = case.q.data_ptr()
+    with pytest.raises(bsm.BsmError) as e:
+        C.bsm_bwd_step(case.dp.handle, 0, case.heads, z, z, z, z, z, z, z, z, z, None)
+    assert e.value.code == C.BSM_E_UNSUPPORTED
+    with pytest.raises(bsm.BsmError) as e:
+        C.bsm_fwd_fetched(case.dp.handle, case.heads, z, z, z, None, None, None, z, z, 0, None)
+    assert e.value.code == C.BSM_E_UNSUPPORTED

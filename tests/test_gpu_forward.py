@@ -8,36 +8,13 @@ from workloads import (ring_toy, toy_qkv, random_small, packed_text, packed_mult
                        sliding_window, long_mixed)
 from oracle import attention as oatt
 from oracle.mask import legal, take
-from gpu_common import Case, O_TOL, LSE_TOL, max_err, needs_gpu
+from gpu_common import Case, O_TOL, LSE_TOL, check_rows, max_err, needs_gpu
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not needs_gpu, reason="needs a GPU")]
 
 
 def _check_rows(case, o, lse, sel=None, tol_o=O_TOL, tol_lse=LSE_TOL):
-    """Compare GPU rows (indices into the rank's shard) with the oracle.
-
-    The O bar applies to the value the kernel rounds to bf16 (O_acc / l from a
-    KEEP_STATE run of the same steps); the bf16 output must be exactly that
-    value rounded to nearest even.  LSE is compared as written."""
-    sel = np.arange(case.S) if sel is None else np.asarray(sel)
-    q, k, v = case.cpu(0), case.cpu(1), case.cpu(2)
-    o_ref, lse_ref = oatt.forward_rows(case.lay.tracks(), case.lay.window, q, k, v,
-                                       case.rows[sel], 1.0 / np.sqrt(case.lay.d))
-    tsel = torch.from_numpy(sel).cuda()
-    _, _, (acc, m, l) = case.ring(keep_state=True)
-    acc = acc[tsel].cpu()
-    l = l[:, tsel].cpu().T[:, :, None]
-    o32 = torch.where(l > 0, acc / torch.where(l > 0, l, torch.ones_like(l)), torch.zeros_like(acc))
-    og = o[tsel].cpu()
-    assert torch.equal(og, o32.to(torch.bfloat16)), "bf16 O is not RNE(O_acc / l)"
-    lg = lse[:, tsel].cpu().numpy()
-    eo = max_err(o32.numpy(), o_ref)
-    eob = max_err(og.float().numpy(), o_ref)
-    el = max_err(lg, lse_ref)
-    print(f"  rows={len(sel)} max|dO32|={eo:.3e} max|dO_bf16|={eob:.3e} max|dLSE|={el:.3e}",
-          flush=True)
-    assert eo <= tol_o and el <= tol_lse
-    return eo, el
+    return check_rows(case, o, lse, sel, tol_o, tol_lse)
 
 
 def test_ring_toy():

@@ -46,7 +46,7 @@ EXPORTS = [
     "bsm_dplan_bytes", "bsm_dplan_upload", "bsm_dplan_free", "bsm_dplan_get_info",
     "bsm_fwd_step", "bsm_fwd_single", "bsm_fwd_merge_bf16", "bsm_fwd_merge_fp32",
     "bsm_bwd_prep", "bsm_bwd_step", "bsm_plan_dense_calls", "bsm_dplan_calls_bytes",
-    "bsm_dplan_calls_upload",
+    "bsm_dplan_calls_upload", "bsm_state_unpack",
 ]
 
 
@@ -115,6 +115,7 @@ _sig = {
     "bsm_dplan_bytes": (C.c_int, [_P, C.c_int32, C.POINTER(C.c_int64)]),
     "bsm_dplan_upload": (C.c_int, [_P, C.c_int32, _P, C.c_int64, _P, C.POINTER(_P)]),
     "bsm_dplan_free": (None, [_P]),
+    "bsm_state_unpack": (C.c_int, [C.POINTER(bsm_heads), C.c_int64, _P, _P, _P]),
     "bsm_dplan_calls_bytes": (C.c_int, [_P, C.c_int32, C.POINTER(C.c_int64)]),
     "bsm_dplan_calls_upload": (C.c_int, [_P, C.c_int32, _P, C.c_int64, _P, C.POINTER(_P)]),
     "bsm_plan_dense_calls": (C.c_int, [_P, C.c_int32, C.c_int32, _P, C.c_int64, C.POINTER(C.c_int64)]),
@@ -271,6 +272,10 @@ def bsm_plan_dense_calls(plan, r, s):
     _check(_lib.bsm_plan_dense_calls(plan, int(r), int(s), buf, cnt.value, C.byref(cnt)))
     return np.ctypeslib.as_array(C.cast(buf, C.POINTER(C.c_int32)), (max(1, cnt.value) * 5,)).reshape(
         -1, 5)[:cnt.value].copy()
+
+
+def bsm_state_unpack(heads, rows, o_acc, out, stream):
+    _check(_lib.bsm_state_unpack(C.byref(heads), int(rows), o_acc, out, stream))
 
 
 def bsm_dplan_free(dplan):

@@ -863,6 +863,15 @@ int bsm_fwd_merge_fp32(const bsm_heads* heads, int64_t rows, float* o_run, float
                     "fp32 merge launch", st);
 }
 
+int bsm_state_unpack(const bsm_heads* heads, int64_t rows, const float* o_acc, float* out, void* stream) {
+  int rc = check_heads(heads);
+  if (rc) return rc;
+  if (rows < 1) { set_error("rows must be >= 1"); return BSM_E_INVALID; }
+  if (!o_acc || !out) { set_error("null tensor pointer"); return BSM_E_INVALID; }
+  hipStream_t st = (hipStream_t)stream;
+  return hip_status(launch_state_unpack(rows, heads->hq, o_acc, out, st), "state unpack launch", st);
+}
+
 int bsm_bwd_prep(const bsm_heads* heads, int64_t rows, const void* o, const void* dout,
                  float* delta, void* stream) {
   int rc = check_heads(heads);

@@ -320,7 +320,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a) {
   f32x16 acc[4];
   float mref = kNegInf, lrun = 0.f;
   const int64_t sidx = (int64_t)h * a.rows + qrow;
-  float* op = a.oacc + (qrow * a.hq + h) * kHeadDim;
+  // this lane's part of the item's tile-blocked state (state_index): float4
+  // number 4 db + i at op + 256 (4 db + i)
+  float* op = a.oacc + ((int64_t)it.x * a.hq + h) * (kTile * kHeadDim) + wave * (32 * kHeadDim) + lane * 4;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -332,7 +334,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a) {
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float4 v4 = *(const float4*)(op + db * 32 + i * 8 + hi * 4);
+        const float4 v4 = *(const float4*)(op + (db * 4 + i) * 256);
         acc[db][4 * i + 0] = v4.x;
         acc[db][4 * i + 1] = v4.y;
         acc[db][4 * i + 2] = v4.z;
@@ -452,7 +454,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a) {
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        *(float4*)(op + db * 32 + i * 8 + hi * 4) =
+        *(float4*)(op + (db * 4 + i) * 256) =
             make_float4(acc[db][4 * i], acc[db][4 * i + 1], acc[db][4 * i + 2], acc[db][4 * i + 3]);
     if (hi == 0) {
       a.m[sidx] = mref;
@@ -528,7 +530,11 @@ __global__ __launch_bounds__(256) void merge_fp32_kernel(int64_t pairs, int64_t 
     const float lr = lse_run[li];
     float wr, ws, lnew;
     merge_weights(lr, ls, wr, ws, lnew);
-    const float* ap = acc_s + gid * 8;
+    // channels d0 .. d0 + 7 of the tile-blocked partial: two float4 runs
+    const int32_t d0 = (int32_t)(gid & 15) * 8;
+    const float4 a0 = *(const float4*)(acc_s + state_index(row, h, d0, hq));
+    const float4 a1 = *(const float4*)(acc_s + state_index(row, h, d0 + 4, hq));
+    const float ap[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
 #pragma unroll
     for (int i = 0; i < 8; ++i) orp[i] = (lr == kNegInf ? 0.f : wr * orp[i]) + ws * (ap[i] / l);
     if ((gid & 15) == 0) lse_run[li] = lnew;
@@ -539,6 +545,16 @@ __global__ __launch_bounds__(256) void merge_fp32_kernel(int64_t pairs, int64_t 
     for (int i = 0; i < 8; ++i) r8[i] = (__bf16)orp[i];
     *(uint4*)(o_bf16 + gid * 8) = __builtin_bit_cast(uint4, r8);
   }
+}
+
+__global__ __launch_bounds__(256) void state_unpack_kernel(int64_t quads, int32_t hq, const float* o_acc,
+                                                           float* out) {
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (g >= quads) return;
+  const int64_t e = g * 4;
+  const int64_t row = e / ((int64_t)hq * kHeadDim);
+  const int32_t h = (int32_t)((e / kHeadDim) % hq), d = (int32_t)(e % kHeadDim);
+  *(float4*)(out + e) = *(const float4*)(o_acc + state_index(row, h, d, hq));
 }
 
 __global__ __launch_bounds__(256) void bwd_prep_kernel(int64_t pairs, int64_t rows, int32_t hq,
@@ -593,6 +609,13 @@ hipError_t launch_merge_fp32(int64_t rows, int32_t hq, float* o_run, float* lse_
   const int64_t blocks = (pairs * 16 + 255) / 256;
   hipLaunchKernelGGL(merge_fp32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, pairs, rows, hq, o_run,
                      lse_run, acc_s, m_s, l_s, (unsigned short*)o_bf16);
+  return hipGetLastError();
+}
+
+hipError_t launch_state_unpack(int64_t rows, int32_t hq, const float* o_acc, float* out, hipStream_t stream) {
+  const int64_t quads = rows * hq * (kHeadDim / 4);
+  const int64_t blocks = (quads + 255) / 256;
+  hipLaunchKernelGGL(state_unpack_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, quads, hq, o_acc, out);
   return hipGetLastError();
 }
 

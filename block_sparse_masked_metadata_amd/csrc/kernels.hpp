@@ -37,6 +37,20 @@ enum : int32_t { kRelFull = 0, kRelCausal = 1, kRelReverse = 2, kRelPastWindow =
 // Key interval of a token (int2): the queries it is legal for are exactly
 // those with x <= pos < y; y < x when it has none (the planner's key_interval).
 
+// The carried forward state O_acc is tile-blocked (each workgroup's state is
+// one contiguous 64 KiB run that its lanes read and write fully coalesced):
+// query tile t = row / 128 and head h own 128 x 128 floats at
+// (t * Hq + h) * 16384; inside, wave w = (row % 128) / 32 owns 4096 floats,
+// and the lane of query row 32w + l (l < 32) for channel d = 32 db + 8 i +
+// 4 hi + c keeps it at float (64 (4 db + i) + l + 32 hi) * 4 + c.  A buffer
+// holds ceil(S / 128) * 128 * Hq * 128 floats.
+__host__ __device__ inline int64_t state_index(int64_t row, int32_t h, int32_t d, int32_t hq) {
+  const int64_t t = row >> 7;
+  const int r = (int)(row & 127), w = r >> 5, l = r & 31;
+  const int db = d >> 5, i = (d >> 3) & 3, hi = (d >> 2) & 1, c = d & 3;
+  return (t * hq + h) * (int64_t)(kTile * kHeadDim) + w * 32 * kHeadDim + (((db * 4 + i) * 64 + l + 32 * hi) << 2) + c;
+}
+
 // Per-token tracks in plan order (int4): sample, seg, noise, pos.
 // bf16 tensors are passed as raw 16-bit patterns (uint16_t).
 
@@ -54,7 +68,7 @@ struct FwdArgs {
   const int4* ktracks;      // tracks of the key buffer rows
   const int2* kint;         // key intervals of the key buffer rows
   int64_t rows;             // S: query shard rows (state stride / ragged bound)
-  float* oacc;              // [S, Hq, d] fp32
+  float* oacc;              // tile-blocked fp32 (state_index)
   float* m;                 // [Hq, S]
   float* l;                 // [Hq, S]
   uint16_t* o;        // [S, Hq, d]
@@ -97,6 +111,8 @@ hipError_t launch_merge_bf16(int64_t rows, int32_t hq, uint16_t* o_run, float* l
                              const float* lse_s, hipStream_t stream);
 hipError_t launch_merge_fp32(int64_t rows, int32_t hq, float* o_run, float* lse_run, const float* acc_s,
                              const float* m_s, const float* l_s, uint16_t* o_bf16, hipStream_t stream);
+// O_acc (tile-blocked) -> fp32 [rows, Hq, d].
+hipError_t launch_state_unpack(int64_t rows, int32_t hq, const float* o_acc, float* out, hipStream_t stream);
 hipError_t launch_bwd_prep(int64_t rows, int32_t hq, const uint16_t* o,
                            const uint16_t* dout, float* delta, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);

@@ -115,11 +115,23 @@ def heads(hq, hkv, d=128, scale=None):
 
 
 def new_state(rows, hq, d, device="cuda"):
-    """Uninitialized fp32 state (O_acc, m, l): the first step initializes it in-kernel."""
+    """Uninitialized fp32 state (O_acc, m, l): the first step initializes it in-kernel.
+    O_acc is the kernels' tile-blocked buffer (flat, ceil(rows/128)*128*hq*d
+    floats); state_rows reads it out in row order."""
     import torch
-    return (torch.empty(rows, hq, d, dtype=torch.float32, device=device),
+    padded = (rows + 127) // 128 * 128
+    return (torch.empty(padded * hq * d, dtype=torch.float32, device=device),
             torch.empty(hq, rows, dtype=torch.float32, device=device),
             torch.empty(hq, rows, dtype=torch.float32, device=device))
+
+
+def state_rows(hd, o_acc, rows):
+    """The tile-blocked O_acc as fp32 [rows, Hq, d]."""
+    import torch
+    _need(o_acc, torch.float32, ((rows + 127) // 128 * 128 * hd.hq * hd.d,), "o_acc")
+    out = torch.empty(rows, hd.hq, hd.d, dtype=torch.float32, device=o_acc.device)
+    C.bsm_state_unpack(hd, rows, _ptr(o_acc), _ptr(out), _stream())
+    return out
 
 
 def fwd_step(dp: DevicePlan, s, hd, q, k, v, state, o, lse, keep_state=False):

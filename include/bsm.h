@@ -20,7 +20,9 @@
  *   - Tensor layouts (all contiguous, 16-byte aligned device memory):
  *       Q, O, dO          bf16  [rows, Hq, d]     token-major
  *       K, V              bf16  [keys, Hkv, d]
- *       O_acc, dQ         fp32  [rows, Hq, d]
+ *       dQ                fp32  [rows, Hq, d]
+ *       O_acc             fp32  tile-blocked, ceil(rows / 128) * 128 * Hq * d
+ *                               floats (bsm_state_unpack reads it out)
  *       dK, dV            fp32  [keys, Hkv, d]
  *       m, l, LSE, delta  fp32  [Hq, rows]        head-major
  *     d must be 128.  Query head h reads key/value head h / (Hq / Hkv).
@@ -326,7 +328,11 @@ typedef struct {
  * shard j = (r - s) mod R into the fp32 running state.
  *   q      bf16 [S, Hq, d]   the rank's query shard in plan order
  *   k, v   bf16 [S, Hkv, d]  shard j in plan order
- *   o_acc  fp32 [S, Hq, d]   unnormalized accumulator   (carried state)
+ *   o_acc  fp32, ceil(S / 128) * 128 * Hq * d floats: the unnormalized
+ *                            accumulator (carried state) in the kernel's
+ *                            tile-blocked order, each (query tile, head)
+ *                            one contiguous 64 KiB run; bsm_state_unpack
+ *                            converts it to [S, Hq, d]
  *   m      fp32 [Hq, S]      reference of the row in base-2 units
  *                            (scale*log2(e)*q.k): the row max at the last
  *                            rescale, -inf before the first legal key; o_acc
@@ -387,8 +393,9 @@ int bsm_fwd_fetched(const bsm_dplan* dplan, const bsm_heads* heads, const void* 
  * bsm_fwd_merge_bf16: o_run, o_s bf16 [rows, Hq, d]; lse_run, lse_s fp32
  *   [Hq, rows] (natural log); the merged O is rounded to bf16 every step.
  * bsm_fwd_merge_fp32: o_run fp32 [rows, Hq, d] normalized; the step is given
- *   as its unnormalized fp32 (acc_s, m_s, l_s) from BSM_FWD_STEP_ONLY |
- *   BSM_FWD_KEEP_STATE; o_bf16 (may be NULL) receives RNE bf16 of the merged O.
+ *   as its unnormalized fp32 (acc_s tile-blocked as o_acc, m_s, l_s) from
+ *   BSM_FWD_STEP_ONLY | BSM_FWD_KEEP_STATE; o_bf16 (may be NULL) receives RNE
+ *   bf16 of the merged O.
  * Rows the step did not reach must read lse_s = -inf (bf16) or l_s = 0
  * (fp32): the caller fills them before the step; they keep the running values.
  * Start from lse_run = -inf (o_run is then ignored).  Stream-ordered on
@@ -399,6 +406,14 @@ int bsm_fwd_merge_bf16(const bsm_heads* heads, int64_t rows, void* o_run, float*
 int bsm_fwd_merge_fp32(const bsm_heads* heads, int64_t rows, float* o_run, float* lse_run,
                        const float* acc_s, const float* m_s, const float* l_s, void* o_bf16,
                        void* stream);
+
+/*
+ * The carried accumulator of bsm_fwd_step / bsm_fwd_single in row order:
+ * out fp32 [rows, Hq, d] from o_acc (tile-blocked, ceil(rows / 128) * 128 *
+ * Hq * d floats).  Stream-ordered on `stream`; rows >= 1.
+ */
+int bsm_state_unpack(const bsm_heads* heads, int64_t rows, const float* o_acc, float* out,
+                     void* stream);
 
 /* ====================================================================== *
  *  Backward.                                                              *

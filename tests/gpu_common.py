@@ -80,7 +80,7 @@ def check_rows(case, o, lse, sel=None, tol_o=O_TOL, tol_lse=LSE_TOL, single=Fals
                                        case.rows[sel], 1.0 / np.sqrt(case.lay.d))
     tsel = torch.from_numpy(sel).cuda()
     acc, m, l = case.single(keep_state=True) if single else case.ring(keep_state=True)[2]
-    acc = acc[tsel].cpu()
+    acc = bsm.state_rows(case.heads, acc, case.S)[tsel].cpu()
     l = l[:, tsel].cpu().T[:, :, None]
     o32 = torch.where(l > 0, acc / torch.where(l > 0, l, torch.ones_like(l)), torch.zeros_like(acc))
     og = o[tsel].cpu()

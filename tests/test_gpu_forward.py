@@ -199,3 +199,24 @@ def test_fwd_errors_before_launch():
             fn()
         assert e.value.code == C.BSM_E_UNSUPPORTED
         assert "4 GiB" in str(e.value)
+
+
+def test_state_unpack_channel_order():
+    """V[k, kvh, c] = c makes every reached row's O_acc / l a weighted mean
+    of c with weights bf16(p) / sum p, i.e. c within 2^-9 relative (P is
+    rounded to bf16 for the product, l sums the fp32 p).  Channels differ by
+    at least 1, so this pins the channel order of the tile-blocked state read
+    back through bsm_state_unpack (rows and heads are pinned by the oracle
+    comparisons above)."""
+    lay = packed_text()
+    base = Case(lay)
+    v = torch.arange(128, dtype=torch.float32, device="cuda").to(torch.bfloat16)
+    v = v.expand_as(base.full[2]).contiguous()
+    case = Case(lay, tensors=(base.full[0], base.full[1], v))
+    _, _, (acc, m, l) = case.ring(keep_state=True)
+    rows = bsm.state_rows(case.heads, acc, case.S)
+    torch.cuda.synchronize()
+    lt = l.T[:, :, None]
+    assert bool((lt > 0).all())
+    want = torch.arange(128, dtype=torch.float32, device="cuda").expand_as(rows)
+    assert bool((((rows / lt) - want).abs() <= want * 2.0 ** -8 + 1e-3).all())

@@ -73,7 +73,8 @@ def parse():
 HERE = os.path.dirname(os.path.abspath(__file__))
 FWD_SOURCES = ["block_sparse_masked_metadata_amd/csrc/fwd.hip",
                "block_sparse_masked_metadata_amd/csrc/kernels.hpp",
-               "block_sparse_masked_metadata_amd/csrc/tile_common.hpp"]
+               "block_sparse_masked_metadata_amd/csrc/tile_common.hpp",
+               "block_sparse_masked_metadata_amd/csrc/capi.hip"]  # the packer sets the item order
 TRAFFIC_PROFILE = "profiles/fwd_kernel_hbm_packed_multimodal_64k.md"
 
 

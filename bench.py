@@ -57,8 +57,7 @@ def parse():
     ap.add_argument("--tau", type=float, default=0.0,
                     help="chunk search: cost of one extra key range per rank and step, in pairs")
     ap.add_argument("--dense", action="store_true",
-                    help="dense-call mode: every ring step as full / causal / reverse calls "
-                         "(forward only)")
+                    help="dense-call mode: every ring step as full / causal / reverse calls")
     ap.add_argument("--ring-estimate", action="store_true",
                     help="also time every rank's forward steps and report the ring's critical "
                          "path (sum over steps of the slowest rank), untimed by the headline")
@@ -319,7 +318,7 @@ def main():
     dks = [torch.zeros(S, lay.hkv, d, dtype=torch.float32, device="cuda") for _ in range(R)]
     dvs = [torch.zeros(S, lay.hkv, d, dtype=torch.float32, device="cuda") for _ in range(R)]
     fwd_steps = [s for s in range(R) if dp.info["fwd_items"][s] > 0]
-    do_bwd = not args.fwd_only and args.merge == "carry" and not args.fetch and not args.dense
+    do_bwd = not args.fwd_only and args.merge == "carry" and not args.fetch
     if args.dense and args.fetch:
         print(json.dumps({"error": "--dense and --fetch exclude each other"}))
         sys.exit(2)

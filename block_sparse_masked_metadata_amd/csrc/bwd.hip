@@ -69,6 +69,9 @@ __device__ inline void two_products(f32x16& s, f32x16& dp, const char* ta, const
   }
 }
 
+// kDense: dense-call lists (entries carry a relation and query rows; the
+// staged key data is the key's position, 2^31 - 1 past the valid rows).
+template <bool kDense>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char sK[kSub * 256];
   __shared__ __attribute__((aligned(1024))) char sV[kSub * 256];
@@ -101,7 +104,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
     int len;
     bool part;
     sub_bounds(ent, 0, r0, len, part);
-    if (part && tid < len) kt_pf = key_mask_data(a.ktracks, a.kint, r0 + tid, (ent.y & kIntervalBit) != 0);
+    if (kDense) kt_pf.x = INT32_MAX;
+    if (part && tid < len) {
+      if (kDense)
+        kt_pf.x = a.ktracks[r0 + tid].w;
+      else
+        kt_pf = key_mask_data(a.ktracks, a.kint, r0 + tid, (ent.y & kIntervalBit) != 0);
+    }
     pf.fetch(kbase, vbase, r0, len, row_bytes, tid);
   }
   bf16x8 qf[8], df[8];
@@ -136,6 +145,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
     bool partial;
     sub_bounds(ent, n, r0, len, partial);
     const bool interval = (ent.y & kIntervalBit) != 0;
+    const int32_t ey = ent.y;
     __syncthreads();  // sub-tile n is in LDS
     const bool more = n + 1 < nsub;
     if (more) {
@@ -144,8 +154,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
       int nlen;
       bool npart;
       sub_bounds(ent, n + 1, nr0, nlen, npart);
-      kt_pf = make_int4(-1, -1, -1, 0);  // keys past len: sample -1, empty range
-      if (npart && tid < nlen) kt_pf = key_mask_data(a.ktracks, a.kint, nr0 + tid, (ent.y & kIntervalBit) != 0);
+      kt_pf = make_int4(kDense ? INT32_MAX : -1, -1, -1, 0);  // keys past len: sample -1, empty range
+      if (npart && tid < nlen) {
+        if (kDense)
+          kt_pf.x = a.ktracks[nr0 + tid].w;
+        else
+          kt_pf = key_mask_data(a.ktracks, a.kint, nr0 + tid, (ent.y & kIntervalBit) != 0);
+      }
       pf.fetch(kbase, vbase, nr0, nlen, row_bytes, tid);
     }
 #pragma unroll
@@ -153,7 +168,18 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
       f32x16 s, dp;
       two_products(s, dp, sK, sV, kc * 32 + l32, qf, df, hi);
       // s[r] = S[query l32][key 32kc + 8(r/4) + 4hi + r%4]
-      if (partial && interval) {
+      if (kDense) {
+        if (partial) {
+          int32_t dlo;
+          uint32_t dspan;
+          dense_range(ey, wave * 32 + l32, qt.w, a.window, dlo, dspan);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kc * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+            s[r] = (uint32_t)(sKT[key].x - dlo) < dspan ? s[r] : kNegInf;
+          }
+        }
+      } else if (partial && interval) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kc * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
@@ -212,6 +238,9 @@ struct RowStage {
   int4 t;
 };
 
+// kDense: dense-call column lists (entries carry a relation and the key rows
+// of the tile they apply to).
+template <bool kDense>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
   // two buffer sets: sub-tile m computes from set m % 2 while m + 1 is staged
   // into the other, one barrier per sub-tile
@@ -244,10 +273,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
   int2 ent;
   bool cur_partial = false, nxt_partial = false;
   int cur_len = 0, nxt_len = 0;
+  int32_t cur_ey = 0, nxt_ey = 0;  // entry words (dense-call relation and key rows)
   auto fetch = [&](int m, int2 e2) {
     const int32_t h = g * grp + m / nsub;
     int64_t r0;
     sub_bounds(e2, m % nsub, r0, nxt_len, nxt_partial);
+    nxt_ey = e2.y;
     rs.v = 0.f;
     rs.t = make_int4(-2, -1, -1, -1);  // rows past len: no sample, no position
     if (tid < kSub) {
@@ -295,6 +326,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
   stage(0);
   cur_len = nxt_len;
   cur_partial = nxt_partial;
+  cur_ey = nxt_ey;
   __builtin_amdgcn_s_waitcnt(0);  // no load is pending when the loop starts
   const TrLane tr(lane);
 
@@ -303,8 +335,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
   // (lane: key; register r: query q0 + 8(r/4) + 4hi + r%4).  On partial
   // sub-tiles illegal pairs get P = 0; rows past len carry sample -2.
   auto p_and_ds = [&](f32x16& s, f32x16& dp, bf16x8 (&pb)[2], bf16x8 (&dsb)[2], int q0, bool partial,
-                      const float* sL, const float* sD, const int4* sQT) {
-    if (partial && kin) {
+                      const float* sL, const float* sD, const int4* sQT, int32_t ey) {
+    if (kDense) {
+      if (partial) {
+        int32_t dlo;
+        uint32_t dspan;
+        dense_key_range(ey, wave * 32 + l32, kt.w, a.window, dlo, dspan);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qi = q0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+          s[r] = (uint32_t)(sQT[qi].w - dlo) < dspan ? s[r] : kNegInf;
+        }
+      }
+    } else if (partial && kin) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int qi = q0 + 8 * (r >> 2) + 4 * hi + (r & 3);
@@ -353,6 +396,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
 
   for (int m = 0; m < total; ++m) {
     const bool partial = cur_partial;
+    const int32_t ey = cur_ey;
     const int cb = m & 1;
     __syncthreads();  // sub-tile m is in LDS; every wave is done with m - 1
     const bool more = m + 1 < total;
@@ -368,14 +412,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
     bf16x8 pb0[2], ds0[2], pb1[2], ds1[2];
     two_products(s0, dp0, sQ[cb], sO[cb], l32, kf, vf, hi);
     two_products(s1, dp1, sQ[cb], sO[cb], 32 + l32, kf, vf, hi);
-    p_and_ds(s0, dp0, pb0, ds0, 0, partial, sL[cb], sD[cb], sQT[cb]);
+    p_and_ds(s0, dp0, pb0, ds0, 0, partial, sL[cb], sD[cb], sQT[cb], ey);
     accumulate(pb0, ds0, 0, sQ[cb], sO[cb]);
-    p_and_ds(s1, dp1, pb1, ds1, 32, partial, sL[cb], sD[cb], sQT[cb]);
+    p_and_ds(s1, dp1, pb1, ds1, 32, partial, sL[cb], sD[cb], sQT[cb], ey);
     accumulate(pb1, ds1, 32, sQ[cb], sO[cb]);
     if (more) {
       stage(cb ^ 1);  // the other set was last read in iteration m - 1
       cur_len = nxt_len;
       cur_partial = nxt_partial;
+      cur_ey = nxt_ey;
     }
   }
 
@@ -406,14 +451,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
   const int64_t blocks = (int64_t)a.nitems * a.hq;
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  if (a.dense)
+    hipLaunchKernelGGL(bwd_dq_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(bwd_dq_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
   const int64_t blocks = (int64_t)a.nitems * a.hkv;
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  if (a.dense)
+    hipLaunchKernelGGL(bwd_dkdv_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(bwd_dkdv_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -298,7 +298,7 @@ struct DenseEnt {
 
 // Dense-call lists of rank r (MARBLE section 03, "Chunked ring attention"):
 // each call of a step becomes, per query tile it meets, one list entry per
-// 128-key piece of its key run, carrying the call's relation and the tile rows
+// key tile its key run meets, carrying the call's relation and the tile rows
 // it applies to; pieces no pair of which satisfies the relation are dropped,
 // pieces every pair of which does become full.  Entries of one tile with the
 // same rows and keys whose relations leave no pair out merge into one full
@@ -327,11 +327,15 @@ static int pack_calls(const Plan& p, int32_t r, Packed& pk) {
     if (rc) return rc;
     for (auto& v : per_tile) v.clear();
     for (const Call& c : calls) {
-      // bounds of the call's key pieces
-      std::vector<std::pair<int64_t, int64_t>> kb;
-      for (int32_t k = c.k0; k < c.k0 + c.kn; k += kTile) {
+      // the call's key pieces: its key run cut at key-tile edges, so each
+      // piece is one column entry of one key tile in the dK/dV lists
+      std::vector<std::pair<int32_t, int32_t>> kp;  // [first row, end)
+      std::vector<std::pair<int64_t, int64_t>> kb;  // position bounds
+      for (int32_t b = c.k0 / kTile; b <= (c.k0 + c.kn - 1) / kTile; ++b) {
+        const int32_t k = std::max(c.k0, b * kTile), ke = std::min(c.k0 + c.kn, (b + 1) * kTile);
         int64_t mn, mx;
-        row_bounds(p, kbase, k, std::min<int64_t>(k + kTile, c.k0 + c.kn), mn, mx);
+        row_bounds(p, kbase, k, ke, mn, mx);
+        kp.push_back({k, ke});
         kb.push_back({mn, mx});
       }
       for (int32_t a = c.q0 / kTile; a <= (c.q0 + c.qn - 1) / kTile; ++a) {
@@ -339,10 +343,9 @@ static int pack_calls(const Plan& p, int32_t r, Packed& pk) {
         int64_t qmn, qmx;
         row_bounds(p, qbase, ra, rb, qmn, qmx);
         for (size_t i = 0; i < kb.size(); ++i) {
-          const int32_t k = c.k0 + (int32_t)i * kTile;
           const int cls = relation_bounds(c.kind, qmn, qmx, kb[i].first, kb[i].second, p.window);
           if (cls == 0) continue;
-          per_tile[a].push_back({k, std::min(kTile, c.k0 + c.kn - k), ra - a * kTile, rb - a * kTile,
+          per_tile[a].push_back({kp[i].first, kp[i].second - kp[i].first, ra - a * kTile, rb - a * kTile,
                                  cls == 2 ? (int32_t)kCallFull : c.kind, qmn, qmx, kb[i].first, kb[i].second});
         }
       }
@@ -400,6 +403,32 @@ static int pack_calls(const Plan& p, int32_t r, Packed& pk) {
       pk.entries.insert(pk.entries.end(), lists[s][a].begin(), lists[s][a].end());
     }
     order_items(st.fitems, qsample);
+    // dK/dV column lists: every row entry, cut at key-tile edges, becomes an
+    // entry of each key tile it meets (x = first query row, the key rows of
+    // the tile it applies to in the row bits), ascending query row.  Query
+    // rows past a column entry's length carry P = 0 (LSE = -inf), so only key
+    // coverage and the relation decide whether it is masked.
+    std::vector<std::vector<int2>> cols(T);
+    for (int32_t a = 0; a < T; ++a)
+      for (const int2& e : lists[s][a]) {
+        const int32_t kl = e.y & kLenMask, rlo = (e.y >> kRowLoShift) & 127, rhi = ((e.y >> kRowHiShift) & 127) + 1;
+        const int32_t kind = (e.y >> kKindShift) & 3;
+        for (int32_t b = e.x / kTile; b <= (e.x + kl - 1) / kTile; ++b) {
+          const int32_t klo = std::max(e.x, b * kTile) - b * kTile, khi = std::min(e.x + kl, (b + 1) * kTile) - b * kTile;
+          const bool whole = klo == 0 && khi == (int32_t)std::min<int64_t>(kTile, S - (int64_t)b * kTile);
+          const bool part = !(kind == kCallFull && whole);
+          cols[b].push_back(make_int2(a * kTile + rlo, (rhi - rlo) | (klo << kRowLoShift) | ((khi - 1) << kRowHiShift) |
+                                                           (kind << kKindShift) | (part ? kPartialBit : 0)));
+        }
+      }
+    for (int32_t b = 0; b < T; ++b) {
+      if (cols[b].empty()) continue;
+      std::stable_sort(cols[b].begin(), cols[b].end(), [](const int2& x, const int2& y) { return x.x < y.x; });
+      st.bitems.push_back(make_int4(b, 0, (int32_t)pk.entries.size(), (int32_t)cols[b].size()));
+      pk.entries.insert(pk.entries.end(), cols[b].begin(), cols[b].end());
+    }
+    std::stable_sort(st.bitems.begin(), st.bitems.end(),
+                     [](const int4& x, const int4& y) { return x.w != y.w ? x.w > y.w : x.x < y.x; });
   }
   pk.sitems.clear();
   for (int32_t a = 0; a < T; ++a) {
@@ -920,10 +949,6 @@ int bsm_bwd_step(const bsm_dplan* d, int32_t s, const bsm_heads* heads, const vo
   int rc = check_heads(heads);
   if (rc) return rc;
   if (s < 0 || s >= d->R) { set_error("step out of range"); return BSM_E_INVALID; }
-  if (d->dense) {
-    set_error("a dense-call device plan has no backward lists");
-    return BSM_E_UNSUPPORTED;
-  }
   if (!q || !k || !v || !dout || !lse || !delta || !dq_acc || !dk || !dv) {
     set_error("null tensor pointer");
     return BSM_E_INVALID;
@@ -944,6 +969,7 @@ int bsm_bwd_step(const bsm_dplan* d, int32_t s, const bsm_heads* heads, const vo
   a.qtracks = d->tracks + (int64_t)d->r * d->S;
   a.ktracks = d->tracks + (int64_t)j * d->S;
   a.kint = d->kint + (int64_t)j * d->S;
+  a.dense = d->dense;
   a.rows = d->S;
   a.krows = d->S;
   a.dq = dq_acc;

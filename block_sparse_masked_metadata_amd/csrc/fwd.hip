@@ -166,18 +166,6 @@ __device__ inline void sub_bounds(const int2 ent, int n, int32_t& k0, int& len, 
   interval = (ent.y & kIntervalBit) != 0;
 }
 
-// Key positions legal for query row `row` of its tile (position pq) under a
-// dense-call entry: [lo, lo + span), span 0 for rows outside the entry.
-__device__ inline void dense_range(int32_t y, int row, int32_t pq, int32_t window, int32_t& lo, uint32_t& span) {
-  const int kind = (y >> kKindShift) & 3;
-  const int rlo = (y >> kRowLoShift) & 127, rhi = ((y >> kRowHiShift) & 127) + 1;
-  // pq >= 0 and 1 <= window <= 2^31 - 1: no overflow below
-  const int32_t below = pq - window + 1;
-  lo = kind == kRelCausal ? below : kind == kRelReverse ? pq + 1 : INT32_MIN;
-  const int32_t hi = kind == kRelCausal ? pq + 1 : kind == kRelPastWindow ? below : INT32_MAX;
-  span = (uint32_t)(row - rlo) < (uint32_t)(rhi - rlo) ? (uint32_t)hi - (uint32_t)lo : 0u;
-}
-
 // S^T = K Q^T for one 64-key sub-tile: s[kb][r] = S[query l32][key 32kb + 8(r/4) + 4hi + r%4],
 // operand reads issued 4 at a time ahead of their MFMAs; on partial sub-tiles
 // illegal pairs (and keys past len) become -inf.

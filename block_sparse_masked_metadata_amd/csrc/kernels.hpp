@@ -33,6 +33,33 @@ constexpr int32_t kLenMask = 0xff;  // valid rows: at most 128
 // and masks keys past the valid rows.
 constexpr int kRowLoShift = 8, kRowHiShift = 24, kKindShift = 19;
 enum : int32_t { kRelFull = 0, kRelCausal = 1, kRelReverse = 2, kRelPastWindow = 3 };
+// Column entries of a dense-call plan (dK/dV lists) mirror this: x = first
+// query row, the rows [lo, hi] bits name the KEY rows of the key tile the
+// entry applies to.
+
+// Dense-call masks as one range per lane (branch-free: a branch on the
+// relation splits the kernels' loops and costs registers).  Positions lie in
+// [0, 2^31 - 1) and 1 <= window <= 2^31 - 1, so nothing below overflows.
+// Query lane (forward, dQ): the key positions legal for query row `row` of
+// its tile at position pq under entry word y are [lo, lo + span).
+__device__ inline void dense_range(int32_t y, int row, int32_t pq, int32_t window, int32_t& lo, uint32_t& span) {
+  const int kind = (y >> kKindShift) & 3;
+  const int rlo = (y >> kRowLoShift) & 127, rhi = ((y >> kRowHiShift) & 127) + 1;
+  const int32_t below = pq - window + 1;
+  lo = kind == kRelCausal ? below : kind == kRelReverse ? pq + 1 : INT32_MIN;
+  const int32_t hi = kind == kRelCausal ? pq + 1 : kind == kRelPastWindow ? below : INT32_MAX;
+  span = (uint32_t)(row - rlo) < (uint32_t)(rhi - rlo) ? (uint32_t)hi - (uint32_t)lo : 0u;
+}
+// Key lane (dK/dV): the query positions legal for key row `row` of its tile
+// at position pk under column entry word y are [lo, lo + span).
+__device__ inline void dense_key_range(int32_t y, int row, int32_t pk, int32_t window, int32_t& lo, uint32_t& span) {
+  const int kind = (y >> kKindShift) & 3;
+  const int rlo = (y >> kRowLoShift) & 127, rhi = ((y >> kRowHiShift) & 127) + 1;
+  const int32_t ahead = window > INT32_MAX - pk ? INT32_MAX : pk + window;  // pk + W, saturated
+  lo = kind == kRelCausal ? pk : kind == kRelPastWindow ? ahead : INT32_MIN;
+  const int32_t hi = kind == kRelCausal ? ahead : kind == kRelReverse ? pk : INT32_MAX;
+  span = (uint32_t)(row - rlo) < (uint32_t)(rhi - rlo) ? (uint32_t)hi - (uint32_t)lo : 0u;
+}
 
 // Key interval of a token (int2): the queries it is legal for are exactly
 // those with x <= pos < y; y < x when it has none (the planner's key_interval).
@@ -95,6 +122,7 @@ struct BwdArgs {
   const int4* qtracks;
   const int4* ktracks;
   const int2* kint;           // key intervals of the key buffer rows
+  int32_t dense;              // the lists hold dense-call entries
   int64_t rows;               // S (query rows)
   int64_t krows;              // key rows of the k/v buffers
   float* dq;                  // [S, Hq, d]

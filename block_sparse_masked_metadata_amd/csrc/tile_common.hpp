@@ -136,7 +136,7 @@ struct PairStage {
 // the partner tile, valid rows | partial bit << 16).
 __device__ inline void sub_bounds(const int2 ent, int n, int64_t& r0, int& len, bool& partial) {
   const int half = n & 1;
-  const int tlen = ent.y & 0xffff;
+  const int tlen = ent.y & kLenMask;
   r0 = (int64_t)ent.x + half * kSub;
   len = tlen - half * kSub;
   len = len < 0 ? 0 : (len > kSub ? kSub : len);

@@ -284,10 +284,12 @@ void bsm_dplan_free(bsm_dplan* dplan);
  * attention"): its forward lists run the calls of bsm_plan_dense_calls, each
  * as 128-key pieces of its key run for every query tile it meets, tested by
  * row range and one position compare (pieces every pair of which satisfies the
- * relation run unmasked).  Same memory rules as bsm_dplan_bytes /
- * bsm_dplan_upload.  bsm_fwd_step and bsm_fwd_single accept the handle with the
- * same arguments and results; bsm_fwd_fetched and bsm_bwd_step refuse it with
- * BSM_E_UNSUPPORTED.  Needs every position below 2^31 - 1 (BSM_E_UNSUPPORTED).
+ * relation run unmasked).  Its backward lists hold the same pieces per key
+ * tile (cut at key-tile edges), tested by key range and one compare.  Same
+ * memory rules as bsm_dplan_bytes / bsm_dplan_upload.  bsm_fwd_step,
+ * bsm_fwd_single and bsm_bwd_step accept the handle with the same arguments
+ * and results; bsm_fwd_fetched refuses it with BSM_E_UNSUPPORTED.  Needs
+ * every position below 2^31 - 1 (BSM_E_UNSUPPORTED).
  */
 int bsm_dplan_calls_bytes(const bsm_plan* plan, int32_t r, int64_t* bytes);
 int bsm_dplan_calls_upload(const bsm_plan* plan, int32_t r, void* dev, int64_t bytes,

@@ -282,10 +282,10 @@ void bsm_dplan_free(bsm_dplan* dplan);
 /*
  * Dense-call device plan of rank r (MARBLE section 03, "Chunked ring
  * attention"): its forward lists run the calls of bsm_plan_dense_calls, each
- * as 128-key pieces of its key run for every query tile it meets, tested by
- * row range and one position compare (pieces every pair of which satisfies the
- * relation run unmasked).  Its backward lists hold the same pieces per key
- * tile (cut at key-tile edges), tested by key range and one compare.  Same
+ * as pieces of its key run cut at key-tile edges, for every query tile it
+ * meets, tested by row range and one position compare (pieces every pair of
+ * which satisfies the relation run unmasked).  Its backward lists hold the
+ * same pieces per key tile, tested by key range and one compare.  Same
  * memory rules as bsm_dplan_bytes / bsm_dplan_upload.  bsm_fwd_step,
  * bsm_fwd_single and bsm_bwd_step accept the handle with the same arguments
  * and results; bsm_fwd_fetched refuses it with BSM_E_UNSUPPORTED.  Needs

@@ -365,6 +365,7 @@ def main():
                 events[-1].record()
 
     delta = torch.empty(lay.hq, S, dtype=torch.float32, device="cuda")
+    bws = bsm.bwd_workspace(dp, hd)  # lets long dK/dV lists split over the GPU
 
     def backward():
         # One rank's backward: delta, then the R steps.  Shard j's dK/dV
@@ -377,7 +378,7 @@ def main():
         dvs[r].zero_()
         for s in range(R):
             j = (r - s) % R
-            bsm.bwd_step(dp, s, hd, q, ks[j], vs[j], dout, lse, delta, dq, dks[j], dvs[j])
+            bsm.bwd_step(dp, s, hd, q, ks[j], vs[j], dout, lse, delta, dq, dks[j], dvs[j], bws)
 
     for _ in range(args.warmup):
         forward()

@@ -46,7 +46,7 @@ EXPORTS = [
     "bsm_dplan_bytes", "bsm_dplan_upload", "bsm_dplan_free", "bsm_dplan_get_info",
     "bsm_fwd_step", "bsm_fwd_single", "bsm_fwd_merge_bf16", "bsm_fwd_merge_fp32",
     "bsm_bwd_prep", "bsm_bwd_step", "bsm_plan_dense_calls", "bsm_dplan_calls_bytes",
-    "bsm_dplan_calls_upload", "bsm_state_unpack",
+    "bsm_dplan_calls_upload", "bsm_state_unpack", "bsm_bwd_step_ws",
 ]
 
 
@@ -78,7 +78,8 @@ class bsm_dplan_info(C.Structure):
                 ("tiles_per_shard", C.c_int32), ("window", C.c_int32),
                 ("fwd_items", C.c_int64 * 64), ("bwd_items", C.c_int64 * 64),
                 ("step_pairs", C.c_int64 * 64), ("single_items", C.c_int64),
-                ("fetch_tiles", C.c_int64), ("fetch_rows", C.c_int64), ("dense_calls", C.c_int32)]
+                ("fetch_tiles", C.c_int64), ("fetch_rows", C.c_int64), ("dense_calls", C.c_int32),
+                ("bwd_workspace_slots", C.c_int32)]
 
 
 class bsm_call(C.Structure):
@@ -129,6 +130,8 @@ _sig = {
     "bsm_bwd_prep": (C.c_int, [C.POINTER(bsm_heads), C.c_int64, _P, _P, _P, _P]),
     "bsm_bwd_step": (C.c_int, [_P, C.c_int32, C.POINTER(bsm_heads), _P, _P, _P, _P, _P, _P,
                                _P, _P, _P, _P]),
+    "bsm_bwd_step_ws": (C.c_int, [_P, C.c_int32, C.POINTER(bsm_heads), _P, _P, _P, _P, _P, _P,
+                                  _P, _P, _P, _P, C.c_int64, _P]),
 }
 for _name, (_res, _args) in _sig.items():
     _fn = getattr(_lib, _name)
@@ -291,7 +294,7 @@ def bsm_dplan_get_info(dplan) -> dict:
             "fwd_items": list(info.fwd_items[:rk]), "bwd_items": list(info.bwd_items[:rk]),
             "step_pairs": list(info.step_pairs[:rk]), "single_items": info.single_items,
             "fetch_tiles": info.fetch_tiles, "fetch_rows": info.fetch_rows,
-            "dense_calls": bool(info.dense_calls)}
+            "dense_calls": bool(info.dense_calls), "bwd_workspace_slots": info.bwd_workspace_slots}
 
 
 def _heads(hq, hkv, d, scale):
@@ -323,3 +326,9 @@ def bsm_bwd_prep(heads, rows, o, dout, delta, stream):
 def bsm_bwd_step(dplan, s, heads, q, k, v, dout, lse, delta, dq_acc, dk, dv, stream):
     _check(_lib.bsm_bwd_step(dplan, int(s), C.byref(heads), q, k, v, dout, lse, delta,
                              dq_acc, dk, dv, stream))
+
+
+def bsm_bwd_step_ws(dplan, s, heads, q, k, v, dout, lse, delta, dq_acc, dk, dv, workspace,
+                    workspace_bytes, stream):
+    _check(_lib.bsm_bwd_step_ws(dplan, int(s), C.byref(heads), q, k, v, dout, lse, delta,
+                                dq_acc, dk, dv, workspace, int(workspace_bytes), stream))

@@ -251,17 +251,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
   __shared__ int4 sQT[2][kSub];
   __shared__ int2 sEnt[kListCache];
 
-  int32_t item, g;
-  map_block((int32_t)blockIdx.x, a.nitems, a.hkv, a.heads_per_xcd, item, g);
-  if (item < 0) return;
-  const int4 it = a.items[item];
+  int32_t unit, g;
+  map_block((int32_t)blockIdx.x, a.nitems, a.hkv, a.heads_per_xcd, unit, g);
+  if (unit < 0) return;
+  // the unit's sub-tiles [n0, n0 + nsub) of its item's column list, for every
+  // query head of the group (a split list cuts long lists into such ranges)
+  const int4 wk = a.work ? a.work[unit] : make_int4(unit, 0, -1, -1);
+  const int4 it = a.items[wk.x];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, hi = lane >> 5;
   const int64_t key = (int64_t)it.x * kTile + wave * 32 + l32;
   const bool kvalid = key < a.krows;
   const int32_t grp = a.hq / a.hkv;
   const uint32_t row_bytes = (uint32_t)a.hq * kHeadDim * 2u;
-  const int nsub = 2 * it.w;
+  const int n0 = wk.y;
+  const int nsub = (wk.z < 0 ? 2 * it.w : wk.z) - n0;
   const int total = grp * nsub;  // (query head of the group, sub-tile) pairs
 
   for (int i = tid; i < it.w && i < kListCache; i += 256) sEnt[i] = a.entries[it.z + i];
@@ -277,7 +281,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
   auto fetch = [&](int m, int2 e2) {
     const int32_t h = g * grp + m / nsub;
     int64_t r0;
-    sub_bounds(e2, m % nsub, r0, nxt_len, nxt_partial);
+    sub_bounds(e2, n0 + m % nsub, r0, nxt_len, nxt_partial);
     nxt_ey = e2.y;
     rs.v = 0.f;
     rs.t = make_int4(-2, -1, -1, -1);  // rows past len: no sample, no position
@@ -298,7 +302,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
     else if (tid < 3 * kSub) sQT[buf][tid - 2 * kSub] = rs.t;
   };
 
-  ent = a.entries[it.z];
+  ent = a.entries[it.z + (n0 >> 1)];
   fetch(0, ent);
   bf16x8 kf[8], vf[8];
   {
@@ -401,8 +405,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
     __syncthreads();  // sub-tile m is in LDS; every wave is done with m - 1
     const bool more = m + 1 < total;
     if (more) {
-      const int n1 = (m + 1) % nsub;
-      if ((n1 & 1) == 0) ent = list_entry(sEnt, list_base, a.entries, it, n1 >> 1, tid);
+      // next sub-tile n0 + (m + 1) % nsub: a new list entry at an even
+      // sub-tile, and at the start of the next head's range
+      const int r1 = (m + 1) % nsub, n1 = n0 + r1;
+      if ((n1 & 1) == 0 || r1 == 0) ent = list_entry(sEnt, list_base, a.entries, it, n1 >> 1, tid);
       fetch(m + 1, ent);
     }
     // The two 32-query halves qc are software-pipelined inside the wave: the
@@ -425,6 +431,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
   }
 
   if (!kvalid) return;
+  if (wk.w >= 0) {
+    // a split unit: its scaled partial goes to its workspace slot
+    float* wp = a.ws + ((int64_t)wk.w * a.hkv + g) * (2 * kTile * kHeadDim) + (wave * 32 + l32) * kHeadDim;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = db * 32 + i * 8 + hi * 4;
+        *(float4*)(wp + c) = make_float4(a.scale * dk[db][4 * i], a.scale * dk[db][4 * i + 1],
+                                         a.scale * dk[db][4 * i + 2], a.scale * dk[db][4 * i + 3]);
+        *(float4*)(wp + kTile * kHeadDim + c) =
+            make_float4(dv[db][4 * i], dv[db][4 * i + 1], dv[db][4 * i + 2], dv[db][4 * i + 3]);
+      }
+    return;
+  }
   const int64_t off = (key * a.hkv + g) * kHeadDim;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
@@ -446,7 +467,45 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
     }
 }
 
+// One workgroup per (reduce entry, kv head): dk/dv of the entry's key tile
+// += its workspace slots in slot order (deterministic), one float4 per
+// thread and step.
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(const BwdArgs a) {
+  const int32_t e = (int32_t)blockIdx.x / a.hkv, g = (int32_t)blockIdx.x % a.hkv;
+  const int4 rd = a.reduce[e];
+  for (int i = threadIdx.x; i < kTile * kHeadDim / 4; i += 256) {
+    const int row = i / (kHeadDim / 4), c = (i % (kHeadDim / 4)) * 4;
+    const int64_t key = (int64_t)rd.x * kTile + row;
+    if (key >= a.krows) continue;
+    const int64_t off = (key * a.hkv + g) * kHeadDim + c;
+    float4 k4 = *(const float4*)(a.dk + off);
+    float4 v4 = *(const float4*)(a.dv + off);
+    for (int sl = rd.y; sl < rd.y + rd.z; ++sl) {
+      const float* wp = a.ws + ((int64_t)sl * a.hkv + g) * (2 * kTile * kHeadDim) + row * kHeadDim + c;
+      const float4 pk = *(const float4*)wp;
+      const float4 pv = *(const float4*)(wp + kTile * kHeadDim);
+      k4.x += pk.x;
+      k4.y += pk.y;
+      k4.z += pk.z;
+      k4.w += pk.w;
+      v4.x += pv.x;
+      v4.y += pv.y;
+      v4.z += pv.z;
+      v4.w += pv.w;
+    }
+    *(float4*)(a.dk + off) = k4;
+    *(float4*)(a.dv + off) = v4;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_bwd_reduce(const BwdArgs& a, hipStream_t stream) {
+  const int64_t blocks = (int64_t)a.nreduce * a.hkv;
+  if (blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
   const int64_t blocks = (int64_t)a.nitems * a.hq;

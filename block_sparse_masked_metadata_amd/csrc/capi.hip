@@ -41,6 +41,8 @@ int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 
 struct StepLists {
   std::vector<int4> fitems, bitems;
+  std::vector<int4> bwork, breduce;  // split dK/dV work and its reduction
+  int32_t slots = 0;                 // workspace slots of the split work
   int64_t pairs = 0;
 };
 }  // namespace
@@ -61,10 +63,42 @@ struct Packed {
   // byte offsets in the device buffer
   int64_t off_tracks = 0, off_kint = 0, off_items = 0, off_entries = 0, bytes = 0;
   std::vector<int64_t> off_f, off_b, off_ff;  // off_ff: first list entry of each forward item
+  std::vector<int64_t> off_w, off_r;         // split dK/dV work units and reduce entries
   int64_t off_s = 0, off_sf = 0, off_x = 0, off_xf = 0, off_xtracks = 0, off_xkint = 0;
 };
 
 static void layout(const Plan& p, Packed& pk);
+
+// Split work of one step's dK/dV items (one workgroup per item and kv head
+// lasts as long as its column list): a list longer than the mean is cut into
+// sub-tile ranges of about the mean length (at most 16); the first range adds
+// into dK/dV, each other one writes a workspace slot that a reduction adds
+// in slot order afterwards.  Units longest first.
+static void split_work(StepLists& st) {
+  st.bwork.clear();
+  st.breduce.clear();
+  st.slots = 0;
+  if (st.bitems.empty()) return;
+  int64_t sum = 0;
+  for (const int4& it : st.bitems) sum += 2 * (int64_t)it.w;
+  const int64_t n_items = (int64_t)st.bitems.size();
+  const int32_t L = (int32_t)std::max<int64_t>(4, (sum + n_items - 1) / n_items);
+  for (int32_t i = 0; i < (int32_t)n_items; ++i) {
+    const int32_t n = 2 * st.bitems[i].w;
+    const int32_t parts = std::min<int32_t>(16, (n + L - 1) / L);
+    if (parts <= 1) {
+      st.bwork.push_back(make_int4(i, 0, n, -1));
+      continue;
+    }
+    st.breduce.push_back(make_int4(st.bitems[i].x, st.slots, parts - 1, 0));
+    for (int32_t q = 0; q < parts; ++q) {
+      const int32_t a0 = (int32_t)((int64_t)n * q / parts), a1 = (int32_t)((int64_t)n * (q + 1) / parts);
+      st.bwork.push_back(make_int4(i, a0, a1, q == 0 ? -1 : st.slots++));
+    }
+  }
+  std::stable_sort(st.bwork.begin(), st.bwork.end(),
+                   [](const int4& x, const int4& y) { return x.z - x.y > y.z - y.y; });
+}
 
 // Work items longest list first, then grouped by the sample of their tile's
 // first row, groups in the order of their longest item: items of one sample
@@ -169,6 +203,7 @@ static void pack(const Plan& p, int32_t r, Packed& pk) {
       }
     }
     std::stable_sort(st.bitems.begin(), st.bitems.end(), by_len);
+    split_work(st);
   }
   // merged single-pass lists: ring step order, then ascending key tile
   pk.sitems.clear();
@@ -251,6 +286,8 @@ static void layout(const Plan& p, Packed& pk) {
   pk.off_f.assign(R, 0);
   pk.off_b.assign(R, 0);
   pk.off_ff.assign(R, 0);
+  pk.off_w.assign(R, 0);
+  pk.off_r.assign(R, 0);
   for (int32_t s = 0; s < R; ++s) {
     pk.off_f[s] = off;
     off = align256(off + (int64_t)pk.steps[s].fitems.size() * sizeof(int4));
@@ -258,6 +295,10 @@ static void layout(const Plan& p, Packed& pk) {
     off = align256(off + (int64_t)pk.steps[s].fitems.size() * sizeof(int2));
     pk.off_b[s] = off;
     off = align256(off + (int64_t)pk.steps[s].bitems.size() * sizeof(int4));
+    pk.off_w[s] = off;
+    off = align256(off + (int64_t)pk.steps[s].bwork.size() * sizeof(int4));
+    pk.off_r[s] = off;
+    off = align256(off + (int64_t)pk.steps[s].breduce.size() * sizeof(int4));
   }
   pk.off_s = off;
   off = align256(off + (int64_t)pk.sitems.size() * sizeof(int4));
@@ -429,6 +470,7 @@ static int pack_calls(const Plan& p, int32_t r, Packed& pk) {
     }
     std::stable_sort(st.bitems.begin(), st.bitems.end(),
                      [](const int4& x, const int4& y) { return x.w != y.w ? x.w > y.w : x.x < y.x; });
+    split_work(st);
   }
   pk.sitems.clear();
   for (int32_t a = 0; a < T; ++a) {
@@ -468,6 +510,11 @@ struct bsm_dplan {
   const int2* ffirst[64] = {};
   const int4* bitems[64] = {};
   int64_t nf[64] = {}, nb[64] = {}, pairs[64] = {};
+  const int4* bwork[64] = {};   // split dK/dV work units
+  const int4* breduce[64] = {};
+  int64_t nwork[64] = {}, nreduce[64] = {};
+  int32_t slots[64] = {};
+  int32_t ws_slots = 0;         // max over steps
   const int4* sitems = nullptr;
   const int2* sfirst = nullptr;
   int64_t ns = 0;
@@ -648,6 +695,8 @@ int dplan_upload(const bsm_plan* plan, int32_t r, bool dense, void* dev, int64_t
       int2* ff = (int2*)(img.data() + pk.off_ff[s]);
       for (size_t i = 0; i < pk.steps[s].fitems.size(); ++i) ff[i] = pk.entries[pk.steps[s].fitems[i].z];
       std::memcpy(img.data() + pk.off_b[s], pk.steps[s].bitems.data(), pk.steps[s].bitems.size() * sizeof(int4));
+      std::memcpy(img.data() + pk.off_w[s], pk.steps[s].bwork.data(), pk.steps[s].bwork.size() * sizeof(int4));
+      std::memcpy(img.data() + pk.off_r[s], pk.steps[s].breduce.data(), pk.steps[s].breduce.size() * sizeof(int4));
     }
     std::memcpy(img.data() + pk.off_s, pk.sitems.data(), pk.sitems.size() * sizeof(int4));
     int2* sf = (int2*)(img.data() + pk.off_sf);
@@ -683,6 +732,12 @@ int dplan_upload(const bsm_plan* plan, int32_t r, bool dense, void* dev, int64_t
       d->nf[s] = (int64_t)pk.steps[s].fitems.size();
       d->nb[s] = (int64_t)pk.steps[s].bitems.size();
       d->pairs[s] = pk.steps[s].pairs;
+      d->bwork[s] = (const int4*)(base + pk.off_w[s]);
+      d->breduce[s] = (const int4*)(base + pk.off_r[s]);
+      d->nwork[s] = (int64_t)pk.steps[s].bwork.size();
+      d->nreduce[s] = (int64_t)pk.steps[s].breduce.size();
+      d->slots[s] = pk.steps[s].slots;
+      d->ws_slots = std::max(d->ws_slots, pk.steps[s].slots);
     }
     d->sitems = (const int4*)(base + pk.off_s);
     d->sfirst = (const int2*)(base + pk.off_sf);
@@ -767,6 +822,7 @@ int bsm_dplan_get_info(const bsm_dplan* d, bsm_dplan_info* out) {
   out->fetch_tiles = d->fetch_tiles;
   out->fetch_rows = d->fetch_rows;
   out->dense_calls = d->dense;
+  out->bwd_workspace_slots = d->ws_slots;
   return BSM_OK;
 }
 
@@ -942,9 +998,21 @@ int bsm_bwd_prep(const bsm_heads* heads, int64_t rows, const void* o, const void
   return hip_status(launch_bwd_prep(rows, heads->hq, bf(o), bf(dout), delta, st), "bwd prep launch", st);
 }
 
-int bsm_bwd_step(const bsm_dplan* d, int32_t s, const bsm_heads* heads, const void* q,
-                 const void* k, const void* v, const void* dout, const float* lse,
-                 const float* delta, float* dq_acc, float* dk, float* dv, void* stream) {
+}  // extern "C"
+
+namespace {
+// Workgroups a launch should have to keep every CU busy past its longest
+// item: twice the CU count of the current device.
+int64_t busy_blocks() {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
+  return 2 * (int64_t)cus;
+}
+
+int bwd_step(const bsm_dplan* d, int32_t s, const bsm_heads* heads, const void* q, const void* k, const void* v,
+             const void* dout, const float* lse, const float* delta, float* dq_acc, float* dk, float* dv,
+             void* workspace, int64_t workspace_bytes, void* stream) {
   if (!d) { set_error("null device plan"); return BSM_E_INVALID; }
   int rc = check_heads(heads);
   if (rc) return rc;
@@ -954,6 +1022,16 @@ int bsm_bwd_step(const bsm_dplan* d, int32_t s, const bsm_heads* heads, const vo
     return BSM_E_INVALID;
   }
   if ((rc = check_rows(d->S, heads->hq, "q/dout")) || (rc = check_rows(d->S, heads->hkv, "k/v"))) return rc;
+  // split the dK/dV work when a workspace is given and the launch would
+  // otherwise leave CUs waiting on its longest column lists
+  const bool split = workspace && d->nreduce[s] > 0 && d->nb[s] * heads->hkv < busy_blocks();
+  if (split) {
+    const int64_t need = (int64_t)d->slots[s] * heads->hkv * 2 * kTile * kHeadDim * (int64_t)sizeof(float);
+    if (workspace_bytes < need) {
+      set_error("backward workspace too small: need " + std::to_string(need) + " bytes");
+      return BSM_E_INVALID;
+    }
+  }
   const int32_t j = ((d->r - s) % d->R + d->R) % d->R;
   BwdArgs a{};
   a.entries = d->entries;
@@ -987,11 +1065,37 @@ int bsm_bwd_step(const bsm_dplan* d, int32_t s, const bsm_heads* heads, const vo
   }
   if (d->nb[s]) {
     a.items = d->bitems[s];
-    a.nitems = (int32_t)d->nb[s];
     a.heads_per_xcd = heads->hkv % 8 == 0 ? heads->hkv / 8 : 0;
-    rc = hip_status(launch_bwd_dkdv(a, st), "bwd dkdv launch", st);
+    if (split) {
+      a.work = d->bwork[s];
+      a.nitems = (int32_t)d->nwork[s];
+      a.ws = (float*)workspace;
+      a.reduce = d->breduce[s];
+      a.nreduce = (int32_t)d->nreduce[s];
+      rc = hip_status(launch_bwd_dkdv(a, st), "bwd dkdv launch", st);
+      if (rc) return rc;
+      rc = hip_status(launch_bwd_reduce(a, st), "bwd reduce launch", st);
+    } else {
+      a.nitems = (int32_t)d->nb[s];
+      rc = hip_status(launch_bwd_dkdv(a, st), "bwd dkdv launch", st);
+    }
   }
   return rc;
+}
+}  // namespace
+
+extern "C" {
+
+int bsm_bwd_step(const bsm_dplan* d, int32_t s, const bsm_heads* heads, const void* q,
+                 const void* k, const void* v, const void* dout, const float* lse,
+                 const float* delta, float* dq_acc, float* dk, float* dv, void* stream) {
+  return bwd_step(d, s, heads, q, k, v, dout, lse, delta, dq_acc, dk, dv, nullptr, 0, stream);
+}
+
+int bsm_bwd_step_ws(const bsm_dplan* d, int32_t s, const bsm_heads* heads, const void* q, const void* k,
+                    const void* v, const void* dout, const float* lse, const float* delta, float* dq_acc,
+                    float* dk, float* dv, void* workspace, int64_t workspace_bytes, void* stream) {
+  return bwd_step(d, s, heads, q, k, v, dout, lse, delta, dq_acc, dk, dv, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -131,6 +131,16 @@ struct BwdArgs {
   float scale;                // softmax scale
   float scale_log2;
   int32_t window;
+  // split dK/dV work (nullable): work units int4 {item, first sub-tile, end
+  // sub-tile, workspace slot or -1}; nitems counts the units.  A unit with a
+  // slot writes its scaled partial dK, dV of the tile to workspace slot
+  // (slot * Hkv + kv head) as two [128 keys][128] fp32 blocks; a unit without
+  // one adds into dk / dv.
+  const int4* work;
+  float* ws;
+  // reduction after a split launch: int4 {key tile, first slot, slots, 0}
+  const int4* reduce;
+  int32_t nreduce;
 };
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
@@ -145,5 +155,7 @@ hipError_t launch_bwd_prep(int64_t rows, int32_t hq, const uint16_t* o,
                            const uint16_t* dout, float* delta, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);
+// dk/dv rows of every reduce entry's key tile += its workspace slots, in slot order.
+hipError_t launch_bwd_reduce(const BwdArgs& a, hipStream_t stream);
 
 }  // namespace bsm

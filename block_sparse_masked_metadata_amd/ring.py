@@ -274,19 +274,36 @@ def bwd_prep(hd, o, dout, delta=None):
     return delta
 
 
-def bwd_step(dp: DevicePlan, s, hd, q, k, v, dout, lse, delta, dq, dk, dv):
+def bwd_workspace(dp: DevicePlan, hd, device="cuda"):
+    """The workspace bsm_bwd_step_ws needs for this plan (None when no step splits)."""
+    import torch
+    slots = dp.info["bwd_workspace_slots"]
+    if slots == 0:
+        return None
+    return torch.empty(slots * hd.hkv * 2 * 128 * 128, dtype=torch.float32, device=device)
+
+
+def bwd_step(dp: DevicePlan, s, hd, q, k, v, dout, lse, delta, dq, dk, dv, workspace=None):
     """One backward ring step against shard j = (r - s) mod R: dq carried
-    (first step with work overwrites), dk/dv of shard j added to."""
-    C.bsm_bwd_step(dp.handle, s, hd, _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(delta),
-                   _ptr(dq), _ptr(dk), _ptr(dv), _stream())
+    (first step with work overwrites), dk/dv of shard j added to.  With a
+    workspace (bwd_workspace), long dK/dV lists may be split."""
+    if workspace is None:
+        C.bsm_bwd_step(dp.handle, s, hd, _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(delta),
+                       _ptr(dq), _ptr(dk), _ptr(dv), _stream())
+    else:
+        C.bsm_bwd_step_ws(dp.handle, s, hd, _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse),
+                          _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                          workspace.numel() * workspace.element_size(), _stream())
 
 
-def bwd_ring(dp: DevicePlan, hd, q, k_shards, v_shards, dout, o, lse, grads=None, steps=None):
+def bwd_ring(dp: DevicePlan, hd, q, k_shards, v_shards, dout, o, lse, grads=None, steps=None,
+             split=True):
     """Backward over ring steps s = 0..R-1.  Returns (dq, dk_shards, dv_shards) in fp32.
 
     dk/dv shards are accumulated (+=) by the kernels: they are cleared here
     first, as the owner of a travelling accumulator would before the first
-    contribution."""
+    contribution.  split: give the steps a workspace so long dK/dV lists can
+    be split (bsm_bwd_step_ws)."""
     import torch
     rows = dp.rows
     _need(dout, torch.bfloat16, (rows, hd.hq, hd.d), "dout")
@@ -301,7 +318,8 @@ def bwd_ring(dp: DevicePlan, hd, q, k_shards, v_shards, dout, o, lse, grads=None
         dq, dks, dvs = grads
         for t in dks + dvs:
             t.zero_()
+    ws = bwd_workspace(dp, hd, q.device) if split else None
     for s in (range(dp.ranks) if steps is None else steps):
         j = (dp.rank - s) % dp.ranks
-        bwd_step(dp, s, hd, q, k_shards[j], v_shards[j], dout, lse, delta, dq, dks[j], dvs[j])
+        bwd_step(dp, s, hd, q, k_shards[j], v_shards[j], dout, lse, delta, dq, dks[j], dvs[j], ws)
     return dq, dks, dvs

@@ -308,6 +308,8 @@ typedef struct {
   int64_t fetch_tiles;       /* remote key tiles the rank needs (sparse fetch) */
   int64_t fetch_rows;        /* rows of the compact key/value buffer          */
   int32_t dense_calls;       /* 1: a dense-call device plan                   */
+  int32_t bwd_workspace_slots; /* max over steps of the split dK/dV work's
+                                  workspace slots (each Hkv * 128 KiB)      */
 } bsm_dplan_info;
 
 int bsm_dplan_get_info(const bsm_dplan* dplan, bsm_dplan_info* out);
@@ -447,6 +449,26 @@ int bsm_bwd_step(const bsm_dplan* dplan, int32_t s, const bsm_heads* heads,
                  const void* q, const void* k, const void* v, const void* dout,
                  const float* lse, const float* delta,
                  float* dq_acc, float* dk, float* dv, void* stream);
+
+/*
+ * bsm_bwd_step with a caller workspace, for layouts whose dK/dV launch would
+ * last as long as its few longest column lists (one workgroup per key tile
+ * and key/value head; MARBLE section 03 balances ring steps across ranks, this
+ * balances one step's work across the GPU).  When the step has fewer than
+ * twice as many (key tile, kv head) units as the device has CUs and its plan
+ * splits lists (bsm_dplan_info.bwd_workspace_slots > 0), each long list is cut
+ * into sub-tile ranges: the first adds into dk/dv, the others write their
+ * partial sums to workspace slots, and a reduction then adds the slots into
+ * dk/dv in slot order (deterministic; sums in a different order than the
+ * unsplit call, so results differ from it by rounding).  workspace: device
+ * memory of at least bwd_workspace_slots * Hkv * 131072 bytes, clobbered; NULL
+ * behaves as bsm_bwd_step.  A smaller workspace_bytes than the step needs
+ * returns BSM_E_INVALID before any launch.  Other arguments as bsm_bwd_step.
+ */
+int bsm_bwd_step_ws(const bsm_dplan* dplan, int32_t s, const bsm_heads* heads,
+                    const void* q, const void* k, const void* v, const void* dout,
+                    const float* lse, const float* delta, float* dq_acc, float* dk, float* dv,
+                    void* workspace, int64_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

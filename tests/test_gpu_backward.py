@@ -83,3 +83,62 @@ def test_full_size_dq_sampled(maker):
     for j in range(case.R):
         if case.dp.info["bwd_items"][(case.r - j) % case.R] == 0:
             assert torch.count_nonzero(dks[j]) == 0 and torch.count_nonzero(dvs[j]) == 0
+
+
+def test_split_dkdv_matches_unsplit_and_oracle():
+    """Packed text: the dK/dV launch has fewer (key tile, kv head) units than
+    twice the CUs, so with a workspace its long column lists are split and
+    reduced in order.  Split and unsplit gradients both match the oracle and
+    each other to rounding."""
+    from workloads import packed_text
+    case = Case(packed_text(), with_do=True)
+    assert case.dp.info["bwd_workspace_slots"] > 0
+    o, lse, _ = case.ring()
+    g_split = bsm.bwd_ring(case.dp, case.heads, case.q, case.k_shards, case.v_shards, case.dout, o, lse,
+                           split=True)
+    g_plain = bsm.bwd_ring(case.dp, case.heads, case.q, case.k_shards, case.v_shards, case.dout, o, lse,
+                           split=False)
+    torch.cuda.synchronize()
+    for x, y in zip([g_split[0]] + g_split[1] + g_split[2], [g_plain[0]] + g_plain[1] + g_plain[2]):
+        assert float((x - y).abs().max()) <= 1e-3 * max(1.0, float(y.abs().max()))
+    sel = np.arange(case.S)
+    ref = _oracle(case, sel)
+    grad_ok(g_split[0].cpu().numpy(), ref["dq"], "dq")
+    n, hkv = case.lay.n, case.hkv
+    dk = np.zeros((n, hkv, 128))
+    dv = np.zeros_like(dk)
+    dk[case.perm] = torch.cat(g_split[1]).cpu().numpy()
+    dv[case.perm] = torch.cat(g_split[2]).cpu().numpy()
+    dk_ref = np.zeros_like(dk)
+    dv_ref = np.zeros_like(dv)
+    for a, b, dkb, dvb in ref["dkv"]:
+        dk_ref[a:b] += dkb
+        dv_ref[a:b] += dvb
+    e2 = grad_ok(dk, dk_ref, "dk")
+    e3 = grad_ok(dv, dv_ref, "dv")
+    print(f"  split dk {e2:.3e} dv {e3:.3e}", flush=True)
+
+
+def test_split_workspace_too_small_is_refused():
+    """Every buffer is real and sized for the step, so the call is a valid
+    launch whether or not the step splits; a step that splits must refuse a
+    16-byte workspace before launching."""
+    from workloads import packed_text
+    case = Case(packed_text(), with_do=True)
+    o, lse, _ = case.ring()
+    delta = bsm.bwd_prep(case.heads, o, case.dout)
+    dq = torch.zeros(case.S, case.hq, 128, dtype=torch.float32, device="cuda")
+    dk = torch.zeros(case.S, case.hkv, 128, dtype=torch.float32, device="cuda")
+    dv = torch.zeros_like(dk)
+    tiny = torch.zeros(4, dtype=torch.float32, device="cuda")
+    refused = 0
+    for s in range(case.R):
+        j = (case.r - s) % case.R
+        try:
+            bsm.bwd_step(case.dp, s, case.heads, case.q, case.k_shards[j], case.v_shards[j], case.dout,
+                         lse, delta, dq, dk, dv, workspace=tiny)
+        except bsm.BsmError as e:
+            assert e.code == bsm._capi.BSM_E_INVALID and "workspace" in str(e)
+            refused += 1
+    torch.cuda.synchronize()
+    assert refused > 0

@@ -148,3 +148,36 @@ def test_dense_calls_backward_equals_block_sparse_closely():
     for x, y in zip([ga[0]] + list(ga[1]) + list(ga[2]), [gb[0]] + list(gb[1]) + list(gb[2])):
         scale = max(1.0, float(x.abs().max()))
         assert float((x - y).abs().max()) <= 2e-3 * scale
+
+
+@pytest.mark.parametrize("dense", [False, True], ids=["block_sparse", "dense_calls"])
+@pytest.mark.parametrize("R,S", [(2, 200), (3, 330)])
+def test_ragged_shards_forward_backward(R, S, dense):
+    """Contiguous shards of S tokens (S not a multiple of 128): a ragged last
+    query and key tile, the padded tile-blocked state, every rank, forward
+    and backward against the oracle."""
+    from oracle import backward as obwd
+    from gpu_common import grad_ok
+    rng = np.random.default_rng(1700 + S + R)
+    lay = random_small(rng, R * S, max_span=150)
+    lay.ranks, lay.order, lay.seed = R, "contiguous", 120 + S
+    lay.hq, lay.hkv, lay.d = 4, 2, 128
+    for r in range(R):
+        case = Case(lay, rank=r, with_do=True, dense=dense)
+        assert case.S == S
+        _check(case, np.arange(S))
+        dq, dks, dvs = _grads(case)
+        ref = obwd.backward_rows(lay.tracks(), lay.window, case.cpu(0), case.cpu(1), case.cpu(2),
+                                 case.cpu(3), case.rows, 1.0 / np.sqrt(lay.d))
+        grad_ok(dq.cpu().numpy(), ref["dq"], "dq")
+        dk = np.zeros((lay.n, lay.hkv, 128))
+        dv = np.zeros_like(dk)
+        dk[case.perm] = torch.cat(dks).cpu().numpy()
+        dv[case.perm] = torch.cat(dvs).cpu().numpy()
+        dk_ref = np.zeros_like(dk)
+        dv_ref = np.zeros_like(dv)
+        for a, b, dkb, dvb in ref["dkv"]:
+            dk_ref[a:b] += dkb
+            dv_ref[a:b] += dvb
+        grad_ok(dk, dk_ref, "dk")
+        grad_ok(dv, dv_ref, "dv")

@@ -184,7 +184,50 @@ def cpu_baseline(lay, plan_pairs_fn, rows_all, q, k, v, target_s):
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"fp64 oracle forward of {done_rows} query rows of the measured rank "
                       f"({len(used)} whole samples, {pairs} legal pairs) in {dt:.1f} s; "
-                      f"host {platform.processor() or platform.machine()}"}
+                      f"host {platform.processor() or platform.machine()}, "
+                      f"{len(os.sched_getaffinity(0))} cores in the affinity mask"}
+
+
+def mfma_probe(torch):
+    """Dense bf16 MFMA rate and shader clock measured on this GPU with the
+    probe library (independent MFMA chains on every SIMD); None if it is not
+    built."""
+    import ctypes
+    path = os.path.join(HERE, "block_sparse_masked_metadata_amd", "libbsm_probe.so")
+    if not os.path.exists(path):
+        return None
+    fn = ctypes.CDLL(path).bsm_probe_mfma
+    fn.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks, iters = 2 * cus, 4000  # two workgroups per CU: two waves per SIMD
+    stamps = torch.zeros(blocks * 16, dtype=torch.int64, device="cuda")
+    sink = torch.zeros(blocks * 4, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    assert fn(blocks, 200, stamps.data_ptr(), sink.data_ptr(), stream) == 0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    assert fn(blocks, iters, stamps.data_ptr(), sink.data_ptr(), stream) == 0
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    st = stamps.view(-1, 4).cpu().double()
+    clock = float(((st[:, 1] - st[:, 0]) / (st[:, 3] - st[:, 2])).median()) * 0.1  # real-time counter: 100 MHz
+    return {"tflops": round(blocks * 4 * iters * 8 * 32768 / (ms * 1e-3) / 1e12, 1),
+            "clock_ghz": round(clock, 3), "cus": cus,
+            "kind": "v_mfma_f32_32x32x16_bf16, 8 independent chains per wave, 2 waves per SIMD"}
+
+
+def planner_timing(bsm, lay):
+    """Host planner wall time at one thread and at every core of this process."""
+    cores = len(os.sched_getaffinity(0))
+    out = {}
+    for name, th in (("threads_1_s", 1), ("threads_all_s", cores)):
+        t0 = time.perf_counter()
+        bsm.Plan.from_layout(lay, threads=th)
+        out[name] = round(time.perf_counter() - t0, 4)
+    out["cores"] = cores
+    return out
 
 
 def ring_estimate(bsm, torch, plan, hd, full, perm, k_all, v_all, lay, d, passes, dense=False):
@@ -407,7 +450,8 @@ def main():
     wall = time.perf_counter() - wall0
 
     total_ms = start.elapsed_time(end)
-    fwd_ms = sum(a.elapsed_time(b) for a, b in marks) / args.steps
+    fwd_each = sorted(a.elapsed_time(b) for a, b in marks)
+    fwd_ms = sum(fwd_each) / args.steps
     step_ms = total_ms / args.steps
     bwd_ms = step_ms - fwd_ms if do_bwd else 0.0
     launches = [launch_ev[i].elapsed_time(launch_ev[i + 1]) for i in range(0, len(launch_ev), 2)]
@@ -455,6 +499,8 @@ def main():
                    "legal_pairs": total_pairs, "layout": lay.order},
         "pct_of_peak": round(100 * fwd_tflops / PEAK_BF16_TFLOPS, 2),
         "fwd_ms": round(fwd_ms, 4),
+        "fwd_ms_median_min_max": [round(float(np.median(fwd_each)), 4), round(fwd_each[0], 4),
+                                  round(fwd_each[-1], 4)],
         "fwd_tflops": round(fwd_tflops, 2),
         "fwd_bwd": None if not do_bwd else {
             "ms": round(step_ms, 4), "bwd_ms": round(bwd_ms, 4),
@@ -486,6 +532,11 @@ def main():
     }
     if args.merge != "carry":
         out["roofline"] = None  # the timed forward includes fills and merge kernels
+    probe = mfma_probe(torch)
+    if probe:
+        probe["fwd_frac"] = round(mfma_tflops / probe["tflops"], 4)  # the forward kernel, per launch
+        out["mfma_probe"] = probe
+    out["planner"] = planner_timing(bsm, lay)
     if chunk_info is not None:
         out["chunking"] = chunk_info
     if args.ring_estimate:

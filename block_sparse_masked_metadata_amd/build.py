@@ -16,6 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbsm.so")
+PROBE_LIB = os.path.join(HERE, "libbsm_probe.so")  # MFMA rate / clock probe for bench.py
 ARCH = os.environ.get("BSM_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -62,8 +63,12 @@ def build(verbose: bool = False) -> str:
     if not _run([[HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-pthread", *objs, "-o", tmp]]):
         raise RuntimeError("libbsm link failed")
     os.replace(tmp, LIB)
+    tmp = PROBE_LIB + ".tmp"
+    if not _run([[HIPCC, *HIP_FLAGS, "-shared", os.path.join(CSRC, "probe.hip"), "-o", tmp]]):
+        raise RuntimeError("libbsm_probe build failed")
+    os.replace(tmp, PROBE_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", os.path.basename(PROBE_LIB))
     return LIB
 
 

@@ -462,7 +462,8 @@ int bsm_bwd_step(const bsm_dplan* dplan, int32_t s, const bsm_heads* heads,
  * dk/dv in slot order (deterministic; sums in a different order than the
  * unsplit call, so results differ from it by rounding).  workspace: device
  * memory of at least bwd_workspace_slots * Hkv * 131072 bytes, clobbered; NULL
- * behaves as bsm_bwd_step.  A smaller workspace_bytes than the step needs
+ * behaves as bsm_bwd_step.  Calls in stream order may share one workspace;
+ * calls that can run concurrently (other streams) need their own.  A smaller workspace_bytes than the step needs
  * returns BSM_E_INVALID before any launch.  Other arguments as bsm_bwd_step.
  */
 int bsm_bwd_step_ws(const bsm_dplan* dplan, int32_t s, const bsm_heads* heads,

@@ -22,3 +22,24 @@ def test_traffic_only_for_matching_sources():
     # either the committed summary matches the current forward sources, or it is
     # stale and reported as unknown
     assert v is None or v > 1e8
+
+
+def test_planner_timing_and_algorithmic_bytes_on_cpu():
+    """The host-only pieces of the bench line: planner timing at 1 and all
+    threads, and the forward's algorithmic bytes (positive, one per step with
+    work, state elided at a tile's first and last step)."""
+    sys.path.insert(0, ROOT)
+    import bench
+    import numpy as np
+    import block_sparse_masked_metadata_amd as bsm
+    from workloads import config
+    lay = config(2)
+    t = bench.planner_timing(bsm, lay)
+    assert t["threads_1_s"] > 0 and t["threads_all_s"] > 0 and t["cores"] >= 1
+    plan = bsm.Plan.from_layout(lay)
+    r, S = plan.info["busiest_rank"], plan.info["shard_tokens"]
+    per = bench.fwd_algorithmic_bytes(plan, r, lay.ranks, S, lay.hq, lay.hkv, 128)
+    pairs = plan.pairs()[r]
+    assert len(per) == int((pairs > 0).sum()) and all(b > 0 for b in per)
+    single = bench.fwd_algorithmic_bytes(plan, r, lay.ranks, S, lay.hq, lay.hkv, 128, single=True)[0]
+    assert single < sum(per)  # the single pass moves no carried state

@@ -220,3 +220,15 @@ def test_state_unpack_channel_order():
     assert bool((lt > 0).all())
     want = torch.arange(128, dtype=torch.float32, device="cuda").expand_as(rows)
     assert bool((((rows / lt) - want).abs() <= want * 2.0 ** -8 + 1e-3).all())
+
+
+def test_mfma_probe_reports_a_plausible_rate_and_clock():
+    """The measurement probe (libbsm_probe.so) runs and reads back sane numbers."""
+    import os
+    import sys
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import bench
+    pr = bench.mfma_probe(torch)
+    assert pr is not None, "libbsm_probe.so is not built"
+    assert 100.0 < pr["tflops"] < 3000.0
+    assert 0.5 < pr["clock_ghz"] < 3.0

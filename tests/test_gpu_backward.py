@@ -70,10 +70,46 @@ def test_packed_multimodal_scaled_full_backward():
     _check_full(Case(lay, with_do=True))
 
 
+def _check_key_sums(case, o, lse, dks, dvs):
+    """Sums over every key of the rank's dK/dV, which hold at any size.
+
+    Rows of P sum to 1, so the sum over keys of dV equals the sum over the
+    rank's queries of dO (per key/value head: the group's query heads added).
+    The kernels round P to bf16 (relative error at most 2^-9 per term), so the
+    two sides differ by at most 2^-9 sum |dO| per channel; the test allows 2^-8.
+
+    Sum_j dS_ij = sum_j P_ij (dP_ij - D_i) = dO_i . (O_exact_i - O_i) plus the
+    bf16 rounding of P and dS, so sum over keys of dK = scale sum_i q_i sum_j
+    dS_ij is zero up to E_i = 2^-7 (|dO_i|_2 Vmax + |D_i|) per query and head,
+    Vmax the largest |v_j|_2 of the head: |O_exact - O| <= 2^-8 Vmax (bf16 O
+    and bf16 P), the dS rounding adds 2^-9 (|dO_i|_2 Vmax + |D_i|).  A wrong
+    D, LSE, scale or a dropped key tile moves either sum by orders of magnitude
+    more than these bounds."""
+    grp = case.hq // case.hkv
+    live = torch.isfinite(lse).T[:, :, None]                      # [S, hq, 1]: rows with a legal key
+    do = torch.where(live, case.dout.double(), torch.zeros((), dtype=torch.float64, device="cuda"))
+    dv_sum = sum(d.double().sum(0) for d in dvs)                  # [hkv, d]
+    do_sum = do.sum(0).view(case.hkv, grp, -1).sum(1)
+    do_abs = do.abs().sum(0).view(case.hkv, grp, -1).sum(1)
+    err_v = ((dv_sum - do_sum).abs() / do_abs.clamp_min(1e-30)).max().item()
+    assert err_v <= 2.0 ** -8, f"sum of dV over keys: relative error {err_v:.3e}"
+    scale = 1.0 / np.sqrt(case.lay.d)
+    vmax = case.v_all.double().norm(dim=2).max(0).values          # [hkv]
+    vmax_q = vmax.repeat_interleave(grp)[None, :]                   # [1, hq]
+    dd = (do * o.double()).sum(2)                                   # D_i per head [S, hq]
+    e = 2.0 ** -7 * (do.norm(dim=2) * vmax_q + dd.abs())            # [S, hq]
+    bound = scale * (case.q.double().abs() * e[:, :, None]).sum(0).view(case.hkv, grp, -1).sum(1)
+    dk_sum = sum(d.double().sum(0) for d in dks)
+    ratio = (dk_sum.abs() / bound.clamp_min(1e-30)).max().item()
+    assert ratio <= 1.0, f"sum of dK over keys exceeds its rounding bound ({ratio:.3f} of it)"
+    print(f"  key sums: dV rel {err_v:.3e}, dK at {ratio:.3e} of its bound", flush=True)
+
+
 @pytest.mark.parametrize("maker", [sliding_window, long_mixed], ids=["sliding_window_128k", "long_mixed_1m"])
 def test_full_size_dq_sampled(maker):
     case = Case(maker(), with_do=True)
     o, lse, dq, dks, dvs = _run(case)
+    _check_key_sums(case, o, lse, dks, dvs)
     rng = np.random.default_rng(3)
     sel = np.sort(rng.choice(case.S, 128, replace=False))
     ref = _oracle(case, sel)

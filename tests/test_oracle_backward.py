@@ -64,3 +64,32 @@ def test_delta_and_unread_keys():
     for a, b, dkb, dvb in g["dkv"]:
         dk[a:b] += dkb
     assert np.all(dk[~read] == 0)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_key_sum_identities(seed):
+    """Summed over every key: dV gives the summed dO of the rows that read a
+    key (each row of P sums to 1), and dK gives zero (sum_j dS_ij =
+    dO_i . O_i - D_i = 0), per key/value head over its group of query heads."""
+    rng = np.random.default_rng(40 + seed)
+    lay = random_small(rng, 40)
+    tr = lay.tracks()
+    n, hq, hkv, d = lay.n, 6, 2, 5
+    q = rng.standard_normal((n, hq, d))
+    k = rng.standard_normal((n, hkv, d))
+    v = rng.standard_normal((n, hkv, d))
+    do = rng.standard_normal((n, hq, d))
+    rows = np.sort(rng.choice(n, size=2 * n // 3, replace=False))
+    g = backward.backward_rows(tr, lay.window, q, k, v, do, rows, 0.61)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for a, b, dkb, dvb in g["dkv"]:
+        dk[a:b] += dkb
+        dv[a:b] += dvb
+    from oracle.mask import legal, take
+    live = legal(take(tr, rows), tr, lay.window).any(1)     # rows with a legal key
+    do_live = do[rows][live]                                 # [rows, hq, d]
+    want = do_live.sum(0).reshape(hkv, hq // hkv, d).sum(1)
+    np.testing.assert_allclose(dv.sum(0), want, rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dk.sum(0), 0.0, rtol=0, atol=1e-11)
+    assert np.abs(dk).max() > 1e-2                           # the identity is not vacuous

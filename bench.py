@@ -16,6 +16,8 @@ every layer), as do plan upload and the input permutation.
 Only unmasked FLOPs count: 4*d*Hq per legal (query, key) pair forward,
 10*d*Hq backward.  `value` is the forward rate (the forward is the quoted
 pass of this workload); the forward+backward rate is reported beside it.
+The roofline's average launch duration comes from HIP events around each
+forward launch of the last timed pass.
 """
 from __future__ import annotations
 
@@ -439,7 +441,9 @@ def main():
         f0 = torch.cuda.Event(enable_timing=True)
         f1 = torch.cuda.Event(enable_timing=True)
         f0.record()
-        forward(launch_ev)
+        # per-launch events on the last timed pass only: recorded between
+        # back-to-back launches they stretch the forward by 5-13%
+        forward(launch_ev if _ == args.steps - 1 else None)
         f1.record()
         marks.append((f0, f1))
         if do_bwd:

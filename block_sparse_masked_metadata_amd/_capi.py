@@ -46,7 +46,7 @@ EXPORTS = [
     "bsm_dplan_bytes", "bsm_dplan_upload", "bsm_dplan_free", "bsm_dplan_get_info",
     "bsm_fwd_step", "bsm_fwd_single", "bsm_fwd_merge_bf16", "bsm_fwd_merge_fp32",
     "bsm_bwd_prep", "bsm_bwd_step", "bsm_plan_dense_calls", "bsm_dplan_calls_bytes",
-    "bsm_dplan_calls_upload", "bsm_state_unpack", "bsm_bwd_step_ws",
+    "bsm_dplan_calls_upload", "bsm_state_unpack", "bsm_bwd_step_ws", "bsm_bwd_step_streams",
 ]
 
 
@@ -132,6 +132,8 @@ _sig = {
                                _P, _P, _P, _P]),
     "bsm_bwd_step_ws": (C.c_int, [_P, C.c_int32, C.POINTER(bsm_heads), _P, _P, _P, _P, _P, _P,
                                   _P, _P, _P, _P, C.c_int64, _P]),
+    "bsm_bwd_step_streams": (C.c_int, [_P, C.c_int32, C.POINTER(bsm_heads), _P, _P, _P, _P, _P, _P,
+                                       _P, _P, _P, _P, C.c_int64, _P, _P]),
 }
 for _name, (_res, _args) in _sig.items():
     _fn = getattr(_lib, _name)
@@ -332,3 +334,10 @@ def bsm_bwd_step_ws(dplan, s, heads, q, k, v, dout, lse, delta, dq_acc, dk, dv, 
                     workspace_bytes, stream):
     _check(_lib.bsm_bwd_step_ws(dplan, int(s), C.byref(heads), q, k, v, dout, lse, delta,
                                 dq_acc, dk, dv, workspace, int(workspace_bytes), stream))
+
+
+def bsm_bwd_step_streams(dplan, s, heads, q, k, v, dout, lse, delta, dq_acc, dk, dv, workspace,
+                         workspace_bytes, dq_stream, kv_stream):
+    _check(_lib.bsm_bwd_step_streams(dplan, int(s), C.byref(heads), q, k, v, dout, lse, delta,
+                                     dq_acc, dk, dv, workspace, int(workspace_bytes), dq_stream,
+                                     kv_stream))

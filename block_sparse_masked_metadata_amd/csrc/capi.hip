@@ -1012,7 +1012,7 @@ int64_t busy_blocks() {
 
 int bwd_step(const bsm_dplan* d, int32_t s, const bsm_heads* heads, const void* q, const void* k, const void* v,
              const void* dout, const float* lse, const float* delta, float* dq_acc, float* dk, float* dv,
-             void* workspace, int64_t workspace_bytes, void* stream) {
+             void* workspace, int64_t workspace_bytes, void* stream, void* kv_stream) {
   if (!d) { set_error("null device plan"); return BSM_E_INVALID; }
   int rc = check_heads(heads);
   if (rc) return rc;
@@ -1063,6 +1063,7 @@ int bwd_step(const bsm_dplan* d, int32_t s, const bsm_heads* heads, const void* 
     rc = hip_status(launch_bwd_dq(a, st), "bwd dq launch", st);
     if (rc) return rc;
   }
+  st = (hipStream_t)kv_stream;
   if (d->nb[s]) {
     a.items = d->bitems[s];
     a.heads_per_xcd = heads->hkv % 8 == 0 ? heads->hkv / 8 : 0;
@@ -1089,13 +1090,22 @@ extern "C" {
 int bsm_bwd_step(const bsm_dplan* d, int32_t s, const bsm_heads* heads, const void* q,
                  const void* k, const void* v, const void* dout, const float* lse,
                  const float* delta, float* dq_acc, float* dk, float* dv, void* stream) {
-  return bwd_step(d, s, heads, q, k, v, dout, lse, delta, dq_acc, dk, dv, nullptr, 0, stream);
+  return bwd_step(d, s, heads, q, k, v, dout, lse, delta, dq_acc, dk, dv, nullptr, 0, stream, stream);
 }
 
 int bsm_bwd_step_ws(const bsm_dplan* d, int32_t s, const bsm_heads* heads, const void* q, const void* k,
                     const void* v, const void* dout, const float* lse, const float* delta, float* dq_acc,
                     float* dk, float* dv, void* workspace, int64_t workspace_bytes, void* stream) {
-  return bwd_step(d, s, heads, q, k, v, dout, lse, delta, dq_acc, dk, dv, workspace, workspace_bytes, stream);
+  return bwd_step(d, s, heads, q, k, v, dout, lse, delta, dq_acc, dk, dv, workspace, workspace_bytes, stream,
+                  stream);
+}
+
+int bsm_bwd_step_streams(const bsm_dplan* d, int32_t s, const bsm_heads* heads, const void* q, const void* k,
+                         const void* v, const void* dout, const float* lse, const float* delta, float* dq_acc,
+                         float* dk, float* dv, void* workspace, int64_t workspace_bytes, void* dq_stream,
+                         void* kv_stream) {
+  return bwd_step(d, s, heads, q, k, v, dout, lse, delta, dq_acc, dk, dv, workspace, workspace_bytes, dq_stream,
+                  kv_stream);
 }
 
 }  // extern "C"

@@ -283,11 +283,19 @@ def bwd_workspace(dp: DevicePlan, hd, device="cuda"):
     return torch.empty(slots * hd.hkv * 2 * 128 * 128, dtype=torch.float32, device=device)
 
 
-def bwd_step(dp: DevicePlan, s, hd, q, k, v, dout, lse, delta, dq, dk, dv, workspace=None):
+def bwd_step(dp: DevicePlan, s, hd, q, k, v, dout, lse, delta, dq, dk, dv, workspace=None, kv_stream=None):
     """One backward ring step against shard j = (r - s) mod R: dq carried
     (first step with work overwrites), dk/dv of shard j added to.  With a
-    workspace (bwd_workspace), long dK/dV lists may be split."""
-    if workspace is None:
+    workspace (bwd_workspace), long dK/dV lists may be split.  With kv_stream
+    (a torch stream), the dK/dV update goes there and dq's on the current
+    stream (bsm_bwd_step_streams); the caller orders the inputs before both
+    and joins them before reading the gradients."""
+    if kv_stream is not None:
+        nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        C.bsm_bwd_step_streams(dp.handle, s, hd, _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse),
+                               _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), nbytes,
+                               _stream(), kv_stream.cuda_stream)
+    elif workspace is None:
         C.bsm_bwd_step(dp.handle, s, hd, _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(delta),
                        _ptr(dq), _ptr(dk), _ptr(dv), _stream())
     else:
@@ -297,13 +305,15 @@ def bwd_step(dp: DevicePlan, s, hd, q, k, v, dout, lse, delta, dq, dk, dv, works
 
 
 def bwd_ring(dp: DevicePlan, hd, q, k_shards, v_shards, dout, o, lse, grads=None, steps=None,
-             split=True):
+             split=True, two_streams=False):
     """Backward over ring steps s = 0..R-1.  Returns (dq, dk_shards, dv_shards) in fp32.
 
     dk/dv shards are accumulated (+=) by the kernels: they are cleared here
     first, as the owner of a travelling accumulator would before the first
     contribution.  split: give the steps a workspace so long dK/dV lists can
-    be split (bsm_bwd_step_ws)."""
+    be split (bsm_bwd_step_ws).  two_streams: run every step's dK/dV update
+    on a second stream beside the dQ chain (bsm_bwd_step_streams); it pays
+    when a step has fewer (key tile, kv head) units than CUs."""
     import torch
     rows = dp.rows
     _need(dout, torch.bfloat16, (rows, hd.hq, hd.d), "dout")
@@ -319,7 +329,16 @@ def bwd_ring(dp: DevicePlan, hd, q, k_shards, v_shards, dout, o, lse, grads=None
         for t in dks + dvs:
             t.zero_()
     ws = bwd_workspace(dp, hd, q.device) if split else None
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream(device=q.device) if two_streams else None
+    if side is not None:
+        side.wait_stream(main)  # delta and the cleared accumulators
     for s in (range(dp.ranks) if steps is None else steps):
         j = (dp.rank - s) % dp.ranks
-        bwd_step(dp, s, hd, q, k_shards[j], v_shards[j], dout, lse, delta, dq, dks[j], dvs[j], ws)
+        bwd_step(dp, s, hd, q, k_shards[j], v_shards[j], dout, lse, delta, dq, dks[j], dvs[j], ws,
+                 kv_stream=side)
+    if side is not None:
+        main.wait_stream(side)
+        for t in [delta, dout, q, lse] + list(k_shards) + list(v_shards) + dks + dvs + ([ws] if ws is not None else []):
+            t.record_stream(side)
     return dq, dks, dvs

@@ -471,6 +471,25 @@ int bsm_bwd_step_ws(const bsm_dplan* dplan, int32_t s, const bsm_heads* heads,
                     const float* lse, const float* delta, float* dq_acc, float* dk, float* dv,
                     void* workspace, int64_t workspace_bytes, void* stream);
 
+/*
+ * bsm_bwd_step_ws with the step's two updates on two streams: the dQ product
+ * on dq_stream, the dK/dV products (and the split reduction) on kv_stream.
+ * MARBLE section 03 ("Exact ring attention accumulation") carries dQ across
+ * steps in the query rank and sends each key shard's dK/dV along the ring, so
+ * within a step the two updates write different buffers and read only the
+ * step's inputs.  Issuing every step's dQ update on one stream and every
+ * step's dK/dV update on another keeps each chain in step order and lets the
+ * GPU run the two side by side (one fills the CUs the other's tail leaves
+ * idle).  The caller orders q, k, v, dout, lse and delta before both streams
+ * and joins the streams before reading dq_acc, dk or dv.  Results equal
+ * bsm_bwd_step_ws bit for bit.  workspace is used on kv_stream only.  Equal
+ * streams make it bsm_bwd_step_ws.  Other arguments as bsm_bwd_step_ws.
+ */
+int bsm_bwd_step_streams(const bsm_dplan* dplan, int32_t s, const bsm_heads* heads,
+                         const void* q, const void* k, const void* v, const void* dout,
+                         const float* lse, const float* delta, float* dq_acc, float* dk, float* dv,
+                         void* workspace, int64_t workspace_bytes, void* dq_stream, void* kv_stream);
+
 #ifdef __cplusplus
 }
 #endif

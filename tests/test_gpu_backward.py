@@ -178,3 +178,30 @@ def test_split_workspace_too_small_is_refused():
             refused += 1
     torch.cuda.synchronize()
     assert refused > 0
+
+
+@pytest.mark.parametrize("maker", ["packed_text", "random"])
+def test_two_streams_equal_one_stream(maker):
+    """bsm_bwd_step_streams: the dK/dV chain on a second stream gives the
+    one-stream gradients bit for bit (same kernels, same inputs)."""
+    from workloads import packed_text
+    if maker == "packed_text":
+        lay = packed_text()
+    else:
+        rng = np.random.default_rng(91)
+        lay = random_small(rng, 128 * 4 * 2, max_span=300)
+        lay.ranks, lay.order, lay.seed = 4, "ptrr", 17
+        lay.hq, lay.hkv, lay.d = 4, 2, 128
+    case = Case(lay, with_do=True)
+    o, lse, _ = case.ring()
+    one = bsm.bwd_ring(case.dp, case.heads, case.q, case.k_shards, case.v_shards, case.dout, o, lse)
+    two = bsm.bwd_ring(case.dp, case.heads, case.q, case.k_shards, case.v_shards, case.dout, o, lse,
+                       two_streams=True)
+    torch.cuda.synchronize()
+    assert torch.equal(one[0], two[0])
+    for a, b in zip(one[1] + one[2], two[1] + two[2]):
+        assert torch.equal(a, b)
+    if maker == "random":
+        sel = np.arange(case.S)
+        ref = _oracle(case, sel)
+        grad_ok(two[0].cpu().numpy(), ref["dq"], "dq")

@@ -314,7 +314,7 @@ def fit_tau(args, bsm, torch, lay, config_qkv):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "this benchmark measures one GPU; --gpus must be 1"}))
         sys.exit(2)
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
     import torch

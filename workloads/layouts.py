@@ -18,7 +18,7 @@ plus one per-layer scalar W (the sliding window; WINDOW_INF for global layers).
 
 Length draws for packed text follow the heavy-tailed corpus the Libra page
 describes (section 1: median 644 tokens); the lognormal with sigma 1.5 and the
-16384-token cap are the workload recipe of this build.
+16384-token cap complete the recipe (the page gives the median only).
 """
 from __future__ import annotations
 

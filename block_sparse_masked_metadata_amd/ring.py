@@ -338,7 +338,7 @@ def bwd_ring(dp: DevicePlan, hd, q, k_shards, v_shards, dout, o, lse, grads=None
         bwd_step(dp, s, hd, q, k_shards[j], v_shards[j], dout, lse, delta, dq, dks[j], dvs[j], ws,
                  kv_stream=side)
     if side is not None:
+        # joined before returning: whatever reuses these buffers later on the
+        # current stream runs after the side stream's work
         main.wait_stream(side)
-        for t in [delta, dout, q, lse] + list(k_shards) + list(v_shards) + dks + dvs + ([ws] if ws is not None else []):
-            t.record_stream(side)
     return dq, dks, dvs

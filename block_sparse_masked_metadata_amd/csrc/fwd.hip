@@ -88,6 +88,7 @@ __device__ inline int v_slot(int r, int c) { return r * 256 + ((c ^ ((r & 3) << 
 constexpr int kSub = 64;             // keys per sub-tile (half of a listed 128-key tile)
 constexpr int kListCache = 512;      // list entries of an item kept in LDS
 constexpr float kSumCap = 4096.0f;   // a lane sum below 2^12 keeps every p below 2^12
+constexpr int kBufferFlags = 0x00020000;  // buffer descriptor word 3: 32-bit data format, untyped loads
 
 // One sub-tile of K, V (and key tracks) staged through registers: thread t
 // holds chunk t%16 of rows t/16 + 16i (i = 0..3), so every 16 lanes read one
@@ -123,11 +124,15 @@ __device__ inline void fetch_sub(SubTile& t, const char* kbase, const char* vbas
   }
   const uint32_t r0 = (uint32_t)k0 * row_bytes;
   if (len == kSub) {
+    // raw buffer loads: the uniform row offset rides in soffset and the
+    // loop-invariant lane offset in voffset, so no per-load address arithmetic
+    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, 0, 0x7fffffff, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, 0, 0x7fffffff, kBufferFlags);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t ro = r0 + 16u * i * row_bytes;
-      t.k[i] = *(const uint4*)(kbase + ro + lane_off);
-      t.v[i] = *(const uint4*)(vbase + ro + lane_off);
+      t.k[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, lane_off, ro, 0));
+      t.v[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vr, lane_off, ro, 0));
     }
   } else {
 #pragma unroll

@@ -125,9 +125,11 @@ __device__ inline void fetch_sub(SubTile& t, const char* kbase, const char* vbas
   const uint32_t r0 = (uint32_t)k0 * row_bytes;
   if (len == kSub) {
     // raw buffer loads: the uniform row offset rides in soffset and the
-    // loop-invariant lane offset in voffset, so no per-load address arithmetic
-    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, 0, 0x7fffffff, kBufferFlags);
-    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, 0, 0x7fffffff, kBufferFlags);
+    // loop-invariant lane offset in voffset, so no per-load address
+    // arithmetic.  The record count is the full 32-bit range: every byte
+    // offset of a key buffer (under 4 GiB) is in range.
+    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, 0, -1, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, 0, -1, kBufferFlags);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t ro = r0 + 16u * i * row_bytes;

@@ -232,3 +232,31 @@ def test_mfma_probe_reports_a_plausible_rate_and_clock():
     assert pr is not None, "libbsm_probe.so is not built"
     assert 100.0 < pr["tflops"] < 3000.0
     assert 0.5 < pr["clock_ghz"] < 3.0
+
+
+def test_key_rows_past_2gib():
+    """Key and value buffers of 2.5 GiB (1,310,720 tokens x 8 kv heads x 256 B):
+    the full sub-tiles of the last query tiles read rows more than 2 GiB into
+    them.  One sample under a 256-token sliding window, single pass; sampled rows
+    of the last tiles against the oracle on the token slice that holds every key
+    they read (the mask depends on positions and samples only)."""
+    from workloads.layouts import Layout
+    n, h, w = 1310720, 8, 256
+    neg = np.full(n, -1, np.int32)
+    lay = Layout("window_2p5gib", sample=np.zeros(n, np.int32), seg=neg, noise=neg.copy(),
+                 pos=np.arange(n, dtype=np.int32), window=w, ranks=1, order="contiguous",
+                 hq=h, hkv=h, seed=21)
+    case = Case(lay)
+    assert case.k_all.numel() * case.k_all.element_size() > 2 ** 31 + 2 ** 28
+    o, lse = case.single()
+    torch.cuda.synchronize()
+    sel = np.arange(n - 512, n, 7)
+    lo = n - 2048
+    tr = tuple(t[lo:] for t in lay.tracks())
+    q, k, v = (case.full[i][lo:].cpu() for i in range(3))
+    o_ref, lse_ref = oatt.forward_rows(tr, w, q, k, v, sel - lo, 1.0 / np.sqrt(lay.d))
+    tsel = torch.from_numpy(sel).cuda()
+    eo = max_err(o[tsel].float().cpu().numpy(), o_ref)
+    el = max_err(lse[:, tsel].cpu().numpy(), lse_ref)
+    print(f"  rows past 2 GiB of K/V: max|dO|={eo:.3e} max|dLSE|={el:.3e}", flush=True)
+    assert eo <= O_TOL and el <= LSE_TOL

@@ -7,6 +7,7 @@
 #include <algorithm>
 #include <cstdlib>
 #include <cstring>
+#include <initializer_list>
 #include <new>
 #include <string>
 #include <tuple>
@@ -554,6 +555,22 @@ int check_rows(int64_t rows, int32_t heads, const char* what) {
 
 const uint16_t* bf(const void* p) { return (const uint16_t*)p; }
 
+// Tensors the kernels move in 16-byte vectors must be 16-byte aligned; the
+// fp32 row arrays (m, l, LSE, delta) are read per element and need 4 bytes.
+int check_aligned(std::initializer_list<const void*> vec16, std::initializer_list<const void*> row4) {
+  for (const void* p : vec16)
+    if (p && ((uintptr_t)p & 15u)) {
+      set_error("tensor pointer not 16-byte aligned");
+      return BSM_E_INVALID;
+    }
+  for (const void* p : row4)
+    if (p && ((uintptr_t)p & 3u)) {
+      set_error("row array pointer not 4-byte aligned");
+      return BSM_E_INVALID;
+    }
+  return BSM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -839,6 +856,7 @@ int bsm_fwd_step(const bsm_dplan* d, int32_t s, const bsm_heads* heads, const vo
     return BSM_E_INVALID;
   }
   if ((rc = check_rows(d->S, heads->hq, "q")) || (rc = check_rows(d->S, heads->hkv, "k/v"))) return rc;
+  if ((rc = check_aligned({q, k, v, o_acc, o}, {m, l, lse}))) return rc;
   if (d->nf[s] == 0) return BSM_OK;
   const int32_t j = ((d->r - s) % d->R + d->R) % d->R;
   FwdArgs a{};
@@ -891,6 +909,7 @@ int fwd_pass(const bsm_dplan* d, bool fetched, const bsm_heads* heads, const voi
   const int64_t krows = fetched ? d->fetch_rows : (int64_t)d->S * d->R;
   if ((rc = check_rows(d->S, heads->hq, "q")) || (rc = check_rows(krows, heads->hkv, "keys/values")))
     return rc;
+  if ((rc = check_aligned({q, k_all, v_all, o_acc, o}, {m, l, lse}))) return rc;
   const int64_t nitems = fetched ? d->nx : d->ns;
   if (nitems == 0) return BSM_OK;
   FwdArgs a{};
@@ -963,6 +982,7 @@ int bsm_fwd_merge_bf16(const bsm_heads* heads, int64_t rows, void* o_run, float*
   if (rc) return rc;
   if (rows < 1) { set_error("rows must be >= 1"); return BSM_E_INVALID; }
   if (!o_run || !lse_run || !o_s || !lse_s) { set_error("null tensor pointer"); return BSM_E_INVALID; }
+  if ((rc = check_aligned({o_run, o_s}, {lse_run, lse_s}))) return rc;
   hipStream_t st = (hipStream_t)stream;
   return hip_status(launch_merge_bf16(rows, heads->hq, (uint16_t*)o_run, lse_run, bf(o_s), lse_s, st),
                     "bf16 merge launch", st);
@@ -974,6 +994,7 @@ int bsm_fwd_merge_fp32(const bsm_heads* heads, int64_t rows, float* o_run, float
   if (rc) return rc;
   if (rows < 1) { set_error("rows must be >= 1"); return BSM_E_INVALID; }
   if (!o_run || !lse_run || !acc_s || !m_s || !l_s) { set_error("null tensor pointer"); return BSM_E_INVALID; }
+  if ((rc = check_aligned({o_run, acc_s, o_bf16}, {lse_run, m_s, l_s}))) return rc;
   hipStream_t st = (hipStream_t)stream;
   return hip_status(launch_merge_fp32(rows, heads->hq, o_run, lse_run, acc_s, m_s, l_s, (uint16_t*)o_bf16, st),
                     "fp32 merge launch", st);
@@ -984,6 +1005,7 @@ int bsm_state_unpack(const bsm_heads* heads, int64_t rows, const float* o_acc, f
   if (rc) return rc;
   if (rows < 1) { set_error("rows must be >= 1"); return BSM_E_INVALID; }
   if (!o_acc || !out) { set_error("null tensor pointer"); return BSM_E_INVALID; }
+  if ((rc = check_aligned({o_acc, out}, {}))) return rc;
   hipStream_t st = (hipStream_t)stream;
   return hip_status(launch_state_unpack(rows, heads->hq, o_acc, out, st), "state unpack launch", st);
 }
@@ -994,6 +1016,7 @@ int bsm_bwd_prep(const bsm_heads* heads, int64_t rows, const void* o, const void
   if (rc) return rc;
   if (rows < 1) { set_error("rows must be >= 1"); return BSM_E_INVALID; }
   if (!o || !dout || !delta) { set_error("null tensor pointer"); return BSM_E_INVALID; }
+  if ((rc = check_aligned({o, dout}, {delta}))) return rc;
   hipStream_t st = (hipStream_t)stream;
   return hip_status(launch_bwd_prep(rows, heads->hq, bf(o), bf(dout), delta, st), "bwd prep launch", st);
 }
@@ -1022,6 +1045,7 @@ int bwd_step(const bsm_dplan* d, int32_t s, const bsm_heads* heads, const void* 
     return BSM_E_INVALID;
   }
   if ((rc = check_rows(d->S, heads->hq, "q/dout")) || (rc = check_rows(d->S, heads->hkv, "k/v"))) return rc;
+  if ((rc = check_aligned({q, k, v, dout, dq_acc, dk, dv, workspace}, {lse, delta}))) return rc;
   // split the dK/dV work when a workspace is given and the launch would
   // otherwise leave CUs waiting on its longest column lists
   const bool split = workspace && d->nreduce[s] > 0 && d->nb[s] * heads->hkv < busy_blocks();

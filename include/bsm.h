@@ -8,7 +8,8 @@
  *   - Return value: BSM_OK (0) on success, a negative BSM_E_* code otherwise.
  *     No entry point aborts, throws or exits; bsm_last_error() returns a
  *     thread-local description of the most recent failure on that thread.
- *   - Argument and shape errors are reported before anything is launched.
+ *   - Argument and shape errors are reported before anything is launched,
+ *     misaligned tensor pointers among them (BSM_E_INVALID).
  *   - GPU entry points enqueue work on the caller's stream (`stream` is a
  *     hipStream_t; NULL means the default stream) and never synchronize.
  *     Faults inside a kernel surface at the caller's next synchronization;
@@ -17,7 +18,8 @@
  *   - The library never allocates device memory.  Every device buffer is
  *     allocated by the caller, who keeps ownership.  Host plans are owned by
  *     the library and released with bsm_plan_free / bsm_dplan_free.
- *   - Tensor layouts (all contiguous, 16-byte aligned device memory):
+ *   - Tensor layouts (all contiguous device memory, 16-byte aligned; the fp32
+ *     row arrays m, l, LSE and delta need only 4-byte alignment):
  *       Q, O, dO          bf16  [rows, Hq, d]     token-major
  *       K, V              bf16  [keys, Hkv, d]
  *       dQ                fp32  [rows, Hq, d]

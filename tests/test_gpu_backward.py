@@ -205,3 +205,44 @@ def test_two_streams_equal_one_stream(maker):
         sel = np.arange(case.S)
         ref = _oracle(case, sel)
         grad_ok(two[0].cpu().numpy(), ref["dq"], "dq")
+
+
+def _offset_view(t, nbytes):
+    """A copy of `t` whose data pointer sits `nbytes` past a 256-byte boundary."""
+    elems = nbytes // t.element_size()
+    buf = torch.empty(t.numel() + elems, dtype=t.dtype, device=t.device)
+    v = buf[elems:elems + t.numel()].view(t.shape)
+    v.copy_(t)
+    return v
+
+
+def test_misaligned_tensors_are_refused():
+    """A tensor pointer 8 bytes off its 16-byte alignment returns BSM_E_INVALID
+    from the forward and the backward step before anything is launched: the
+    outputs keep their contents."""
+    rng = np.random.default_rng(5)
+    lay = random_small(rng, 128 * 2 * 2, max_span=200)
+    lay.ranks, lay.order, lay.seed = 2, "ptrr", 3
+    lay.hq, lay.hkv, lay.d = 2, 2, 128
+    case = Case(lay, with_do=True)
+    q_bad = _offset_view(case.q, 8)
+    assert q_bad.data_ptr() % 16 == 8
+    state = bsm.new_state(case.S, case.hq, 128)
+    o = torch.full((case.S, case.hq, 128), 7.0, dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((case.hq, case.S), 7.0, dtype=torch.float32, device="cuda")
+    with pytest.raises(bsm.BsmError) as err:
+        bsm.fwd_step(case.dp, 0, case.heads, q_bad, case.k_shards[case.r], case.v_shards[case.r], state, o, lse)
+    assert err.value.code == bsm._capi.BSM_E_INVALID and "16-byte" in str(err.value)
+    o_ok, lse_ok, _ = case.ring()
+    delta = bsm.bwd_prep(case.heads, o_ok, case.dout)
+    dq = torch.full((case.S, case.hq, 128), 7.0, dtype=torch.float32, device="cuda")
+    dq_bad = _offset_view(dq, 8)
+    dk = torch.zeros(case.S, case.hkv, 128, dtype=torch.float32, device="cuda")
+    dv = torch.zeros_like(dk)
+    with pytest.raises(bsm.BsmError) as err:
+        bsm.bwd_step(case.dp, 0, case.heads, case.q, case.k_shards[case.r], case.v_shards[case.r], case.dout,
+                     lse_ok, delta, dq_bad, dk, dv)
+    assert err.value.code == bsm._capi.BSM_E_INVALID
+    torch.cuda.synchronize()
+    assert bool((o == 7.0).all()) and bool((lse == 7.0).all()) and bool((dq_bad == 7.0).all())
+    assert torch.count_nonzero(dk) == 0 and torch.count_nonzero(dv) == 0

@@ -217,17 +217,24 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
   if (!qvalid) return;
   float* out = a.dq + (qrow * a.hq + h) * kHeadDim;
   const bool first = (it.y & kFirst) != 0;
+  // every running value is read before the first store (interleaved, each
+  // load waits for the store before it: one memory round trip per float4)
+  float4 o4[16];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      o4[4 * db + i] = first ? make_float4(0.f, 0.f, 0.f, 0.f) : *(const float4*)(out + db * 32 + i * 8 + hi * 4);
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float* p = out + db * 32 + i * 8 + hi * 4;
-      float4 o4 = first ? make_float4(0.f, 0.f, 0.f, 0.f) : *(const float4*)p;
-      o4.x += a.scale * acc[db][4 * i + 0];
-      o4.y += a.scale * acc[db][4 * i + 1];
-      o4.z += a.scale * acc[db][4 * i + 2];
-      o4.w += a.scale * acc[db][4 * i + 3];
-      *(float4*)p = o4;
+      float4 x = o4[4 * db + i];
+      x.x += a.scale * acc[db][4 * i + 0];
+      x.y += a.scale * acc[db][4 * i + 1];
+      x.z += a.scale * acc[db][4 * i + 2];
+      x.w += a.scale * acc[db][4 * i + 3];
+      *(float4*)(out + db * 32 + i * 8 + hi * 4) = x;
     }
 }
 
@@ -446,24 +453,35 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
       }
     return;
   }
+  // every running value is read before the first store: dk and dv may alias
+  // as far as the compiler knows, so loads interleaved with the stores would
+  // take one memory round trip each
   const int64_t off = (key * a.hkv + g) * kHeadDim;
+  float4 k4[16], v4[16];
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int c = db * 32 + i * 8 + hi * 4;
-      float4 k4 = *(const float4*)(a.dk + off + c);
-      float4 v4 = *(const float4*)(a.dv + off + c);
-      k4.x += a.scale * dk[db][4 * i + 0];
-      k4.y += a.scale * dk[db][4 * i + 1];
-      k4.z += a.scale * dk[db][4 * i + 2];
-      k4.w += a.scale * dk[db][4 * i + 3];
-      v4.x += dv[db][4 * i + 0];
-      v4.y += dv[db][4 * i + 1];
-      v4.z += dv[db][4 * i + 2];
-      v4.w += dv[db][4 * i + 3];
-      *(float4*)(a.dk + off + c) = k4;
-      *(float4*)(a.dv + off + c) = v4;
+      k4[4 * db + i] = *(const float4*)(a.dk + off + c);
+      v4[4 * db + i] = *(const float4*)(a.dv + off + c);
+    }
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = db * 32 + i * 8 + hi * 4;
+      float4 kx = k4[4 * db + i], vx = v4[4 * db + i];
+      kx.x += a.scale * dk[db][4 * i + 0];
+      kx.y += a.scale * dk[db][4 * i + 1];
+      kx.z += a.scale * dk[db][4 * i + 2];
+      kx.w += a.scale * dk[db][4 * i + 3];
+      vx.x += dv[db][4 * i + 0];
+      vx.y += dv[db][4 * i + 1];
+      vx.z += dv[db][4 * i + 2];
+      vx.w += dv[db][4 * i + 3];
+      *(float4*)(a.dk + off + c) = kx;
+      *(float4*)(a.dv + off + c) = vx;
     }
 }
 

@@ -71,9 +71,10 @@ def grad_ok(g, ref, name):
 def check_rows(case, o, lse, sel=None, tol_o=O_TOL, tol_lse=LSE_TOL, single=False):
     """Compare GPU rows (indices into the rank's shard) with the oracle.
 
-    The O bar applies to the value the kernel rounds to bf16 (O_acc / l from a
-    KEEP_STATE run of the same launches); the bf16 output must be exactly that
-    value rounded to nearest even.  LSE is compared as written."""
+    The O bar applies to the value the kernel rounds to bf16 (O_acc times the
+    fp32 reciprocal of l, from a KEEP_STATE run of the same launches); the
+    bf16 output must be exactly that value rounded to nearest even.  LSE is
+    compared as written."""
     sel = np.arange(case.S) if sel is None else np.asarray(sel)
     q, k, v = case.cpu(0), case.cpu(1), case.cpu(2)
     o_ref, lse_ref = oatt.forward_rows(case.lay.tracks(), case.lay.window, q, k, v,
@@ -82,9 +83,10 @@ def check_rows(case, o, lse, sel=None, tol_o=O_TOL, tol_lse=LSE_TOL, single=Fals
     acc, m, l = case.single(keep_state=True) if single else case.ring(keep_state=True)[2]
     acc = bsm.state_rows(case.heads, acc, case.S)[tsel].cpu()
     l = l[:, tsel].cpu().T[:, :, None]
-    o32 = torch.where(l > 0, acc / torch.where(l > 0, l, torch.ones_like(l)), torch.zeros_like(acc))
+    rl = torch.where(l > 0, 1.0 / torch.where(l > 0, l, torch.ones_like(l)), torch.zeros_like(l))
+    o32 = acc * rl
     og = o[tsel].cpu()
-    assert torch.equal(og, o32.to(torch.bfloat16)), "bf16 O is not RNE(O_acc / l)"
+    assert torch.equal(og, o32.to(torch.bfloat16)), "bf16 O is not RNE(O_acc * (1 / l))"
     lg = lse[:, tsel].cpu().numpy()
     eo = max_err(o32.numpy(), o_ref)
     eob = max_err(og.float().numpy(), o_ref)

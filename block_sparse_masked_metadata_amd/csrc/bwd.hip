@@ -92,10 +92,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
   const char* vbase = (const char*)(a.v + (int64_t)kvh * kHeadDim);
   const int nsub = 2 * it.w;
 
-  for (int i = tid; i < it.w && i < kListCache; i += 256) sEnt[i] = a.entries[it.z + i];
   int list_base = 0;
 
-  // prologue: first sub-tile, then Q, dO and the row scalars
+  // prologue: first sub-tile, then Q, dO, the row scalars and the list
+  // window, all issued before anything computes on a loaded value
   PairStage pf;
   int4 kt_pf = make_int4(-1, -1, -1, 0);
   int2 ent = a.entries[it.z];
@@ -125,9 +125,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
     }
   }
   const int64_t sidx = (int64_t)h * a.rows + qrow;
-  const float nlse2 = qvalid ? -a.lse[sidx] * kLog2e : kNegInf;  // invalid rows: p = 0
-  const float dl = qvalid ? a.delta[sidx] : 0.f;
-  const int4 qt = qvalid ? a.qtracks[qrow] : make_int4(0, -1, -1, 0);
+  float lse_raw = 0.f, dl = 0.f;
+  int4 qt = make_int4(0, -1, -1, 0);
+  if (qvalid) {
+    lse_raw = a.lse[sidx];
+    dl = a.delta[sidx];
+    qt = a.qtracks[qrow];
+  }
+  for (int i = tid; i < it.w && i < kListCache; i += 256) sEnt[i] = a.entries[it.z + i];
+  const float nlse2 = qvalid ? -lse_raw * kLog2e : kNegInf;  // invalid rows: p = 0
 
   f32x16 acc[4];  // dQ^T[d = 32db + 8(r/4) + 4hi + r%4][query l32], unscaled
 #pragma unroll
@@ -241,7 +247,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
 // Row scalars and tracks of one 64-row query sub-tile, staged with Q and dO:
 // threads 0..63 carry -LSE*log2(e), 64..127 delta, 128..191 the query tracks.
 struct RowStage {
-  float v;
+  float v;  // LSE (wave 0) or delta (wave 1), raw
   int4 t;
 };
 
@@ -275,7 +281,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
   const int nsub = (wk.z < 0 ? 2 * it.w : wk.z) - n0;
   const int total = grp * nsub;  // (query head of the group, sub-tile) pairs
 
-  for (int i = tid; i < it.w && i < kListCache; i += 256) sEnt[i] = a.entries[it.z + i];
   int list_base = 0;
 
   // Stage (head g*grp + m/nsub, sub-tile m%nsub) into registers.
@@ -290,27 +295,28 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
     int64_t r0;
     sub_bounds(e2, n0 + m % nsub, r0, nxt_len, nxt_partial);
     nxt_ey = e2.y;
+    // Wave 0 loads the LSE rows, wave 1 the delta rows, wave 2 the query
+    // tracks (partial sub-tiles only), raw into registers set beforehand:
+    // nothing computes on a loaded value before stage(), and no register
+    // is written after a load into it is issued, so no wave waits here
+    // before issuing the Q/dO loads.
+    const int row = tid & (kSub - 1);
     rs.v = 0.f;
     rs.t = make_int4(-2, -1, -1, -1);  // rows past len: no sample, no position
-    if (tid < kSub) {
-      rs.v = tid < nxt_len ? -a.lse[(int64_t)h * a.rows + r0 + tid] * kLog2e : kNegInf;
-    } else if (tid < 2 * kSub) {
-      rs.v = tid - kSub < nxt_len ? a.delta[(int64_t)h * a.rows + r0 + tid - kSub] : 0.f;
-    } else if (tid < 3 * kSub) {
-      if (nxt_partial && tid - 2 * kSub < nxt_len) rs.t = a.qtracks[r0 + tid - 2 * kSub];
-    }
+    if (tid < 2 * kSub && row < nxt_len) rs.v = (tid < kSub ? a.lse : a.delta)[(int64_t)h * a.rows + r0 + row];
+    if (tid >= 2 * kSub && tid < 3 * kSub && nxt_partial && row < nxt_len) rs.t = a.qtracks[r0 + row];
     pf.fetch((const char*)(a.q + (int64_t)h * kHeadDim), (const char*)(a.dout + (int64_t)h * kHeadDim),
              r0, nxt_len, row_bytes, tid);
   };
   auto stage = [&](int buf) {
     pf.store(sQ[buf], sO[buf], tid);
-    if (tid < kSub) sL[buf][tid] = rs.v;
+    if (tid < kSub) sL[buf][tid] = tid < nxt_len ? -rs.v * kLog2e : kNegInf;
     else if (tid < 2 * kSub) sD[buf][tid - kSub] = rs.v;
     else if (tid < 3 * kSub) sQT[buf][tid - 2 * kSub] = rs.t;
   };
 
-  ent = a.entries[it.z + (n0 >> 1)];
-  fetch(0, ent);
+  // the unit's K/V rows depend on nothing loaded: issue them before the
+  // list entry and the first query sub-tile that depends on it
   bf16x8 kf[8], vf[8];
   {
     const int64_t off = (key * a.hkv + g) * kHeadDim + hi * 8;
@@ -325,7 +331,24 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
   // this lane's key: its tracks, or its key interval when every key of the
   // tile has one (kKeyInterval); invalid keys admit no query
   const bool kin = (it.y & kKeyInterval) != 0;
-  const int4 kt = kvalid ? key_mask_data(a.ktracks, a.kint, key, kin) : make_int4(-1, -1, -1, 0);
+  // Loaded raw with no value written into these registers afterwards; an
+  // invalid key reads the tile's first row (always present) and is replaced
+  // once every prologue load has landed.
+  const int64_t krow = kvalid ? key : (int64_t)it.x * kTile;
+  int4 kraw;
+  if (kin) {
+    kraw.z = 0;
+    kraw.w = 0;
+    const int2 iv = a.kint[krow];
+    kraw.x = iv.x;
+    kraw.y = iv.y;
+  } else {
+    kraw = a.ktracks[krow];
+  }
+  ent = a.entries[it.z + (n0 >> 1)];
+  fetch(0, ent);
+  for (int i = tid; i < it.w && i < kListCache; i += 256) sEnt[i] = a.entries[it.z + i];
+  const int4 kt = kvalid ? kraw : make_int4(-1, -1, -1, 0);
   f32x16 dk[4], dv[4];  // dK^T / dV^T[d = 32db + 8(r/4) + 4hi + r%4][key]
 #pragma unroll
   for (int db = 0; db < 4; ++db)

@@ -94,46 +94,58 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
 
   int list_base = 0;
 
-  // prologue: first sub-tile, then Q, dO, the row scalars and the list
-  // window, all issued before anything computes on a loaded value
+  // prologue: the first sub-tile, Q, dO, the row scalars, the first key data
+  // and the list window are all issued before anything uses a loaded value,
+  // into registers that nothing else writes, so it takes one memory round
+  // trip.  An invalid query row reads the tile's first row (always present)
+  // and is replaced afterwards; its p is 0 through the -inf LSE.
   PairStage pf;
-  int4 kt_pf = make_int4(-1, -1, -1, 0);
   int2 ent = a.entries[it.z];
-  {
-    int64_t r0;
-    int len;
-    bool part;
-    sub_bounds(ent, 0, r0, len, part);
-    if (kDense) kt_pf.x = INT32_MAX;
-    if (part && tid < len) {
-      if (kDense)
-        kt_pf.x = a.ktracks[r0 + tid].w;
-      else
-        kt_pf = key_mask_data(a.ktracks, a.kint, r0 + tid, (ent.y & kIntervalBit) != 0);
-    }
-    pf.fetch(kbase, vbase, r0, len, row_bytes, tid);
-  }
+  int64_t r0f;
+  int lenf;
+  bool partf;
+  sub_bounds(ent, 0, r0f, lenf, partf);
+  pf.fetch(kbase, vbase, r0f, lenf, row_bytes, tid);
+  const int64_t qr = qvalid ? qrow : (int64_t)it.x * kTile;
   bf16x8 qf[8], df[8];
   {
-    const int64_t off = (qrow * a.hq + h) * kHeadDim + hi * 8;
+    const int64_t off = (qr * a.hq + h) * kHeadDim + hi * 8;
     const unsigned short* qp = (const unsigned short*)a.q + off;
     const unsigned short* dp = (const unsigned short*)a.dout + off;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      qf[kk] = qvalid ? as_bf16x8(*(const uint4*)(qp + kk * 16)) : as_bf16x8(make_uint4(0, 0, 0, 0));
-      df[kk] = qvalid ? as_bf16x8(*(const uint4*)(dp + kk * 16)) : as_bf16x8(make_uint4(0, 0, 0, 0));
+      qf[kk] = as_bf16x8(*(const uint4*)(qp + kk * 16));
+      df[kk] = as_bf16x8(*(const uint4*)(dp + kk * 16));
     }
   }
-  const int64_t sidx = (int64_t)h * a.rows + qrow;
-  float lse_raw = 0.f, dl = 0.f;
-  int4 qt = make_int4(0, -1, -1, 0);
-  if (qvalid) {
-    lse_raw = a.lse[sidx];
-    dl = a.delta[sidx];
-    qt = a.qtracks[qrow];
+  const int64_t sidx = (int64_t)h * a.rows + qr;
+  const float lse_raw = a.lse[sidx], dl_raw = a.delta[sidx];
+  const int4 qt_raw = a.qtracks[qr];
+  const bool kload = partf && lenf > 0, kinterval = (ent.y & kIntervalBit) != 0;
+  int4 kraw;  // an interval fills x and y only
+  if (kload) {
+    const int64_t kr = r0f + (tid < lenf ? tid : lenf - 1);
+    if (kDense) {
+      kraw.x = a.ktracks[kr].w;
+    } else if (kinterval) {
+      const int2 iv = a.kint[kr];
+      kraw.x = iv.x;
+      kraw.y = iv.y;
+    } else {
+      kraw = a.ktracks[kr];
+    }
   }
   for (int i = tid; i < it.w && i < kListCache; i += 256) sEnt[i] = a.entries[it.z + i];
   const float nlse2 = qvalid ? -lse_raw * kLog2e : kNegInf;  // invalid rows: p = 0
+  const float dl = qvalid ? dl_raw : 0.f;
+  const int4 qt = qvalid ? qt_raw : make_int4(0, -1, -1, 0);
+  int4 kt_pf = make_int4(kDense ? INT32_MAX : -1, -1, -1, 0);  // keys past len: sample -1, empty range
+  if (kload && tid < lenf) {
+    if (kDense)
+      kt_pf.x = kraw.x;
+    else
+      kt_pf = kinterval ? make_int4(kraw.x, kraw.y, 0, 0) : kraw;
+  }
 
   f32x16 acc[4];  // dQ^T[d = 32db + 8(r/4) + 4hi + r%4][query l32], unscaled
 #pragma unroll

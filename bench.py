@@ -412,6 +412,8 @@ def main():
     delta = torch.empty(lay.hq, S, dtype=torch.float32, device="cuda")
     bws = bsm.bwd_workspace(dp, hd)  # lets long dK/dV lists split over the GPU
 
+    side = torch.cuda.Stream()
+
     def backward():
         # One rank's backward: delta, then the R steps.  Shard j's dK/dV
         # accumulator travels the ring and arrives holding the other ranks'
@@ -421,9 +423,13 @@ def main():
         bsm.bwd_prep(hd, o, dout, delta)
         dks[r].zero_()
         dvs[r].zero_()
+        # dQ chain on the current stream, dK/dV chain on a second one (each in
+        # step order), joined at the end, as bwd_ring runs them by default
+        side.wait_stream(torch.cuda.current_stream())
         for s in range(R):
             j = (r - s) % R
-            bsm.bwd_step(dp, s, hd, q, ks[j], vs[j], dout, lse, delta, dq, dks[j], dvs[j], bws)
+            bsm.bwd_step(dp, s, hd, q, ks[j], vs[j], dout, lse, delta, dq, dks[j], dvs[j], bws, kv_stream=side)
+        torch.cuda.current_stream().wait_stream(side)
 
     for _ in range(args.warmup):
         forward()

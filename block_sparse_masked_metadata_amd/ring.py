@@ -305,15 +305,16 @@ def bwd_step(dp: DevicePlan, s, hd, q, k, v, dout, lse, delta, dq, dk, dv, works
 
 
 def bwd_ring(dp: DevicePlan, hd, q, k_shards, v_shards, dout, o, lse, grads=None, steps=None,
-             split=True, two_streams=False):
+             split=True, two_streams=True):
     """Backward over ring steps s = 0..R-1.  Returns (dq, dk_shards, dv_shards) in fp32.
 
     dk/dv shards are accumulated (+=) by the kernels: they are cleared here
     first, as the owner of a travelling accumulator would before the first
     contribution.  split: give the steps a workspace so long dK/dV lists can
     be split (bsm_bwd_step_ws).  two_streams: run every step's dK/dV update
-    on a second stream beside the dQ chain (bsm_bwd_step_streams); it pays
-    when a step has fewer (key tile, kv head) units than CUs."""
+    on a second stream beside the dQ chain (bsm_bwd_step_streams), so each
+    kernel's launch tail is filled by the other's work; the gradients are
+    bit-identical either way."""
     import torch
     rows = dp.rows
     _need(dout, torch.bfloat16, (rows, hd.hq, hd.d), "dout")

@@ -194,7 +194,8 @@ def test_two_streams_equal_one_stream(maker):
         lay.hq, lay.hkv, lay.d = 4, 2, 128
     case = Case(lay, with_do=True)
     o, lse, _ = case.ring()
-    one = bsm.bwd_ring(case.dp, case.heads, case.q, case.k_shards, case.v_shards, case.dout, o, lse)
+    one = bsm.bwd_ring(case.dp, case.heads, case.q, case.k_shards, case.v_shards, case.dout, o, lse,
+                       two_streams=False)
     two = bsm.bwd_ring(case.dp, case.heads, case.q, case.k_shards, case.v_shards, case.dout, o, lse,
                        two_streams=True)
     torch.cuda.synchronize()

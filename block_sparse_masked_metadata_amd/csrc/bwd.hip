@@ -526,28 +526,53 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(const BwdArgs a) {
   const int32_t e = (int32_t)blockIdx.x / a.hkv, g = (int32_t)blockIdx.x % a.hkv;
   const int4 rd = a.reduce[e];
-  for (int i = threadIdx.x; i < kTile * kHeadDim / 4; i += 256) {
-    const int row = i / (kHeadDim / 4), c = (i % (kHeadDim / 4)) * 4;
-    const int64_t key = (int64_t)rd.x * kTile + row;
-    if (key >= a.krows) continue;
-    const int64_t off = (key * a.hkv + g) * kHeadDim + c;
-    float4 k4 = *(const float4*)(a.dk + off);
-    float4 v4 = *(const float4*)(a.dv + off);
-    for (int sl = rd.y; sl < rd.y + rd.z; ++sl) {
-      const float* wp = a.ws + ((int64_t)sl * a.hkv + g) * (2 * kTile * kHeadDim) + row * kHeadDim + c;
-      const float4 pk = *(const float4*)wp;
-      const float4 pv = *(const float4*)(wp + kTile * kHeadDim);
-      k4.x += pk.x;
-      k4.y += pk.y;
-      k4.z += pk.z;
-      k4.w += pk.w;
-      v4.x += pv.x;
-      v4.y += pv.y;
-      v4.z += pv.z;
-      v4.w += pv.w;
+  // kU float4 per thread per round, all read before any store: dk and dv may
+  // alias as far as the compiler knows, so a load placed after a store waits
+  // for a memory round trip of its own.  Each element still adds its slots in
+  // slot order.
+  constexpr int kN = kTile * kHeadDim / 4, kU = 4;
+  static_assert(kN % (256 * kU) == 0, "rounds cover the key tile exactly");
+  for (int i0 = threadIdx.x; i0 < kN; i0 += 256 * kU) {
+    float4 k4[kU], v4[kU];
+    int64_t off[kU];
+    bool ok[kU];
+    int rc[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i = i0 + 256 * u, row = i / (kHeadDim / 4), c = (i % (kHeadDim / 4)) * 4;
+      const int64_t key = (int64_t)rd.x * kTile + row;
+      ok[u] = key < a.krows;
+      off[u] = (key * a.hkv + g) * kHeadDim + c;
+      rc[u] = row * kHeadDim + c;
+      k4[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      v4[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (ok[u]) {
+        k4[u] = *(const float4*)(a.dk + off[u]);
+        v4[u] = *(const float4*)(a.dv + off[u]);
+      }
     }
-    *(float4*)(a.dk + off) = k4;
-    *(float4*)(a.dv + off) = v4;
+    for (int sl = rd.y; sl < rd.y + rd.z; ++sl) {
+      const float* wp = a.ws + ((int64_t)sl * a.hkv + g) * (2 * kTile * kHeadDim);
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const float4 pk = *(const float4*)(wp + rc[u]);
+        const float4 pv = *(const float4*)(wp + kTile * kHeadDim + rc[u]);
+        k4[u].x += pk.x;
+        k4[u].y += pk.y;
+        k4[u].z += pk.z;
+        k4[u].w += pk.w;
+        v4[u].x += pv.x;
+        v4[u].y += pv.y;
+        v4[u].z += pv.z;
+        v4[u].w += pv.w;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      if (ok[u]) {
+        *(float4*)(a.dk + off[u]) = k4[u];
+        *(float4*)(a.dv + off[u]) = v4[u];
+      }
   }
 }
 

@@ -4,7 +4,8 @@ One ring rank's share on one gfx950 GPU: a host planner (metadata tracks ->
 exact tile classes + PTRR order), HIP kernels that carry the fp32 online-softmax
 state across ring steps, and backward kernels against the final LSE.  The
 compute lives in libbsm.so (C ABI, include/bsm.h); `_capi` binds it 1:1 and
-`ring` adds torch-facing step loops.  Importing fails if libbsm.so is missing.
+`ring` adds torch-facing step loops.  The first call into the library raises
+ImportError if libbsm.so has not been built (there is no fallback).
 """
 from . import _capi
 from ._capi import BsmError, LIB_PATH

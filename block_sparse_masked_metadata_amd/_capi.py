@@ -2,8 +2,11 @@
 
 Argument marshalling only: host arrays are passed as numpy buffers, device
 buffers as integer addresses, streams as integer hipStream_t handles.  Every
-non-zero status raises BsmError with the library's error text.  Importing this
-module fails loudly (ImportError) when the library has not been built.
+non-zero status raises BsmError with the library's error text.  The library is
+opened at the first call into it (so the package imports, and builds itself,
+from a tree where libbsm.so does not exist yet); that call raises ImportError
+when the library has not been built.  There is no other implementation to fall
+back to.
 """
 from __future__ import annotations
 
@@ -23,10 +26,6 @@ try:
 except ImportError:  # the C ABI itself does not need torch
     pass
 
-if not os.path.exists(LIB_PATH):
-    raise ImportError(f"libbsm.so is not built ({LIB_PATH}); run "
-                      "`python -m block_sparse_masked_metadata_amd.build`")
-_lib = C.CDLL(LIB_PATH)
 
 BSM_OK, BSM_E_INVALID, BSM_E_UNSUPPORTED, BSM_E_NOMEM, BSM_E_HIP = 0, -1, -2, -3, -4
 BSM_WINDOW_INF = 0x7FFFFFFF
@@ -135,10 +134,37 @@ _sig = {
     "bsm_bwd_step_streams": (C.c_int, [_P, C.c_int32, C.POINTER(bsm_heads), _P, _P, _P, _P, _P, _P,
                                        _P, _P, _P, _P, C.c_int64, _P, _P]),
 }
-for _name, (_res, _args) in _sig.items():
-    _fn = getattr(_lib, _name)
-    _fn.restype = _res
-    _fn.argtypes = _args
+
+
+def _open():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libbsm.so is not built ({LIB_PATH}); run "
+                          "`python -m block_sparse_masked_metadata_amd.build`")
+    lib = C.CDLL(LIB_PATH)
+    for name, (res, args) in _sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+class _Library:
+    """libbsm.so, opened (and its signatures declared) on first attribute access."""
+    handle = None
+
+    def __getattr__(self, name):
+        if _Library.handle is None:
+            _Library.handle = _open()
+        return getattr(_Library.handle, name)
+
+
+_lib = _Library()
+
+
+def load():
+    """Open libbsm.so now (ImportError if it is not built); returns the ctypes handle."""
+    _lib.bsm_version
+    return _Library.handle
 
 
 def bsm_last_error() -> str:

@@ -138,7 +138,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
   for (int i = tid; i < it.w && i < kListCache; i += 256) sEnt[i] = a.entries[it.z + i];
   const float nlse2 = qvalid ? -lse_raw * kLog2e : kNegInf;  // invalid rows: p = 0
   const float dl = qvalid ? dl_raw : 0.f;
-  const int4 qt = qvalid ? qt_raw : make_int4(0, -1, -1, 0);
+  const int4 qt = query_tracks(qvalid ? qt_raw : make_int4(0, -1, -1, 0));
   int4 kt_pf = make_int4(kDense ? INT32_MAX : -1, -1, -1, 0);  // keys past len: sample -1, empty range
   if (kload && tid < lenf) {
     if (kDense)
@@ -194,7 +194,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = kc * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-            s[r] = (uint32_t)(sKT[key].x - dlo) < dspan ? s[r] : kNegInf;
+            s[r] = (uint32_t)sKT[key].x - (uint32_t)dlo < dspan ? s[r] : kNegInf;
           }
         }
       } else if (partial && interval) {
@@ -324,7 +324,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
     pf.store(sQ[buf], sO[buf], tid);
     if (tid < kSub) sL[buf][tid] = tid < nxt_len ? -rs.v * kLog2e : kNegInf;
     else if (tid < 2 * kSub) sD[buf][tid - kSub] = rs.v;
-    else if (tid < 3 * kSub) sQT[buf][tid - 2 * kSub] = rs.t;
+    else if (tid < 3 * kSub) sQT[buf][tid - 2 * kSub] = query_tracks(rs.t);
   };
 
   // the unit's K/V rows depend on nothing loaded: issue them before the
@@ -390,7 +390,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int qi = q0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          s[r] = (uint32_t)(sQT[qi].w - dlo) < dspan ? s[r] : kNegInf;
+          s[r] = (uint32_t)sQT[qi].w - (uint32_t)dlo < dspan ? s[r] : kNegInf;
         }
       }
     } else if (partial && kin) {

@@ -28,54 +28,21 @@
 //      permutation.  The output accumulator again holds one query per lane,
 //      so the rescale by exp2(m_old - m_new) is a per-lane scalar.
 
-#include "kernels.hpp"
+#include "tile_common.hpp"
 
 namespace bsm {
 namespace {
 
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
-typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
-typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s16x8;
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-constexpr float kNegInf = -__builtin_inff();
-constexpr float kLn2 = 0.693147180559945309f;
-
-__device__ inline bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
-
-// Two LDS transpose reads -> one 8-element MFMA operand.
-__device__ inline bf16x8 lds_tr8(const unsigned short* p0, const unsigned short* p1) {
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p1);
-  const s16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, both);
-}
-
-// The mask predicate of MARBLE section 01 over per-token tracks (x = sample,
-// y = seg, z = noise, w = pos).  The query's seg is pre-mapped to -2 when it
-// is negative, so seg equality alone means "same span".  pos - pos as an
-// unsigned number is below the window exactly when 0 <= d < window.
-__device__ inline bool legal(const int4 q, const int4 k, int32_t window) {
-  const uint32_t d = (uint32_t)(q.w - k.w);
-  return ((d < (uint32_t)window) | (q.y == k.y)) & ((k.z < 0) | (q.z == k.z)) & (q.x == k.x);
-}
-
-__device__ inline void map_block(int32_t b, int32_t nitems, int32_t hq, int32_t hpx,
-                                 int32_t& item, int32_t& h) {
-  if (hpx > 0) {
-    // blocks are dispatched round-robin over the 8 XCDs: give XCD x the heads
-    // [x*hpx, (x+1)*hpx) so the key/value tiles of a head stay in one L2, and
-    // walk its items in list order (longest first) with its heads inner.
-    const int32_t x = b & 7, i = b >> 3;
-    item = i / hpx;
-    h = x * hpx + i % hpx;
-  } else {
-    item = b / hq;
-    h = b % hq;
-  }
-  if (item >= nitems) item = -1;
-}
+using dev::bf16x8;
+using dev::f32x16;
+using dev::kNegInf;
+using dev::kLn2;
+using dev::kSub;
+using dev::as_bf16x8;
+using dev::lds_tr8;
+using dev::legal;
+using dev::query_tracks;
+using dev::map_block;
 
 // ---- LDS sub-tiles: 64 key rows x 256 B, unpadded, 16-byte chunks XOR-swizzled ----
 // K: chunk c of row r sits in slot c ^ (r & 15), so the MFMA A-operand reads
@@ -85,7 +52,6 @@ __device__ inline void map_block(int32_t b, int32_t nitems, int32_t hq, int32_t 
 __device__ inline int k_slot(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
 __device__ inline int v_slot(int r, int c) { return r * 256 + ((c ^ ((r & 3) << 2)) << 4); }
 
-constexpr int kSub = 64;             // keys per sub-tile (half of a listed 128-key tile)
 constexpr int kListCache = 512;      // list entries of an item kept in LDS
 constexpr float kSumCap = 4096.0f;   // a lane sum below 2^12 keeps every p below 2^12
 constexpr int kBufferFlags = 0x00020000;  // buffer descriptor word 3: 32-bit data format, untyped loads
@@ -211,7 +177,7 @@ __device__ inline void scores(f32x16 (&s)[2], const char* sK, const bf16x8 (&qf)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          s[kb][r] = (uint32_t)(sKT[key].x - dlo) < dspan ? s[kb][r] : kNegInf;
+          s[kb][r] = (uint32_t)sKT[key].x - (uint32_t)dlo < dspan ? s[kb][r] : kNegInf;
         }
     }
   } else if (partial && interval) {
@@ -307,8 +273,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a) {
     for (int kk = 0; kk < 8; ++kk)
       qf[kk] = qvalid ? as_bf16x8(*(const uint4*)(qp + kk * 16)) : as_bf16x8(make_uint4(0, 0, 0, 0));
   }
-  int4 qt = qvalid ? a.qtracks[qrow] : make_int4(0, -1, -1, 0);
-  if (qt.y < 0) qt.y = -2;  // a query outside every span matches no key's seg
+  const int4 qt = query_tracks(qvalid ? a.qtracks[qrow] : make_int4(0, -1, -1, 0));
 
   // Running state.  acc[db][r] = O^T[d = 32db + 8(r/4) + 4hi + r%4][query l32];
   // mref is the base-2 reference the accumulator and l are scaled against.
@@ -431,7 +396,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a) {
       for (int db = 0; db < 4; ++db) {
         const char* p0 = sV + v_slot(r0, 4 * db + tr_chunk) + tr_off8;
         const char* p1 = sV + v_slot(r0 + 8, 4 * db + tr_chunk) + tr_off8;
-        vf[db] = lds_tr8((const unsigned short*)p0, (const unsigned short*)p1);
+        vf[db] = lds_tr8(p0, p1);
       }
       __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);  // 8 transpose reads
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);  // then 4 MFMAs

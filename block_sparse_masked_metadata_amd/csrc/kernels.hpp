@@ -39,7 +39,11 @@ enum : int32_t { kRelFull = 0, kRelCausal = 1, kRelReverse = 2, kRelPastWindow =
 
 // Dense-call masks as one range per lane (branch-free: a branch on the
 // relation splits the kernels' loops and costs registers).  Positions lie in
-// [0, 2^31 - 1) and 1 <= window <= 2^31 - 1, so nothing below overflows.
+// [0, 2^31 - 1) and 1 <= window <= 2^31 - 1, so the signed arithmetic below
+// does not overflow.  A lane tests a position x with the unsigned difference
+// (uint32_t)x - (uint32_t)lo < span (modulo 2^32, well defined also for
+// lo = INT32_MIN); the pad position INT32_MAX of keys past a ragged tile's
+// valid rows lies outside every range, since no range reaches 2^31 - 1.
 // Query lane (forward, dQ): the key positions legal for query row `row` of
 // its tile at position pq under entry word y are [lo, lo + span).
 __device__ inline void dense_range(int32_t y, int row, int32_t pq, int32_t window, int32_t& lo, uint32_t& span) {

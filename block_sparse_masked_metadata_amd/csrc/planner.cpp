@@ -117,6 +117,9 @@ int validate(const bsm_plan_desc& d) {
     return BSM_E_INVALID;
   }
   for (int64_t i = 0; i < d.n; ++i) {
+    // The kernels give rows and keys past a ragged tile's valid rows sample id
+    // -1, which must equal no real sample.
+    if (d.sample[i] < 0) { set_error("sample ids must be >= 0"); return BSM_E_INVALID; }
     if (d.seg[i] < -1 || d.noise[i] < -1) { set_error("seg and noise ids must be >= -1"); return BSM_E_INVALID; }
     if (d.pos[i] < 0) { set_error("pos must be >= 0"); return BSM_E_INVALID; }
     if (i > 0) {

@@ -34,14 +34,20 @@ __device__ inline bf16x8 lds_tr8(const char* p0, const char* p1) {
   return __builtin_bit_cast(bf16x8, both);
 }
 
-// The mask predicate of MARBLE section 01 over per-token tracks
-// (x = sample, y = seg, z = noise, w = pos).
+// The mask predicate of MARBLE section 01 over per-token tracks (x = sample,
+// y = seg, z = noise, w = pos).  The query side must come through
+// query_tracks(): a negative query seg becomes -2, which no key seg (>= -1)
+// equals, so seg equality alone means "same span" (seg_q == seg_k >= 0).
+// Positions lie in [-1, 2^31 - 1) (-1 only on pad rows), so pos_q - pos_k
+// does not overflow, and as an unsigned number it is below the window
+// exactly when 0 <= pos_q - pos_k < window.
+__device__ inline int4 query_tracks(int4 q) {
+  q.y = q.y < 0 ? -2 : q.y;
+  return q;
+}
 __device__ inline bool legal(const int4 q, const int4 k, int32_t window) {
-  const int32_t d = q.w - k.w;
-  const bool causal = (d >= 0) & (d < window);
-  const bool span = (q.y == k.y) & (k.y >= 0);
-  const bool keep = (k.z < 0) | (q.z == k.z);
-  return (causal | span) & keep & (q.x == k.x);
+  const uint32_t d = (uint32_t)(q.w - k.w);
+  return ((d < (uint32_t)window) | (q.y == k.y)) & ((k.z < 0) | (q.z == k.z)) & (q.x == k.x);
 }
 
 // Workgroup -> (list item, head).  Workgroups are dispatched round-robin over

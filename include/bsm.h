@@ -92,7 +92,9 @@ typedef struct bsm_plan bsm_plan;
 /*
  * Per-token metadata of one packed sequence, in its ORIGINAL order
  * (MARBLE section 01, the four tracks and the mask_mod code block):
- *   sample[i]  sample id; each sample is one contiguous run, ids non-decreasing
+ *   sample[i]  sample id >= 0; each sample is one contiguous run, ids
+ *              non-decreasing (a negative id is BSM_E_INVALID: padding tokens
+ *              need a sample id of their own)
  *   seg[i]     id of the bidirectional span / group, -1 for causal tokens
  *   noise[i]   id of the generated (noise) span, -1 otherwise
  *   pos[i]     original position, strictly increasing, >= 0

@@ -127,6 +127,9 @@ def test_invalid_metadata_errors():
     bad_cases.append((good[:3] + [p], WINDOW_INF, 2, "ptrr"))            # pos not increasing
     g = good[1].copy(); g[0] = -2
     bad_cases.append(([good[0], g] + good[2:], WINDOW_INF, 2, "ptrr"))  # seg < -1
+    s = good[0].copy(); s[:100] = -1
+    bad_cases.append(([s] + good[1:], WINDOW_INF, 2, "ptrr"))           # negative sample id
+    bad_cases.append(([s] + good[1:], WINDOW_INF, 2, "contiguous"))     # (kernels pad with -1)
     bad_cases.append((good, 0, 2, "ptrr"))                                # window < 1
     bad_cases.append((good, WINDOW_INF, 3, "ptrr"))                       # n % (128*R) != 0
     bad_cases.append((good, WINDOW_INF, 3, "contiguous"))                 # n % R != 0

@@ -187,18 +187,29 @@ def test_fwd_errors_before_launch():
                          case.v_all.data_ptr(), None, None, None, case.q.data_ptr(),
                          case.q.data_ptr(), 0, None)
     assert e.value.code == C.BSM_E_UNSUPPORTED
+    acc, m, l = bsm.new_state(case.S, case.hq, 128)
+    o, lse = torch.empty_like(case.q), torch.empty_like(m)
+    ptrs = [t.data_ptr() for t in (case.q, case.k_shards[0], case.v_shards[0], acc, m, l, o, lse)]
     with pytest.raises(bsm.BsmError) as e:
-        C.bsm_fwd_step(case.dp.handle, 99, case.heads, 1, 1, 1, 1, 1, 1, 1, 1, 0, None)
+        C.bsm_fwd_step(case.dp.handle, 99, case.heads, *ptrs, 0, None)
     assert e.value.code == C.BSM_E_INVALID
-    # 4096 x 4096 heads x 256 B = 4 GiB per key tensor: refused before any launch
-    # (the pointers are never dereferenced)
+    # 4096 shard rows x 4096 heads x 256 B = 4 GiB per bf16 tensor: refused before
+    # any launch.  The buffers are real and as large as such a call would address,
+    # so nothing would fault even if the refusal went missing.
     big = bsm.heads(4096, 4096)
-    for fn in (lambda: C.bsm_fwd_step(case.dp.handle, 0, big, 1, 1, 1, 1, 1, 1, 1, 1, 0, None),
-               lambda: C.bsm_bwd_step(case.dp.handle, 0, big, 1, 1, 1, 1, 1, 1, 1, 1, 1, None)):
+    bf = torch.empty(case.S * 4096 * 128, dtype=torch.bfloat16, device="cuda")
+    f32 = torch.empty(case.S * 4096 * 128, dtype=torch.float32, device="cuda")
+    rowf = torch.empty(4096 * case.S, dtype=torch.float32, device="cuda")
+    B, F, W = bf.data_ptr(), f32.data_ptr(), rowf.data_ptr()
+    for fn in (lambda: C.bsm_fwd_step(case.dp.handle, 0, big, B, B, B, F, W, W, B, W, 0, None),
+               lambda: C.bsm_bwd_step(case.dp.handle, 0, big, B, B, B, B, W, W, F, F, F, None)):
         with pytest.raises(bsm.BsmError) as e:
             fn()
         assert e.value.code == C.BSM_E_UNSUPPORTED
         assert "4 GiB" in str(e.value)
+    del bf, f32, rowf
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
 
 
 def test_state_unpack_channel_order():

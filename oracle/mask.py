@@ -24,15 +24,18 @@ def legal(q_tracks, k_tracks, window: int) -> np.ndarray:
     """Boolean matrix [nq, nk]: may query i attend key j.
 
     q_tracks, k_tracks: tuples (sample, seg, noise, pos) of int arrays.
+    Evaluated with torch's CPU integer ops (threaded) on int32 copies of the
+    tracks; the result is a numpy bool array.
     """
-    qs, qg, qn, qp = (np.asarray(a, np.int32)[:, None] for a in q_tracks)
-    ks, kg, kn, kp = (np.asarray(a, np.int32)[None, :] for a in k_tracks)
+    import torch
+    qs, qg, qn, qp = (torch.from_numpy(np.ascontiguousarray(a, np.int32))[:, None] for a in q_tracks)
+    ks, kg, kn, kp = (torch.from_numpy(np.ascontiguousarray(a, np.int32))[None, :] for a in k_tracks)
     diff = qp - kp          # positions are non-negative int32: no overflow
-    causal = (diff >= 0) & (diff < np.int32(min(int(window), 0x7FFFFFFF)))
+    causal = (diff >= 0) & (diff < min(int(window), 0x7FFFFFFF))
     same_span = (qg == kg) & (kg >= 0)
     keep_noise = (kn < 0) | (qn == kn)
     same_sample = qs == ks
-    return (causal | same_span) & keep_noise & same_sample
+    return ((causal | same_span) & keep_noise & same_sample).numpy()
 
 
 def take(tracks, idx):

@@ -176,9 +176,3 @@ def build(tracks, window: int, ranks: int, block: int = 128, order: str = "ptrr"
                       tiles_new=np.asarray(tiles_new, np.int64), owner=owner, local=local,
                       cost=cost, pairs_k=ks, pairs_c=cs, perm=perm)
 
-
-def unmasked_flops(pairs: int, hq: int, d: int, backward: bool = False) -> int:
-    """4*d*Hq FLOPs per legal pair forward (QK^T and PV, two multiply-adds per
-    pair and channel, as the ring-attention explainer counts a dense step), and
-    10*d*Hq for the backward (QK^T recompute plus the dV, dP, dQ and dK products)."""
-    return (10 if backward else 4) * d * hq * int(pairs)

@@ -110,3 +110,29 @@ def test_layout_invariance():
     o2, l2 = attention.attention_fp64(q[p.perm][inv[rows]], k[p.perm], v[p.perm], allowed, 0.3)
     np.testing.assert_allclose(o1, o2, atol=1e-12)
     np.testing.assert_allclose(l1, l2, atol=1e-12)
+
+
+def test_legal_counts_closed_forms():
+    """legal_counts (the checker of the GPU zero-query test) against counts
+    that follow from the layouts' structure alone: a causal text document
+    gives query i of a document starting at a exactly i - a + 1 keys; a clip
+    under the sliding window sees its whole clip, plus the last W - 1 - t keys
+    of the previous clip of its document at offset t < W - 1 in the clip."""
+    from workloads import sliding_window
+    lay = packed_text()
+    rng = np.random.default_rng(4)
+    rows = np.sort(rng.choice(lay.n, 300, replace=False))
+    start = {}
+    for a, b, mode, sid in lay.spans:
+        assert mode == "causal"
+        start[sid] = a
+    want = rows - np.array([start[int(lay.sample[t])] for t in rows]) + 1
+    assert np.array_equal(attention.legal_counts(lay.tracks(), lay.window, rows), want)
+    clip, w = 2048, 512
+    lay = sliding_window(n=16384, clip=clip, window=w)
+    rows = np.concatenate([np.arange(0, 2 * clip, 97), np.arange(clip, clip + w + 3),
+                           rng.choice(lay.n, 200, replace=False)])
+    c, t = rows // clip, rows % clip
+    prev_same_doc = (c % 4) != 0
+    want = clip + np.where(prev_same_doc, np.maximum(0, w - 1 - t), 0)
+    assert np.array_equal(attention.legal_counts(lay.tracks(), lay.window, rows), want)

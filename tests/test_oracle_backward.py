@@ -23,7 +23,8 @@ def test_finite_differences(seed):
     do = rng.standard_normal((n, hq, d))
     rows = np.sort(rng.choice(n, size=n // 2, replace=False))
     scale = 0.37
-    g = backward.backward_rows(tr, lay.window, q, k, v, do, rows, scale)
+    # chunks of 5 rows: every chunk's key restriction is exercised
+    g = backward.backward_rows(tr, lay.window, q, k, v, do, rows, scale, chunk=5)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
     for a, b, dkb, dvb in g["dkv"]:
@@ -55,7 +56,7 @@ def test_delta_and_unread_keys():
     v = rng.standard_normal((n, 1, 4))
     do = rng.standard_normal((n, 2, 4))
     rows = np.arange(0, n, 2)
-    g = backward.backward_rows(tr, lay.window, q, k, v, do, rows, 0.5)
+    g = backward.backward_rows(tr, lay.window, q, k, v, do, rows, 0.5, chunk=4)
     np.testing.assert_allclose(g["delta"], (g["o"] * do[rows]).sum(-1).T, atol=1e-13)
     from oracle.mask import legal, take
     m = legal(take(tr, rows), tr, lay.window)
@@ -80,7 +81,7 @@ def test_key_sum_identities(seed):
     v = rng.standard_normal((n, hkv, d))
     do = rng.standard_normal((n, hq, d))
     rows = np.sort(rng.choice(n, size=2 * n // 3, replace=False))
-    g = backward.backward_rows(tr, lay.window, q, k, v, do, rows, 0.61)
+    g = backward.backward_rows(tr, lay.window, q, k, v, do, rows, 0.61, chunk=7)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
     for a, b, dkb, dvb in g["dkv"]:
@@ -93,3 +94,23 @@ def test_key_sum_identities(seed):
     np.testing.assert_allclose(dv.sum(0), want, rtol=0, atol=1e-11)
     np.testing.assert_allclose(dk.sum(0), 0.0, rtol=0, atol=1e-11)
     assert np.abs(dk).max() > 1e-2                           # the identity is not vacuous
+
+
+def test_forward_terms_match_the_forward_oracle():
+    """O and LSE that the backward evaluates (chunked, keys restricted) equal
+    the forward oracle's (numpy, all keys of each sample) to fp64 rounding."""
+    rng = np.random.default_rng(12)
+    lay = random_small(rng, 200, max_span=60)
+    tr = lay.tracks()
+    n = lay.n
+    q = rng.standard_normal((n, 4, 8))
+    k = rng.standard_normal((n, 2, 8))
+    v = rng.standard_normal((n, 2, 8))
+    do = rng.standard_normal((n, 4, 8))
+    rows = np.sort(rng.choice(n, size=150, replace=False))
+    g = backward.backward_rows(tr, lay.window, q, k, v, do, rows, 0.3, chunk=9)
+    o, lse = attention.forward_rows(tr, lay.window, q, k, v, rows, 0.3)
+    np.testing.assert_allclose(g["o"], o, rtol=0, atol=1e-12)
+    fin = np.isfinite(lse)
+    assert np.array_equal(np.isfinite(g["lse"]), fin)
+    np.testing.assert_allclose(g["lse"][fin], lse[fin], rtol=0, atol=1e-12)

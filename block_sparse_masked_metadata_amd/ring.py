@@ -227,14 +227,20 @@ def gather_fetched(plan: Plan, r: int, k_all, v_all):
     return k_all.index_select(0, src), v_all.index_select(0, src)
 
 
-def fwd_fetched(dp: DevicePlan, hd, q, k_fetch, v_fetch, out=None):
-    """One pass over the rank's shard and its fetched remote tiles."""
+def fwd_fetched(dp: DevicePlan, hd, q, k_fetch, v_fetch, out=None, keep_state=False):
+    """One pass over the rank's shard and its fetched remote tiles.
+    keep_state: return the unnormalized state (O_acc, m, l) instead of (o, lse)."""
     import torch
     rows = dp.rows
     _need(q, torch.bfloat16, (rows, hd.hq, hd.d), "q")
     fr = dp.info["fetch_rows"]
     _need(k_fetch, torch.bfloat16, (fr, hd.hkv, hd.d), "k_fetch")
     _need(v_fetch, torch.bfloat16, (fr, hd.hkv, hd.d), "v_fetch")
+    if keep_state:
+        state = new_state(rows, hd.hq, hd.d, q.device)
+        C.bsm_fwd_fetched(dp.handle, hd, _ptr(q), _ptr(k_fetch), _ptr(v_fetch), *(_ptr(t) for t in state),
+                          None, None, C.BSM_FWD_KEEP_STATE, _stream())
+        return state
     if out is None:
         out = (torch.empty(rows, hd.hq, hd.d, dtype=torch.bfloat16, device=q.device),
                torch.empty(hd.hq, rows, dtype=torch.float32, device=q.device))

@@ -68,19 +68,22 @@ def grad_ok(g, ref, name):
     return err
 
 
-def check_rows(case, o, lse, sel=None, tol_o=O_TOL, tol_lse=LSE_TOL, single=False):
+def check_rows(case, o, lse, sel=None, tol_o=O_TOL, tol_lse=LSE_TOL, single=False, state=None):
     """Compare GPU rows (indices into the rank's shard) with the oracle.
 
     The O bar applies to the value the kernel rounds to bf16 (O_acc times the
     fp32 reciprocal of l, from a KEEP_STATE run of the same launches); the
     bf16 output must be exactly that value rounded to nearest even.  LSE is
-    compared as written."""
+    compared as written.  state: the KEEP_STATE (O_acc, m, l) of the launches
+    that wrote o and lse, when neither the ring nor the single pass did."""
     sel = np.arange(case.S) if sel is None else np.asarray(sel)
     q, k, v = case.cpu(0), case.cpu(1), case.cpu(2)
     o_ref, lse_ref = oatt.forward_rows(case.lay.tracks(), case.lay.window, q, k, v,
                                        case.rows[sel], 1.0 / np.sqrt(case.lay.d))
     tsel = torch.from_numpy(sel).cuda()
-    acc, m, l = case.single(keep_state=True) if single else case.ring(keep_state=True)[2]
+    if state is None:
+        state = case.single(keep_state=True) if single else case.ring(keep_state=True)[2]
+    acc, m, l = state
     acc = bsm.state_rows(case.heads, acc, case.S)[tsel].cpu()
     l = l[:, tsel].cpu().T[:, :, None]
     rl = torch.where(l > 0, 1.0 / torch.where(l > 0, l, torch.ones_like(l)), torch.zeros_like(l))

@@ -137,6 +137,98 @@ def fwd_algorithmic_bytes(plan, r, R, S, hq, hkv, d, single=False):
     return out
 
 
+def bwd_algorithmic(plan, r, R, S, hq, hkv, d):
+    """Per backward step with work: legal pairs and the HBM bytes each kernel
+    must move, from the plan's tile maps.
+
+    bwd_dq (per query tile with work): Q and dO (4*d*Hq per row), LSE and
+    delta (8*Hq), the fp32 dQ written (4*d*Hq) and read unless it is the tile's
+    first step with work, and K and V of the key tiles in its lists (4*d*Hkv
+    per key).  bwd_dkdv (per key tile with work): K and V (4*d*Hkv per key),
+    the shard's fp32 dK and dV read and written (16*d*Hkv per key), and Q, dO,
+    LSE and delta of the query tiles in its lists ((4*d + 8)*Hq per row)."""
+    T = plan.info["tiles_per_shard"]
+    rows = np.minimum(128, S - 128 * np.arange(T)).astype(np.int64)
+    maps = [plan.step_map(r, s) for s in range(R)]
+    act = np.array([(mp > 0).any(axis=1) for mp, _ in maps])   # [R, T] query tiles with work
+    has = act.any(axis=0)
+    first = np.where(has, act.argmax(axis=0), -1)
+    out = []
+    for s in range(R):
+        mp, pairs = maps[s]
+        qa = act[s]
+        if not qa.any():
+            continue
+        ka = (mp > 0).any(axis=0)                               # key tiles with work
+        qrows, krows = int(rows[qa].sum()), int(rows[ka].sum())
+        dq = qrows * ((4 * d + 8) * hq + 4 * d * hq) + int(rows[qa & (first != s)].sum()) * 4 * d * hq \
+            + krows * 4 * d * hkv
+        dkdv = krows * (4 * d * hkv + 16 * d * hkv) + qrows * (4 * d + 8) * hq
+        out.append({"step": s, "pairs": int(pairs), "dq_bytes": dq, "dkdv_bytes": dkdv})
+    return out
+
+
+def kernel_line(flops, nbytes, us, launches, credited=None):
+    """Roofline of one kernel from its per-launch algorithmic work and its
+    average launch duration: bound by the longer of the MFMA and HBM times."""
+    t_mfma = flops / (PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+    tf = flops / (us * 1e-6) / 1e12
+    gbs = nbytes / (us * 1e-6) / 1e9
+    if t_hbm > t_mfma:
+        bound, achieved, peak, unit = "hbm", gbs, PEAK_HBM_GBS, "GB/s"
+    else:
+        bound, achieved, peak, unit = "mfma", tf, PEAK_BF16_TFLOPS, "TFLOP/s"
+    line = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "algorithmic_bytes": int(nbytes),
+            "executed_flops": int(flops), "avg_launch_us": round(us, 2), "launches_per_step": launches,
+            "mfma_tflops": round(tf, 2), "hbm_gbs": round(gbs, 1)}
+    if credited is not None:
+        line["credited_flops"] = int(credited)
+    return line
+
+
+def pass_rates(bsm, torch, hd, S, hq, d, reps=20):
+    """HBM rate of the elementwise passes on the share's shape (untimed by the
+    headline): the two accuracy-control merges of a ring step, with every row
+    reached.  Algorithmic bytes: merge_bf16 reads O_run, O_s (bf16) and both
+    LSEs and writes O_run and LSE_run: (6*d + 12)*Hq per row; merge_fp32 reads
+    O_run (fp32), the step's O_acc, m, l and LSE_run and writes O_run and
+    LSE_run: (12*d + 16)*Hq per row."""
+    C = bsm._capi
+    st = torch.cuda.current_stream().cuda_stream
+    g = torch.Generator(device="cuda").manual_seed(1)
+    o_run = torch.randn(S, hq, d, device="cuda", generator=g).to(torch.bfloat16)
+    o_s = torch.randn(S, hq, d, device="cuda", generator=g).to(torch.bfloat16)
+    lse_run = torch.zeros(hq, S, device="cuda")
+    lse_s = torch.zeros(hq, S, device="cuda")
+    acc, m, l = bsm.new_state(S, hq, d)
+    acc.normal_(generator=g)
+    m.zero_()
+    l.fill_(1.0)
+    o32 = torch.randn(S, hq, d, device="cuda", generator=g)
+    calls = {
+        "merge_bf16": ((6 * d + 12) * hq * S, lambda: C.bsm_fwd_merge_bf16(
+            hd, S, o_run.data_ptr(), lse_run.data_ptr(), o_s.data_ptr(), lse_s.data_ptr(), st)),
+        "merge_fp32": ((12 * d + 16) * hq * S, lambda: C.bsm_fwd_merge_fp32(
+            hd, S, o32.data_ptr(), lse_run.data_ptr(), acc.data_ptr(), m.data_ptr(), l.data_ptr(), None, st)),
+    }
+    out = {}
+    for name, (nbytes, fn) in calls.items():
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        out[name] = {"algorithmic_bytes": int(nbytes), "avg_launch_us": round(us, 2),
+                     "hbm_gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+                     "frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+    return out
+
+
 def sparse_fetch_summary(lay, plan, r):
     """Remote key tiles the measured rank needs under this plan's order and
     under contiguous chunks (MARBLE section 04: the sparse all-to-all moves only
@@ -410,26 +502,47 @@ def main():
                 events[-1].record()
 
     delta = torch.empty(lay.hq, S, dtype=torch.float32, device="cuda")
+    bwd_work = bwd_algorithmic(plan, r, R, S, lay.hq, lay.hkv, d)
+    bwd_steps = {w["step"] for w in bwd_work}
     bws = bsm.bwd_workspace(dp, hd)  # lets long dK/dV lists split over the GPU
 
     side = torch.cuda.Stream()
 
-    def backward():
+    def event(stream=None):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        return e
+
+    def backward(events=None):
         # One rank's backward: delta, then the R steps.  Shard j's dK/dV
         # accumulator travels the ring and arrives holding the other ranks'
         # contributions; only the rank's own shard (j = r) starts from zero
         # here, so the others keep accumulating across timed passes (their
         # values are not checked; the kernels do the same work either way).
+        # events: per-launch events of the prep and of every step, each on
+        # the stream its kernels run on (the dQ launch alone on the current
+        # stream, the dK/dV launch (and its split reduction) alone on `side`).
+        main = torch.cuda.current_stream()
+        if events is not None:
+            events["prep"].append(event())
         bsm.bwd_prep(hd, o, dout, delta)
+        if events is not None:
+            events["prep"].append(event())
         dks[r].zero_()
         dvs[r].zero_()
         # dQ chain on the current stream, dK/dV chain on a second one (each in
         # step order), joined at the end, as bwd_ring runs them by default
-        side.wait_stream(torch.cuda.current_stream())
+        side.wait_stream(main)
         for s in range(R):
             j = (r - s) % R
+            if events is not None and s in bwd_steps:
+                events["dq"].append(event())
+                events["dkdv"].append(event(side))
             bsm.bwd_step(dp, s, hd, q, ks[j], vs[j], dout, lse, delta, dq, dks[j], dvs[j], bws, kv_stream=side)
-        torch.cuda.current_stream().wait_stream(side)
+            if events is not None and s in bwd_steps:
+                events["dq"].append(event())
+                events["dkdv"].append(event(side))
+        main.wait_stream(side)
 
     for _ in range(args.warmup):
         forward()
@@ -438,6 +551,7 @@ def main():
     torch.cuda.synchronize()
 
     launch_ev = []
+    bwd_ev = {"prep": [], "dq": [], "dkdv": []}
     marks = []
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -453,7 +567,7 @@ def main():
         f1.record()
         marks.append((f0, f1))
         if do_bwd:
-            backward()
+            backward(bwd_ev if _ == args.steps - 1 else None)
     end = torch.cuda.Event(enable_timing=True)
     end.record()
     torch.cuda.synchronize()
@@ -483,6 +597,30 @@ def main():
         bound, achieved, peak, unit = "hbm", hbm_gbs, PEAK_HBM_GBS, "GB/s"
     else:
         bound, achieved, peak, unit = "mfma", mfma_tflops, PEAK_BF16_TFLOPS, "TFLOP/s"
+
+    bwd_roof = None
+    if do_bwd:
+        def avg_us(ev):
+            return 1e3 * sum(ev[i].elapsed_time(ev[i + 1]) for i in range(0, len(ev), 2)) / (len(ev) // 2)
+        nb = len(bwd_work)
+        bpairs = sum(w["pairs"] for w in bwd_work)
+        prep_bytes = S * lay.hq * (4 * d + 4)
+        prep_us = avg_us(bwd_ev["prep"])
+        bwd_roof = {
+            # executed FLOPs: the dQ kernel recomputes S and dP and forms dQ
+            # (6*d*Hq per pair), the dK/dV kernel recomputes S and dP and forms
+            # dV and dK (8*d*Hq); the metric credits 10*d*Hq for both
+            "bwd_dkdv": kernel_line(8 * d * lay.hq * bpairs / nb, sum(w["dkdv_bytes"] for w in bwd_work) / nb,
+                                    avg_us(bwd_ev["dkdv"]), nb),
+            "bwd_dq": kernel_line(6 * d * lay.hq * bpairs / nb, sum(w["dq_bytes"] for w in bwd_work) / nb,
+                                  avg_us(bwd_ev["dq"]), nb),
+            "bwd_prep": {"bound": "hbm", "algorithmic_bytes": prep_bytes, "avg_launch_us": round(prep_us, 2),
+                         "hbm_gbs": round(prep_bytes / (prep_us * 1e-6) / 1e9, 1),
+                         "frac": round(prep_bytes / (prep_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
+            "credited_flops_per_step": int(bwd_flops),
+            "executed_flops_per_step": int(14 * d * lay.hq * bpairs),
+            "streams": "dQ and dK/dV launches overlap on two streams; each duration is measured on its own stream",
+        }
 
     if args.copy_mib:
         src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device="cuda")
@@ -540,8 +678,11 @@ def main():
         "planner_s": round(plan_s, 4),
         "wall_s": round(wall, 3),
     }
+    if bwd_roof is not None:
+        out["bwd_roofline"] = bwd_roof
     if args.merge != "carry":
         out["roofline"] = None  # the timed forward includes fills and merge kernels
+    out["passes"] = pass_rates(bsm, torch, hd, S, lay.hq, d)
     probe = mfma_probe(torch)
     if probe:
         probe["fwd_frac"] = round(mfma_tflops / probe["tflops"], 4)  # the forward kernel, per launch

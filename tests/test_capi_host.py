@@ -79,6 +79,16 @@ def test_planner_matches_oracle_configs(maker):
     _compare(lay, lay.ranks, 128, lay.order)
 
 
+@pytest.mark.slow
+@pytest.mark.parametrize("maker", [sliding_window, long_mixed], ids=["sliding_window_128k", "long_mixed_1m"])
+def test_planner_matches_oracle_full_size(maker):
+    """The two largest layouts at full size: permutation, per-tile cost and
+    owner, busiest rank, and every rank's step maps and pair counts byte-equal
+    with the enumeration of the oracle planner (minutes of CPU)."""
+    lay = maker()
+    _compare(lay, lay.ranks, 128, lay.order)
+
+
 def test_full_size_closed_forms():
     """Sliding-window 128K and long-mixed 1M layouts: pair totals against closed
     forms, and the window tile map (C++ planner only; the oracle is too slow here)."""

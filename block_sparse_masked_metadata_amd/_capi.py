@@ -46,6 +46,7 @@ EXPORTS = [
     "bsm_fwd_step", "bsm_fwd_single", "bsm_fwd_merge_bf16", "bsm_fwd_merge_fp32",
     "bsm_bwd_prep", "bsm_bwd_step", "bsm_plan_dense_calls", "bsm_dplan_calls_bytes",
     "bsm_dplan_calls_upload", "bsm_state_unpack", "bsm_bwd_step_ws", "bsm_bwd_step_streams",
+    "bsm_bwd_step_noalloc",
 ]
 
 
@@ -133,6 +134,8 @@ _sig = {
                                   _P, _P, _P, _P, C.c_int64, _P]),
     "bsm_bwd_step_streams": (C.c_int, [_P, C.c_int32, C.POINTER(bsm_heads), _P, _P, _P, _P, _P, _P,
                                        _P, _P, _P, _P, C.c_int64, _P, _P]),
+    "bsm_bwd_step_noalloc": (C.c_int, [_P, C.c_int32, C.POINTER(bsm_heads), _P, _P, _P, _P, _P, _P,
+                                       _P, _P, _P, _P]),
 }
 
 
@@ -367,3 +370,8 @@ def bsm_bwd_step_streams(dplan, s, heads, q, k, v, dout, lse, delta, dq_acc, dk,
     _check(_lib.bsm_bwd_step_streams(dplan, int(s), C.byref(heads), q, k, v, dout, lse, delta,
                                      dq_acc, dk, dv, workspace, int(workspace_bytes), dq_stream,
                                      kv_stream))
+
+
+def bsm_bwd_step_noalloc(dplan, s, heads, q, k, v, dout, lse, delta, dq_acc, dk, dv, stream):
+    _check(_lib.bsm_bwd_step_noalloc(dplan, int(s), C.byref(heads), q, k, v, dout, lse, delta,
+                                     dq_acc, dk, dv, stream))

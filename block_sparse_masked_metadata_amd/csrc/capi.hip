@@ -8,6 +8,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <initializer_list>
+#include <mutex>
 #include <new>
 #include <string>
 #include <tuple>
@@ -1033,6 +1034,14 @@ int64_t busy_blocks() {
   return 2 * (int64_t)cus;
 }
 
+// Workspace bytes step s needs when its dK/dV work is split: the split is
+// taken when the plan cut long column lists at that step and the step has
+// fewer (key tile, kv head) units than twice the CUs; 0 otherwise.
+int64_t split_bytes(const bsm_dplan* d, int32_t s, const bsm_heads* heads) {
+  if (d->nreduce[s] == 0 || d->nb[s] * heads->hkv >= busy_blocks()) return 0;
+  return (int64_t)d->slots[s] * heads->hkv * 2 * kTile * kHeadDim * (int64_t)sizeof(float);
+}
+
 int bwd_step(const bsm_dplan* d, int32_t s, const bsm_heads* heads, const void* q, const void* k, const void* v,
              const void* dout, const float* lse, const float* delta, float* dq_acc, float* dk, float* dv,
              void* workspace, int64_t workspace_bytes, void* stream, void* kv_stream) {
@@ -1048,9 +1057,9 @@ int bwd_step(const bsm_dplan* d, int32_t s, const bsm_heads* heads, const void* 
   if ((rc = check_aligned({q, k, v, dout, dq_acc, dk, dv, workspace}, {lse, delta}))) return rc;
   // split the dK/dV work when a workspace is given and the launch would
   // otherwise leave CUs waiting on its longest column lists
-  const bool split = workspace && d->nreduce[s] > 0 && d->nb[s] * heads->hkv < busy_blocks();
+  const int64_t need = workspace ? split_bytes(d, s, heads) : 0;
+  const bool split = need > 0;
   if (split) {
-    const int64_t need = (int64_t)d->slots[s] * heads->hkv * 2 * kTile * kHeadDim * (int64_t)sizeof(float);
     if (workspace_bytes < need) {
       set_error("backward workspace too small: need " + std::to_string(need) + " bytes");
       return BSM_E_INVALID;
@@ -1107,9 +1116,66 @@ int bwd_step(const bsm_dplan* d, int32_t s, const bsm_heads* heads, const void* 
   }
   return rc;
 }
+// Scratch of bsm_bwd_step_noalloc: the split dK/dV partial sums of a step
+// go here instead of into a caller workspace.  Every device the library runs
+// on holds its own copy from the module load until the process ends.  In host
+// code `scratch` names a host-side stand-in, never the device memory: kernels
+// get the address hipGetSymbolAddress returns for the current device.
+constexpr int64_t kScratchBytes = 64ll << 20;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address, looked up on the first call on that
+// device (with the device current) and kept.
+int scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    set_error(std::string("hipGetDevice: ") + hipGetErrorString(e));
+    return BSM_E_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    set_error("device index beyond the scratch table");
+    return BSM_E_UNSUPPORTED;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      set_error(std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+      return BSM_E_HIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return BSM_OK;
+}
 }  // namespace
 
 extern "C" {
+
+int bsm_bwd_step_noalloc(const bsm_dplan* d, int32_t s, const bsm_heads* heads, const void* q, const void* k,
+                         const void* v, const void* dout, const float* lse, const float* delta, float* dq_acc,
+                         float* dk, float* dv, void* stream) {
+  if (!d) { set_error("null device plan"); return BSM_E_INVALID; }
+  int rc = check_heads(heads);
+  if (rc) return rc;
+  if (s < 0 || s >= d->R) { set_error("step out of range"); return BSM_E_INVALID; }
+  const int64_t need = split_bytes(d, s, heads);
+  if (need > kScratchBytes) {
+    set_error("bsm_bwd_step_noalloc: step " + std::to_string(s) + " needs " + std::to_string(need) +
+              " bytes of split-work scratch, the static scratch holds " + std::to_string(kScratchBytes) +
+              "; use bsm_bwd_step_ws with a caller workspace");
+    return BSM_E_UNSUPPORTED;
+  }
+  void* ws = nullptr;
+  if ((rc = scratch_address(&ws))) return rc;
+  return bwd_step(d, s, heads, q, k, v, dout, lse, delta, dq_acc, dk, dv, ws, kScratchBytes, stream, stream);
+}
 
 int bsm_bwd_step(const bsm_dplan* d, int32_t s, const bsm_heads* heads, const void* q,
                  const void* k, const void* v, const void* dout, const float* lse,

@@ -494,6 +494,27 @@ int bsm_bwd_step_streams(const bsm_dplan* dplan, int32_t s, const bsm_heads* hea
                          const float* lse, const float* delta, float* dq_acc, float* dk, float* dv,
                          void* workspace, int64_t workspace_bytes, void* dq_stream, void* kv_stream);
 
+/*
+ * bsm_bwd_step_ws without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The split dK/dV partial sums go to a
+ * static device array of the library, 64 MiB per device, resident from the
+ * library's load until the process ends; its address is looked up once per
+ * device, on the first call with that device current.  The call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine) and writes
+ * every scratch slot it reads within the same call, so no clearing is needed
+ * and nothing carries over between calls.  All calls on one device share the
+ * array: calls that can overlap on one device (other streams, other host
+ * threads without ordering) race and must be serialized by the caller.  A step
+ * whose split needs more than 64 MiB (bwd_workspace_slots * Hkv * 131072
+ * bytes) returns BSM_E_UNSUPPORTED before any launch; bsm_bwd_step_ws takes
+ * such steps.  Arguments and results as bsm_bwd_step_ws on one stream.
+ */
+int bsm_bwd_step_noalloc(const bsm_dplan* dplan, int32_t s, const bsm_heads* heads,
+                         const void* q, const void* k, const void* v, const void* dout,
+                         const float* lse, const float* delta, float* dq_acc, float* dk, float* dv,
+                         void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -66,6 +66,9 @@ def parse():
     ap.add_argument("--fit-tau", action="store_true",
                     help="fit the chunk cost's per-range term: time the ring critical path at "
                          "1, 2, 4, ..., 64 chunks per rank and print one JSON line with the fit")
+    ap.add_argument("--one-stream", action="store_true",
+                    help="backward: the dK/dV launches on the same stream as the dQ launches "
+                         "(counter runs; no per-kernel backward roofline)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
     return ap.parse_args()
@@ -538,7 +541,8 @@ def main():
             if events is not None and s in bwd_steps:
                 events["dq"].append(event())
                 events["dkdv"].append(event(side))
-            bsm.bwd_step(dp, s, hd, q, ks[j], vs[j], dout, lse, delta, dq, dks[j], dvs[j], bws, kv_stream=side)
+            bsm.bwd_step(dp, s, hd, q, ks[j], vs[j], dout, lse, delta, dq, dks[j], dvs[j], bws,
+                         kv_stream=None if args.one_stream else side)
             if events is not None and s in bwd_steps:
                 events["dq"].append(event())
                 events["dkdv"].append(event(side))
@@ -567,7 +571,7 @@ def main():
         f1.record()
         marks.append((f0, f1))
         if do_bwd:
-            backward(bwd_ev if _ == args.steps - 1 else None)
+            backward(bwd_ev if _ == args.steps - 1 and not args.one_stream else None)
     end = torch.cuda.Event(enable_timing=True)
     end.record()
     torch.cuda.synchronize()
@@ -599,7 +603,7 @@ def main():
         bound, achieved, peak, unit = "mfma", mfma_tflops, PEAK_BF16_TFLOPS, "TFLOP/s"
 
     bwd_roof = None
-    if do_bwd:
+    if do_bwd and not args.one_stream:
         def avg_us(ev):
             return 1e3 * sum(ev[i].elapsed_time(ev[i + 1]) for i in range(0, len(ev), 2)) / (len(ev) // 2)
         nb = len(bwd_work)

@@ -46,7 +46,7 @@ EXPORTS = [
     "bsm_fwd_step", "bsm_fwd_single", "bsm_fwd_merge_bf16", "bsm_fwd_merge_fp32",
     "bsm_bwd_prep", "bsm_bwd_step", "bsm_plan_dense_calls", "bsm_dplan_calls_bytes",
     "bsm_dplan_calls_upload", "bsm_state_unpack", "bsm_bwd_step_ws", "bsm_bwd_step_streams",
-    "bsm_bwd_step_noalloc",
+    "bsm_bwd_step_noalloc", "bsm_bwd_fetched", "bsm_fetched_accumulate",
 ]
 
 
@@ -136,6 +136,8 @@ _sig = {
                                        _P, _P, _P, _P, C.c_int64, _P, _P]),
     "bsm_bwd_step_noalloc": (C.c_int, [_P, C.c_int32, C.POINTER(bsm_heads), _P, _P, _P, _P, _P, _P,
                                        _P, _P, _P, _P]),
+    "bsm_bwd_fetched": (C.c_int, [_P, C.POINTER(bsm_heads), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "bsm_fetched_accumulate": (C.c_int, [_P, C.POINTER(bsm_heads), _P, _P, _P, _P, _P]),
 }
 
 
@@ -375,3 +377,12 @@ def bsm_bwd_step_streams(dplan, s, heads, q, k, v, dout, lse, delta, dq_acc, dk,
 def bsm_bwd_step_noalloc(dplan, s, heads, q, k, v, dout, lse, delta, dq_acc, dk, dv, stream):
     _check(_lib.bsm_bwd_step_noalloc(dplan, int(s), C.byref(heads), q, k, v, dout, lse, delta,
                                      dq_acc, dk, dv, stream))
+
+
+def bsm_bwd_fetched(dplan, heads, q, k_fetch, v_fetch, dout, lse, delta, dq, dk_fetch, dv_fetch, stream):
+    _check(_lib.bsm_bwd_fetched(dplan, C.byref(heads), q, k_fetch, v_fetch, dout, lse, delta, dq,
+                                dk_fetch, dv_fetch, stream))
+
+
+def bsm_fetched_accumulate(dplan, heads, dk_fetch, dv_fetch, dk_all, dv_all, stream):
+    _check(_lib.bsm_fetched_accumulate(dplan, C.byref(heads), dk_fetch, dv_fetch, dk_all, dv_all, stream))

@@ -285,8 +285,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
   const int4 it = a.items[wk.x];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, hi = lane >> 5;
-  const int64_t key = (int64_t)it.x * kTile + wave * 32 + l32;
-  const bool kvalid = key < a.krows;
+  const int64_t key = (int64_t)it.x + wave * 32 + l32;  // it.x: the tile's first key row
+  const bool kvalid = wave * 32 + l32 < key_rows(it.y);
   const int32_t grp = a.hq / a.hkv;
   const uint32_t row_bytes = (uint32_t)a.hq * kHeadDim * 2u;
   const int n0 = wk.y;
@@ -346,7 +346,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
   // Loaded raw with no value written into these registers afterwards; an
   // invalid key reads the tile's first row (always present) and is replaced
   // once every prologue load has landed.
-  const int64_t krow = kvalid ? key : (int64_t)it.x * kTile;
+  const int64_t krow = kvalid ? key : (int64_t)it.x;
   int4 kraw;
   if (kin) {
     kraw.z = 0;
@@ -540,8 +540,8 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(const BwdArgs a) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int i = i0 + 256 * u, row = i / (kHeadDim / 4), c = (i % (kHeadDim / 4)) * 4;
-      const int64_t key = (int64_t)rd.x * kTile + row;
-      ok[u] = key < a.krows;
+      const int64_t key = (int64_t)rd.x + row;
+      ok[u] = row < rd.w;
       off[u] = (key * a.hkv + g) * kHeadDim + c;
       rc[u] = row * kHeadDim + c;
       k4[u] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -576,7 +576,41 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(const BwdArgs a) {
   }
 }
 
+// The sparse fetch's way back (MARBLE section 04: the fetched blocks' dK and
+// dV return with the inverse all-to-all and are accumulated in fp32 by their
+// owner): one thread per float4 of a compact row and kv head.  Each shard row
+// appears at most once in the compact buffer, so no two threads add into one
+// element.
+__global__ __launch_bounds__(256) void fetch_accumulate_kernel(const FetchAccArgs a) {
+  const int64_t quads = (int64_t)a.hkv * (kHeadDim / 4);
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (g >= a.rows * quads) return;
+  const int64_t c = g / quads, e = (g % quads) * 4;
+  const int32_t src = a.src[c];
+  if (src < 0) return;
+  const int64_t from = c * a.hkv * kHeadDim + e, to = (int64_t)src * a.hkv * kHeadDim + e;
+  const float4 k = *(const float4*)(a.dk_fetch + from), v = *(const float4*)(a.dv_fetch + from);
+  float4 x = *(const float4*)(a.dk + to), y = *(const float4*)(a.dv + to);
+  x.x += k.x;
+  x.y += k.y;
+  x.z += k.z;
+  x.w += k.w;
+  y.x += v.x;
+  y.y += v.y;
+  y.z += v.z;
+  y.w += v.w;
+  *(float4*)(a.dk + to) = x;
+  *(float4*)(a.dv + to) = y;
+}
+
 }  // namespace
+
+hipError_t launch_fetch_accumulate(const FetchAccArgs& a, hipStream_t stream) {
+  const int64_t threads = a.rows * a.hkv * (kHeadDim / 4);
+  if (threads <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fetch_accumulate_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_bwd_reduce(const BwdArgs& a, hipStream_t stream) {
   const int64_t blocks = (int64_t)a.nreduce * a.hkv;

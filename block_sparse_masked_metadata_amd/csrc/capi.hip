@@ -60,6 +60,8 @@ struct Packed {
   // sparse fetch: one pass over [local shard | needed remote tiles]
   std::vector<int4> xitems, xtracks;
   std::vector<int2> xkint;
+  std::vector<int4> yitems;   // the fetched pass's dK/dV column items (compact key tiles)
+  std::vector<int32_t> xsrc;  // shard row (plan order) of each compact row, -1 for padding
   int64_t fetch_tiles = 0, fetch_rows = 0;
   std::vector<int2> entries;
   // byte offsets in the device buffer
@@ -67,6 +69,7 @@ struct Packed {
   std::vector<int64_t> off_f, off_b, off_ff;  // off_ff: first list entry of each forward item
   std::vector<int64_t> off_w, off_r;         // split dK/dV work units and reduce entries
   int64_t off_s = 0, off_sf = 0, off_x = 0, off_xf = 0, off_xtracks = 0, off_xkint = 0;
+  int64_t off_y = 0, off_xsrc = 0;
 };
 
 static void layout(const Plan& p, Packed& pk);
@@ -92,7 +95,7 @@ static void split_work(StepLists& st) {
       st.bwork.push_back(make_int4(i, 0, n, -1));
       continue;
     }
-    st.breduce.push_back(make_int4(st.bitems[i].x, st.slots, parts - 1, 0));
+    st.breduce.push_back(make_int4(st.bitems[i].x, st.slots, parts - 1, key_rows(st.bitems[i].y)));
     for (int32_t q = 0; q < parts; ++q) {
       const int32_t a0 = (int32_t)((int64_t)n * q / parts), a1 = (int32_t)((int64_t)n * (q + 1) / parts);
       st.bwork.push_back(make_int4(i, a0, a1, q == 0 ? -1 : st.slots++));
@@ -196,8 +199,8 @@ static void pack(const Plan& p, int32_t r, Packed& pk) {
     for (int32_t b = 0; b < T; ++b) {
       if (cols[b].empty()) continue;
       const int32_t jb = ((r - s) % R + R) % R;
-      st.bitems.push_back(make_int4(b, kint_tile(jb, b) ? kKeyInterval : 0, (int32_t)pk.entries.size(),
-                                    (int32_t)cols[b].size()));
+      st.bitems.push_back(make_int4(b * kTile, (kint_tile(jb, b) ? kKeyInterval : 0) | (tlen(b) << kKeyRowsShift),
+                                    (int32_t)pk.entries.size(), (int32_t)cols[b].size()));
       for (auto& ac : cols[b]) {
         const int32_t ql = tlen(ac.first);
         const bool part = ac.second == BSM_TILE_PARTIAL || ql < kTile;
@@ -245,6 +248,7 @@ static void pack(const Plan& p, int32_t r, Packed& pk) {
     pk.fetch_rows = next;
     pk.xtracks.assign(next, make_int4(-1, -1, -1, 0));
     pk.xkint.assign(next, make_int2(0, -1));
+    pk.xsrc.assign(next, -1);
     for (int32_t j = 0; j < R; ++j)
       for (int32_t b = 0; b < T; ++b) {
         const int64_t base = slot[(size_t)j * T + b];
@@ -252,6 +256,7 @@ static void pack(const Plan& p, int32_t r, Packed& pk) {
         for (int32_t i = 0; i < tlen(b); ++i) {
           pk.xtracks[base + i] = pk.tracks[(int64_t)j * S + (int64_t)b * kTile + i];
           pk.xkint[base + i] = pk.kint[(int64_t)j * S + (int64_t)b * kTile + i];
+          pk.xsrc[base + i] = (int32_t)((int64_t)j * S + (int64_t)b * kTile + i);
         }
       }
     pk.xitems.clear();
@@ -271,6 +276,28 @@ static void pack(const Plan& p, int32_t r, Packed& pk) {
       if (cnt) pk.xitems.push_back(make_int4(a, kFirst | kLast, beg, cnt));
     }
     order_items(pk.xitems, qsample);
+    // dK/dV over the compact buffer: per compact key tile, its query tiles
+    // in ascending order (one pass, every step's pairs of that tile)
+    pk.yitems.clear();
+    for (int32_t s = 0; s < R; ++s) {
+      const int32_t j = ((r - s) % R + R) % R;
+      std::vector<std::vector<std::pair<int32_t, uint8_t>>> cols(T);
+      for (int32_t a = 0; a < T; ++a)
+        for (auto& bc : rows[s][a]) cols[bc.first].push_back({a, bc.second});
+      for (int32_t b = 0; b < T; ++b) {
+        if (cols[b].empty()) continue;
+        const int64_t base = slot[(size_t)j * T + b];
+        pk.yitems.push_back(make_int4((int32_t)base,
+                                      (kint_tile(j, b) ? kKeyInterval : 0) | (tlen(b) << kKeyRowsShift),
+                                      (int32_t)pk.entries.size(), (int32_t)cols[b].size()));
+        for (auto& ac : cols[b]) {
+          const int32_t ql = tlen(ac.first);
+          const bool part = ac.second == BSM_TILE_PARTIAL || ql < kTile;
+          pk.entries.push_back(make_int2(ac.first * kTile, ql | (part ? kPartialBit : 0)));
+        }
+      }
+    }
+    std::stable_sort(pk.yitems.begin(), pk.yitems.end(), by_len);
   }
 
   layout(p, pk);
@@ -314,6 +341,10 @@ static void layout(const Plan& p, Packed& pk) {
   off = align256(off + pk.fetch_rows * (int64_t)sizeof(int4));
   pk.off_xkint = off;
   off = align256(off + pk.fetch_rows * (int64_t)sizeof(int2));
+  pk.off_y = off;
+  off = align256(off + (int64_t)pk.yitems.size() * sizeof(int4));
+  pk.off_xsrc = off;
+  off = align256(off + (int64_t)pk.xsrc.size() * sizeof(int32_t));
   pk.off_entries = off;
   off = align256(off + (int64_t)pk.entries.size() * sizeof(int2));
   pk.bytes = std::max<int64_t>(off, 256);
@@ -467,7 +498,9 @@ static int pack_calls(const Plan& p, int32_t r, Packed& pk) {
     for (int32_t b = 0; b < T; ++b) {
       if (cols[b].empty()) continue;
       std::stable_sort(cols[b].begin(), cols[b].end(), [](const int2& x, const int2& y) { return x.x < y.x; });
-      st.bitems.push_back(make_int4(b, 0, (int32_t)pk.entries.size(), (int32_t)cols[b].size()));
+      const int32_t kl = (int32_t)std::min<int64_t>(kTile, S - (int64_t)b * kTile);
+      st.bitems.push_back(make_int4(b * kTile, kl << kKeyRowsShift, (int32_t)pk.entries.size(),
+                                    (int32_t)cols[b].size()));
       pk.entries.insert(pk.entries.end(), cols[b].begin(), cols[b].end());
     }
     std::stable_sort(st.bitems.begin(), st.bitems.end(),
@@ -488,6 +521,8 @@ static int pack_calls(const Plan& p, int32_t r, Packed& pk) {
   pk.xitems.clear();
   pk.xtracks.clear();
   pk.xkint.clear();
+  pk.yitems.clear();
+  pk.xsrc.clear();
   pk.fetch_tiles = pk.fetch_rows = 0;
   layout(p, pk);
   return BSM_OK;
@@ -525,6 +560,9 @@ struct bsm_dplan {
   const int4* xtracks = nullptr;
   const int2* xkint = nullptr;
   int64_t nx = 0, fetch_tiles = 0, fetch_rows = 0;
+  const int4* yitems = nullptr;  // the fetched pass's dK/dV column items
+  int64_t ny = 0;
+  const int32_t* xsrc = nullptr;
 };
 
 using namespace bsm;
@@ -724,6 +762,8 @@ int dplan_upload(const bsm_plan* plan, int32_t r, bool dense, void* dev, int64_t
     for (size_t i = 0; i < pk.xitems.size(); ++i) xf[i] = pk.entries[pk.xitems[i].z];
     std::memcpy(img.data() + pk.off_xtracks, pk.xtracks.data(), pk.xtracks.size() * sizeof(int4));
     std::memcpy(img.data() + pk.off_xkint, pk.xkint.data(), pk.xkint.size() * sizeof(int2));
+    std::memcpy(img.data() + pk.off_y, pk.yitems.data(), pk.yitems.size() * sizeof(int4));
+    std::memcpy(img.data() + pk.off_xsrc, pk.xsrc.data(), pk.xsrc.size() * sizeof(int32_t));
     std::memcpy(img.data() + pk.off_entries, pk.entries.data(), pk.entries.size() * sizeof(int2));
     hipStream_t st = (hipStream_t)stream;
     int rc = hip_status(hipMemcpyAsync(dev, img.data(), pk.bytes, hipMemcpyHostToDevice, st),
@@ -767,6 +807,9 @@ int dplan_upload(const bsm_plan* plan, int32_t r, bool dense, void* dev, int64_t
     d->nx = (int64_t)pk.xitems.size();
     d->fetch_tiles = pk.fetch_tiles;
     d->fetch_rows = pk.fetch_rows;
+    d->yitems = (const int4*)(base + pk.off_y);
+    d->ny = (int64_t)pk.yitems.size();
+    d->xsrc = (const int32_t*)(base + pk.off_xsrc);
     *out = d;
   } catch (const std::bad_alloc&) {
     set_error("out of host memory");
@@ -1196,6 +1239,87 @@ int bsm_bwd_step_streams(const bsm_dplan* d, int32_t s, const bsm_heads* heads, 
                          void* kv_stream) {
   return bwd_step(d, s, heads, q, k, v, dout, lse, delta, dq_acc, dk, dv, workspace, workspace_bytes, dq_stream,
                   kv_stream);
+}
+
+int bsm_bwd_fetched(const bsm_dplan* d, const bsm_heads* heads, const void* q, const void* k_fetch,
+                    const void* v_fetch, const void* dout, const float* lse, const float* delta, float* dq,
+                    float* dk_fetch, float* dv_fetch, void* stream) {
+  if (!d) { set_error("null device plan"); return BSM_E_INVALID; }
+  int rc = check_heads(heads);
+  if (rc) return rc;
+  if (d->dense) {
+    set_error("a dense-call device plan has no sparse-fetch lists");
+    return BSM_E_UNSUPPORTED;
+  }
+  if (!q || !k_fetch || !v_fetch || !dout || !lse || !delta || !dq || !dk_fetch || !dv_fetch) {
+    set_error("null tensor pointer");
+    return BSM_E_INVALID;
+  }
+  if ((rc = check_rows(d->S, heads->hq, "q/dout")) || (rc = check_rows(d->fetch_rows, heads->hkv, "k/v fetched")))
+    return rc;
+  if ((rc = check_aligned({q, k_fetch, v_fetch, dout, dq, dk_fetch, dv_fetch}, {lse, delta}))) return rc;
+  BwdArgs a{};
+  a.entries = d->entries;
+  a.hq = heads->hq;
+  a.hkv = heads->hkv;
+  a.q = bf(q);
+  a.k = bf(k_fetch);
+  a.v = bf(v_fetch);
+  a.dout = bf(dout);
+  a.lse = lse;
+  a.delta = delta;
+  a.qtracks = d->tracks + (int64_t)d->r * d->S;
+  a.ktracks = d->xtracks;
+  a.kint = d->xkint;
+  a.dense = 0;
+  a.rows = d->S;
+  a.krows = d->fetch_rows;
+  a.dq = dq;
+  a.dk = dk_fetch;
+  a.dv = dv_fetch;
+  a.scale = heads->scale;
+  a.scale_log2 = heads->scale * 1.44269504088896340736f;
+  a.window = d->window;
+  hipStream_t st = (hipStream_t)stream;
+  if (d->nx) {
+    a.items = d->xitems;
+    a.nitems = (int32_t)d->nx;
+    a.heads_per_xcd = heads_per_xcd(heads->hq);
+    if ((rc = hip_status(launch_bwd_dq(a, st), "bwd fetched dq launch", st))) return rc;
+  }
+  if (d->ny) {
+    a.items = d->yitems;
+    a.nitems = (int32_t)d->ny;
+    a.heads_per_xcd = heads->hkv % 8 == 0 ? heads->hkv / 8 : 0;
+    if ((rc = hip_status(launch_bwd_dkdv(a, st), "bwd fetched dkdv launch", st))) return rc;
+  }
+  return BSM_OK;
+}
+
+int bsm_fetched_accumulate(const bsm_dplan* d, const bsm_heads* heads, const float* dk_fetch,
+                           const float* dv_fetch, float* dk_all, float* dv_all, void* stream) {
+  if (!d) { set_error("null device plan"); return BSM_E_INVALID; }
+  int rc = check_heads(heads);
+  if (rc) return rc;
+  if (d->dense) {
+    set_error("a dense-call device plan has no sparse-fetch lists");
+    return BSM_E_UNSUPPORTED;
+  }
+  if (!dk_fetch || !dv_fetch || !dk_all || !dv_all) {
+    set_error("null tensor pointer");
+    return BSM_E_INVALID;
+  }
+  if ((rc = check_aligned({dk_fetch, dv_fetch, dk_all, dv_all}, {}))) return rc;
+  FetchAccArgs a{};
+  a.src = d->xsrc;
+  a.rows = d->fetch_rows;
+  a.hkv = heads->hkv;
+  a.dk_fetch = dk_fetch;
+  a.dv_fetch = dv_fetch;
+  a.dk = dk_all;
+  a.dv = dv_all;
+  hipStream_t st = (hipStream_t)stream;
+  return hip_status(launch_fetch_accumulate(a, st), "fetched accumulate launch", st);
 }
 
 }  // extern "C"

@@ -10,12 +10,20 @@ constexpr int kHeadDim = 128;   // d
 constexpr int kTile = 128;      // query and key tile tokens
 
 // Work item of a list-driven kernel (int4 in device memory):
-//   x = tile index (query tile for forward / dQ, key tile for dK/dV)
+//   x = query tile index (forward / dQ), or the first key row of the key tile
+//       (dK/dV column items: the tiles of a compact sparse-fetch buffer start
+//       at any row, not only at multiples of 128)
 //   y = flags (kFirst: the tile's first step with work, kLast: its last)
 //   z = first entry of the tile's list, w = number of entries
 //   kKeyInterval (backward column items): every key of the tile has a key
 //   interval, so partial pairs test lo <= pos_q < hi
+//   Backward column items also carry the key tile's valid rows (1..128) in
+//   bits kKeyRowsShift.. of y: a tile of a compact sparse-fetch buffer can be
+//   ragged in the middle of the buffer, so the row count cannot come from the
+//   buffer's length.
 enum : int32_t { kFirst = 1, kLast = 2, kKeyInterval = 4 };
+constexpr int kKeyRowsShift = 8;
+__host__ __device__ inline int32_t key_rows(int32_t y) { return (y >> kKeyRowsShift) & 0xff; }
 
 // List entry (int2): x = first row of the partner tile in the partner buffer,
 //                    y = valid rows of the partner tile | (partial << 16)
@@ -142,9 +150,22 @@ struct BwdArgs {
   // one adds into dk / dv.
   const int4* work;
   float* ws;
-  // reduction after a split launch: int4 {key tile, first slot, slots, 0}
+  // reduction after a split launch: int4 {first key row of the tile, first
+  // slot, slots, valid rows of the key tile}
   const int4* reduce;
   int32_t nreduce;
+};
+
+// Sparse fetch, the way back: dk_all[src[c]] += dk_fetch[c] (and dV) for every
+// row c of the compact buffer with src[c] >= 0, all key/value heads.
+struct FetchAccArgs {
+  const int32_t* src;    // [fetch_rows] shard row (plan order) or -1
+  int64_t rows;          // fetch_rows
+  int32_t hkv;
+  const float* dk_fetch;
+  const float* dv_fetch;
+  float* dk;             // [R * S, Hkv, d]
+  float* dv;
 };
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
@@ -159,6 +180,7 @@ hipError_t launch_bwd_prep(int64_t rows, int32_t hq, const uint16_t* o,
                            const uint16_t* dout, float* delta, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_fetch_accumulate(const FetchAccArgs& a, hipStream_t stream);
 // dk/dv rows of every reduce entry's key tile += its workspace slots, in slot order.
 hipError_t launch_bwd_reduce(const BwdArgs& a, hipStream_t stream);
 

@@ -250,6 +250,37 @@ def fwd_fetched(dp: DevicePlan, hd, q, k_fetch, v_fetch, out=None, keep_state=Fa
     return o, lse
 
 
+def bwd_fetched(dp: DevicePlan, hd, q, k_fetch, v_fetch, dout, o, lse):
+    """Backward of the sparse-fetch pass: (dq, dk_fetch, dv_fetch) in fp32,
+    dk/dv over the rows of the compact buffer (the rank's contributions, to be
+    sent back to the owners: fetched_accumulate)."""
+    import torch
+    rows = dp.rows
+    _need(dout, torch.bfloat16, (rows, hd.hq, hd.d), "dout")
+    fr = dp.info["fetch_rows"]
+    _need(k_fetch, torch.bfloat16, (fr, hd.hkv, hd.d), "k_fetch")
+    _need(v_fetch, torch.bfloat16, (fr, hd.hkv, hd.d), "v_fetch")
+    delta = bwd_prep(hd, o, dout)
+    dq = torch.empty(rows, hd.hq, hd.d, dtype=torch.float32, device=q.device)
+    dkf = torch.zeros(fr, hd.hkv, hd.d, dtype=torch.float32, device=q.device)
+    dvf = torch.zeros_like(dkf)
+    C.bsm_bwd_fetched(dp.handle, hd, _ptr(q), _ptr(k_fetch), _ptr(v_fetch), _ptr(dout), _ptr(lse), _ptr(delta),
+                      _ptr(dq), _ptr(dkf), _ptr(dvf), _stream())
+    return dq, dkf, dvf
+
+
+def fetched_accumulate(dp: DevicePlan, hd, dk_fetch, dv_fetch, dk_all, dv_all):
+    """dk_all/dv_all (fp32, all shards in plan order) += the compact rows'
+    contributions at their shard rows (the sparse fetch's way back)."""
+    import torch
+    fr = dp.info["fetch_rows"]
+    for t, name in ((dk_fetch, "dk_fetch"), (dv_fetch, "dv_fetch")):
+        _need(t, torch.float32, (fr, hd.hkv, hd.d), name)
+    for t, name in ((dk_all, "dk_all"), (dv_all, "dv_all")):
+        _need(t, torch.float32, (dp.rows * dp.ranks, hd.hkv, hd.d), name)
+    C.bsm_fetched_accumulate(dp.handle, hd, _ptr(dk_fetch), _ptr(dv_fetch), _ptr(dk_all), _ptr(dv_all), _stream())
+
+
 def fwd_single(dp: DevicePlan, hd, q, k_all, v_all, keep_state=False, out=None):
     """Single pass over all shards (k_all/v_all = shards concatenated in plan order)."""
     import torch

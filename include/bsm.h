@@ -495,6 +495,42 @@ int bsm_bwd_step_streams(const bsm_dplan* dplan, int32_t s, const bsm_heads* hea
                          void* workspace, int64_t workspace_bytes, void* dq_stream, void* kv_stream);
 
 /*
+ * Backward of the sparse-fetch pass (MARBLE section 04, "Sparse all-to-all and
+ * strategy selection": the fetched blocks' dK and dV go back to their owners
+ * with the inverse all-to-all and are accumulated there in fp32).  One pass
+ * over the rank's queries and the compact buffer of bsm_fwd_fetched, against
+ * the final LSE:
+ *   q, dout            bf16 [S, Hq, d]
+ *   k_fetch, v_fetch   bf16 [fetch_rows, Hkv, d], laid out as for
+ *                      bsm_fwd_fetched; rows of a ragged tile past its valid
+ *                      rows are never read
+ *   lse, delta         fp32 [Hq, S] (forward LSE, bsm_bwd_prep)
+ *   dq                 fp32 [S, Hq, d], written for every query tile with work
+ *   dk_fetch, dv_fetch fp32 [fetch_rows, Hkv, d]: this call ADDS the rank's
+ *                      contribution of every compact row (caller clears);
+ *                      padding rows are never written
+ * Results equal the ring backward's up to the order of the fp32 sums.  A
+ * dense-call device plan returns BSM_E_UNSUPPORTED.
+ */
+int bsm_bwd_fetched(const bsm_dplan* dplan, const bsm_heads* heads, const void* q,
+                    const void* k_fetch, const void* v_fetch, const void* dout,
+                    const float* lse, const float* delta, float* dq, float* dk_fetch,
+                    float* dv_fetch, void* stream);
+
+/*
+ * The way back of the sparse fetch on one device: for every row c of the
+ * compact buffer that holds a shard row (not padding), dk_all[src] +=
+ * dk_fetch[c] and dv_all[src] += dv_fetch[c] in fp32, src being that row's
+ * position in the shards concatenated in plan order (dk_all, dv_all fp32
+ * [R * S, Hkv, d]).  Across devices this is the inverse all-to-all followed
+ * by each owner's fp32 add; every shard row receives at most one compact row,
+ * so the adds never collide.  Stream-ordered; BSM_E_UNSUPPORTED for a
+ * dense-call device plan.
+ */
+int bsm_fetched_accumulate(const bsm_dplan* dplan, const bsm_heads* heads, const float* dk_fetch,
+                           const float* dv_fetch, float* dk_all, float* dv_all, void* stream);
+
+/*
  * bsm_bwd_step_ws without a caller workspace, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  The split dK/dV partial sums go to a

@@ -39,7 +39,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=3, help="workload index 1..5")
+    ap.add_argument("--config", type=int, default=3,
+                    help="workload index 1..5; 6 = video frames in one group per sample (layout transforms)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU seconds of the oracle baseline sample")
@@ -54,6 +55,8 @@ def parse():
                          "fetched remote tiles (forward only; the fetch itself is not timed)")
     ap.add_argument("--order", choices=["ptrr", "contiguous"], default=None,
                     help="token order of the ring layout (default: the workload's own)")
+    ap.add_argument("--vision-group", action="store_true",
+                    help="permute tokens into the vision-group order before planning (layout transform)")
     ap.add_argument("--chunks", type=int, default=0,
                     help="chunked ring layout: search 1..K contiguous chunks per rank")
     ap.add_argument("--tau", type=float, default=0.0,
@@ -421,6 +424,9 @@ def main():
     if args.fit_tau:
         print(json.dumps(fit_tau(args, bsm, torch, lay, qkv)), flush=True)
         return
+    if args.vision_group:
+        from workloads import permuted
+        lay = permuted(lay, bsm.vision_group_order(lay.tracks()), name=lay.name + "_vision_group")
     if args.order:
         lay = dataclasses.replace(lay, order=args.order)
     if args.fetch:

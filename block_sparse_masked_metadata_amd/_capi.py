@@ -46,7 +46,7 @@ EXPORTS = [
     "bsm_fwd_step", "bsm_fwd_single", "bsm_fwd_merge_bf16", "bsm_fwd_merge_fp32",
     "bsm_bwd_prep", "bsm_bwd_step", "bsm_plan_dense_calls", "bsm_dplan_calls_bytes",
     "bsm_dplan_calls_upload", "bsm_state_unpack", "bsm_bwd_step_ws", "bsm_bwd_step_streams",
-    "bsm_bwd_step_noalloc", "bsm_bwd_fetched", "bsm_fetched_accumulate",
+    "bsm_bwd_step_noalloc", "bsm_bwd_fetched", "bsm_fetched_accumulate", "bsm_vision_group_order",
 ]
 
 
@@ -138,6 +138,7 @@ _sig = {
                                        _P, _P, _P, _P]),
     "bsm_bwd_fetched": (C.c_int, [_P, C.POINTER(bsm_heads), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "bsm_fetched_accumulate": (C.c_int, [_P, C.POINTER(bsm_heads), _P, _P, _P, _P, _P]),
+    "bsm_vision_group_order": (C.c_int, [C.c_int64, _P, _P, _P]),
 }
 
 
@@ -386,3 +387,13 @@ def bsm_bwd_fetched(dplan, heads, q, k_fetch, v_fetch, dout, lse, delta, dq, dk_
 
 def bsm_fetched_accumulate(dplan, heads, dk_fetch, dv_fetch, dk_all, dv_all, stream):
     _check(_lib.bsm_fetched_accumulate(dplan, C.byref(heads), dk_fetch, dv_fetch, dk_all, dv_all, stream))
+
+
+def bsm_vision_group_order(sample, seg):
+    """new_to_orig (int32[n]) of the vision-group token order."""
+    sm, sg = _i32(sample), _i32(seg)
+    if len(sm) != len(sg):
+        raise ValueError("tracks must have equal length")
+    out = np.empty(len(sm), np.int32)
+    _check(_lib.bsm_vision_group_order(len(sm), sm.ctypes.data, sg.ctypes.data, out.ctypes.data))
+    return out

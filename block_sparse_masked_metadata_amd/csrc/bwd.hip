@@ -121,6 +121,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
   const int64_t sidx = (int64_t)h * a.rows + qr;
   const float lse_raw = a.lse[sidx], dl_raw = a.delta[sidx];
   const int4 qt_raw = a.qtracks[qr];
+  const int32_t qc_raw = a.qcoord[qr];
   const bool kload = partf && lenf > 0, kinterval = (ent.y & kIntervalBit) != 0;
   int4 kraw;  // an interval fills x and y only
   if (kload) {
@@ -139,6 +140,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
   const float nlse2 = qvalid ? -lse_raw * kLog2e : kNegInf;  // invalid rows: p = 0
   const float dl = qvalid ? dl_raw : 0.f;
   const int4 qt = query_tracks(qvalid ? qt_raw : make_int4(0, -1, -1, 0));
+  const int32_t qc = qvalid ? qc_raw : -1;  // the query's token index (key-interval coordinate)
   int4 kt_pf = make_int4(kDense ? INT32_MAX : -1, -1, -1, 0);  // keys past len: sample -1, empty range
   if (kload && tid < lenf) {
     if (kDense)
@@ -202,7 +204,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
         for (int r = 0; r < 16; ++r) {
           const int key = kc * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
           const int2 iv = *(const int2*)&sKT[key];
-          s[r] = in_interval(qt.w, iv.x, iv.y) ? s[r] : kNegInf;
+          s[r] = in_interval(qc, iv.x, iv.y) ? s[r] : kNegInf;
         }
       } else if (partial) {
 #pragma unroll
@@ -294,6 +296,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
   const int total = grp * nsub;  // (query head of the group, sub-tile) pairs
 
   int list_base = 0;
+  // every key of the tile has a key interval: partial pairs test the query's
+  // token index against it (staged in place of the query tracks)
+  const bool kin = (it.y & kKeyInterval) != 0;
 
   // Stage (head g*grp + m/nsub, sub-tile m%nsub) into registers.
   PairStage pf;
@@ -316,7 +321,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
     rs.v = 0.f;
     rs.t = make_int4(-2, -1, -1, -1);  // rows past len: no sample, no position
     if (tid < 2 * kSub && row < nxt_len) rs.v = (tid < kSub ? a.lse : a.delta)[(int64_t)h * a.rows + r0 + row];
-    if (tid >= 2 * kSub && tid < 3 * kSub && nxt_partial && row < nxt_len) rs.t = a.qtracks[r0 + row];
+    if (tid >= 2 * kSub && tid < 3 * kSub && nxt_partial && row < nxt_len) {
+      if (kin)
+        rs.t.w = a.qcoord[r0 + row];
+      else
+        rs.t = a.qtracks[r0 + row];
+    }
     pf.fetch((const char*)(a.q + (int64_t)h * kHeadDim), (const char*)(a.dout + (int64_t)h * kHeadDim),
              r0, nxt_len, row_bytes, tid);
   };
@@ -342,7 +352,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
   }
   // this lane's key: its tracks, or its key interval when every key of the
   // tile has one (kKeyInterval); invalid keys admit no query
-  const bool kin = (it.y & kKeyInterval) != 0;
   // Loaded raw with no value written into these registers afterwards; an
   // invalid key reads the tile's first row (always present) and is replaced
   // once every prologue load has landed.

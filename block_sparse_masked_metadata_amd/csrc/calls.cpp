@@ -97,6 +97,12 @@ int relation_bounds(int32_t kind, int64_t qmin, int64_t qmax, int64_t kmin, int6
 
 int dense_calls(const Plan& p, int32_t r, int32_t s, std::vector<Call>& out) {
   out.clear();
+  // the relations of a call compare positions over runs of rows, which
+  // needs positions that rise with the token index
+  if (!p.pos_rising) {
+    set_error("dense calls need positions that rise with the token index");
+    return BSM_E_UNSUPPORTED;
+  }
   const int32_t R = p.ranks;
   const int32_t j = ((r - s) % R + R) % R;
   const int64_t S = p.shard, qbase = (int64_t)r * S, kbase = (int64_t)j * S;

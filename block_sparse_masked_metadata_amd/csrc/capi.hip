@@ -54,6 +54,7 @@ void set_error(const std::string& msg) { g_error = msg; }
 // Host image of one rank's device plan.
 struct Packed {
   std::vector<int4> tracks;
+  std::vector<int32_t> coord;  // per plan row: its token index in the caller's order
   std::vector<StepLists> steps;
   std::vector<int4> sitems;
   std::vector<int2> kint;  // key intervals (lo, hi) in plan order
@@ -65,7 +66,7 @@ struct Packed {
   int64_t fetch_tiles = 0, fetch_rows = 0;
   std::vector<int2> entries;
   // byte offsets in the device buffer
-  int64_t off_tracks = 0, off_kint = 0, off_items = 0, off_entries = 0, bytes = 0;
+  int64_t off_tracks = 0, off_coord = 0, off_kint = 0, off_items = 0, off_entries = 0, bytes = 0;
   std::vector<int64_t> off_f, off_b, off_ff;  // off_ff: first list entry of each forward item
   std::vector<int64_t> off_w, off_r;         // split dK/dV work units and reduce entries
   int64_t off_s = 0, off_sf = 0, off_x = 0, off_xf = 0, off_xtracks = 0, off_xkint = 0;
@@ -139,6 +140,7 @@ static void pack(const Plan& p, int32_t r, Packed& pk) {
   const int64_t S = p.shard;
   pk.tracks.resize(p.n);
   pk.kint.resize(p.n);
+  pk.coord.assign(p.perm.begin(), p.perm.end());
   for (int64_t i = 0; i < p.n; ++i) {
     const int32_t t = p.perm[i];
     pk.tracks[i] = make_int4(p.sample[t], p.seg[t], p.noise[t], p.pos[t]);
@@ -309,6 +311,8 @@ static void layout(const Plan& p, Packed& pk) {
   int64_t off = 0;
   pk.off_tracks = off;
   off = align256(off + p.n * (int64_t)sizeof(int4));
+  pk.off_coord = off;
+  off = align256(off + p.n * (int64_t)sizeof(int32_t));
   pk.off_kint = off;
   off = align256(off + p.n * (int64_t)sizeof(int2));
   pk.off_items = off;
@@ -386,6 +390,7 @@ static int pack_calls(const Plan& p, int32_t r, Packed& pk) {
   }
   pk.tracks.resize(p.n);
   pk.kint.assign(p.n, make_int2(0, -1));
+  pk.coord.assign(p.perm.begin(), p.perm.end());
   for (int64_t i = 0; i < p.n; ++i) {
     const int32_t t = p.perm[i];
     pk.tracks[i] = make_int4(p.sample[t], p.seg[t], p.noise[t], p.pos[t]);
@@ -541,6 +546,7 @@ struct bsm_dplan {
   int32_t r = 0, R = 1, tps = 0, window = 0;
   int64_t S = 0, n = 0;
   const int4* tracks = nullptr;
+  const int32_t* coord = nullptr;  // per plan row: token index in the caller's order
   const int2* kint = nullptr;
   const int2* entries = nullptr;
   const int4* fitems[64] = {};
@@ -745,6 +751,7 @@ int dplan_upload(const bsm_plan* plan, int32_t r, bool dense, void* dev, int64_t
     }
     std::vector<char> img(pk.bytes, 0);
     std::memcpy(img.data() + pk.off_tracks, pk.tracks.data(), pk.tracks.size() * sizeof(int4));
+    std::memcpy(img.data() + pk.off_coord, pk.coord.data(), pk.coord.size() * sizeof(int32_t));
     std::memcpy(img.data() + pk.off_kint, pk.kint.data(), pk.kint.size() * sizeof(int2));
     for (int32_t s = 0; s < p.ranks; ++s) {
       std::memcpy(img.data() + pk.off_f[s], pk.steps[s].fitems.data(), pk.steps[s].fitems.size() * sizeof(int4));
@@ -781,6 +788,7 @@ int dplan_upload(const bsm_plan* plan, int32_t r, bool dense, void* dev, int64_t
     d->S = p.shard;
     d->n = p.n;
     d->tracks = (const int4*)(base + pk.off_tracks);
+    d->coord = (const int32_t*)(base + pk.off_coord);
     d->kint = (const int2*)(base + pk.off_kint);
     d->entries = (const int2*)(base + pk.off_entries);
     for (int32_t s = 0; s < p.ranks; ++s) {
@@ -915,6 +923,7 @@ int bsm_fwd_step(const bsm_dplan* d, int32_t s, const bsm_heads* heads, const vo
   a.k = bf(k);
   a.v = bf(v);
   a.qtracks = d->tracks + (int64_t)d->r * d->S;
+  a.qcoord = d->coord + (int64_t)d->r * d->S;
   a.ktracks = d->tracks + (int64_t)j * d->S;
   a.kint = d->kint + (int64_t)j * d->S;
   a.rows = d->S;
@@ -968,6 +977,7 @@ int fwd_pass(const bsm_dplan* d, bool fetched, const bsm_heads* heads, const voi
   a.k = bf(k_all);
   a.v = bf(v_all);
   a.qtracks = d->tracks + (int64_t)d->r * d->S;
+  a.qcoord = d->coord + (int64_t)d->r * d->S;
   a.ktracks = fetched ? d->xtracks : d->tracks;
   a.kint = fetched ? d->xkint : d->kint;
   a.rows = d->S;
@@ -1010,6 +1020,15 @@ int bsm_plan_chunk_order(const bsm_plan* plan, int32_t min_chunks, int32_t max_c
   out->step_max_sum = res.step_max_sum;
   out->range_term = res.range_term;
   return BSM_OK;
+}
+
+int bsm_vision_group_order(int64_t n, const int32_t* sample, const int32_t* seg, int32_t* new_to_orig) {
+  try {
+    return vision_group_order(n, sample, seg, new_to_orig);
+  } catch (const std::bad_alloc&) {
+    set_error("out of host memory");
+    return BSM_E_NOMEM;
+  }
 }
 
 int bsm_plan_fetch_set(const bsm_plan* plan, int32_t r, uint8_t* needed, int64_t* tiles) {
@@ -1121,6 +1140,7 @@ int bwd_step(const bsm_dplan* d, int32_t s, const bsm_heads* heads, const void* 
   a.lse = lse;
   a.delta = delta;
   a.qtracks = d->tracks + (int64_t)d->r * d->S;
+  a.qcoord = d->coord + (int64_t)d->r * d->S;
   a.ktracks = d->tracks + (int64_t)j * d->S;
   a.kint = d->kint + (int64_t)j * d->S;
   a.dense = d->dense;
@@ -1269,6 +1289,7 @@ int bsm_bwd_fetched(const bsm_dplan* d, const bsm_heads* heads, const void* q, c
   a.lse = lse;
   a.delta = delta;
   a.qtracks = d->tracks + (int64_t)d->r * d->S;
+  a.qcoord = d->coord + (int64_t)d->r * d->S;
   a.ktracks = d->xtracks;
   a.kint = d->xkint;
   a.dense = 0;

@@ -146,8 +146,8 @@ __device__ inline void sub_bounds(const int2 ent, int n, int32_t& k0, int& len, 
 // the range dense_range gives the lane's query for entry word `ey`.
 template <bool kDense>
 __device__ inline void scores(f32x16 (&s)[2], const char* sK, const bf16x8 (&qf)[8], const int4* sKT,
-                              const int4 qt, bool partial, bool interval, int32_t window, int l32, int hi,
-                              int32_t ey, int row) {
+                              const int4 qt, int32_t qc, bool partial, bool interval, int32_t window, int l32,
+                              int hi, int32_t ey, int row) {
   __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
@@ -181,14 +181,15 @@ __device__ inline void scores(f32x16 (&s)[2], const char* sK, const bf16x8 (&qf)
         }
     }
   } else if (partial && interval) {
-    // Key intervals: legal iff lo <= pos_q < hi, one unsigned compare.
+    // Key intervals: legal iff lo <= qc < hi (qc: the query's token index),
+    // one unsigned compare.
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
         const int2 iv = *(const int2*)&sKT[key];
-        s[kb][r] = (uint32_t)(qt.w - iv.x) < (uint32_t)(iv.y - iv.x) ? s[kb][r] : kNegInf;
+        s[kb][r] = (uint32_t)(qc - iv.x) < (uint32_t)(iv.y - iv.x) ? s[kb][r] : kNegInf;
       }
   } else if (partial) {
     // Keys past len carry sample -1 and fail the sample test.  Every lane of
@@ -274,6 +275,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a) {
       qf[kk] = qvalid ? as_bf16x8(*(const uint4*)(qp + kk * 16)) : as_bf16x8(make_uint4(0, 0, 0, 0));
   }
   const int4 qt = query_tracks(qvalid ? a.qtracks[qrow] : make_int4(0, -1, -1, 0));
+  const int32_t qc = qvalid ? a.qcoord[qrow] : -1;
 
   // Running state.  acc[db][r] = O^T[d = 32db + 8(r/4) + 4hi + r%4][query l32];
   // mref is the base-2 reference the accumulator and l are scaled against.
@@ -342,7 +344,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a) {
     }
 
     f32x16 s[2];
-    scores<kDense>(s, sK, qf, sKT, qt, partial, interval, a.window, l32, hi, ey, (int)qi);
+    scores<kDense>(s, sK, qf, sKT, qt, qc, partial, interval, a.window, l32, hi, ey, (int)qi);
 
     // Online softmax in base-2 units against a lazily updated reference mref.
     // Common case: exponentiate against the current reference; every p stays
@@ -357,7 +359,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a) {
       ls = exp_sum(s, a.scale_log2, -mref);
       if (__any(!(ls < kSumCap))) {
         fast = false;
-        scores<kDense>(s, sK, qf, sKT, qt, partial, interval, a.window, l32, hi, ey, (int)qi);
+        scores<kDense>(s, sK, qf, sKT, qt, qc, partial, interval, a.window, l32, hi, ey, (int)qi);
       }
     }
     if (!fast) {

@@ -74,7 +74,9 @@ __device__ inline void dense_key_range(int32_t y, int row, int32_t pk, int32_t w
 }
 
 // Key interval of a token (int2): the queries it is legal for are exactly
-// those with x <= pos < y; y < x when it has none (the planner's key_interval).
+// those whose index in the caller's token order lies in [x, y); y < x when it
+// has none (the planner's key_interval).  The device plan carries that index
+// per plan row (`coord`), the coordinate the kernels test it against.
 
 // The carried forward state O_acc is tile-blocked (each workgroup's state is
 // one contiguous 64 KiB run that its lanes read and write fully coalesced):
@@ -104,6 +106,7 @@ struct FwdArgs {
   const uint16_t* k;  // [*, Hkv, d]
   const uint16_t* v;
   const int4* qtracks;      // tracks of the query shard rows
+  const int32_t* qcoord;    // key-interval coordinate of the query shard rows
   const int4* ktracks;      // tracks of the key buffer rows
   const int2* kint;         // key intervals of the key buffer rows
   int64_t rows;             // S: query shard rows (state stride / ragged bound)
@@ -132,6 +135,7 @@ struct BwdArgs {
   const float* lse;           // [Hq, S] natural log
   const float* delta;         // [Hq, S]
   const int4* qtracks;
+  const int32_t* qcoord;      // key-interval coordinate of the query shard rows
   const int4* ktracks;
   const int2* kint;           // key intervals of the key buffer rows
   int32_t dense;              // the lists hold dense-call entries

@@ -10,9 +10,10 @@
 //   section 04, "Planning cost"        - built once per batch on CPU threads
 //
 // Key intervals: for each key the planner also derives the set of queries it
-// is legal for from the track structure (its causal window, the runs of its
-// seg id, the run of its noise id, its sample); when that set is one range of
-// positions the kernels test partial tiles with two compares per pair.
+// is legal for from the track structure (its causal window, the tokens of its
+// seg id, the tokens of its noise id, its sample); when that set is one range
+// of token indices (in the caller's order) the kernels test partial tiles
+// with one unsigned compare per pair.
 //
 // Classification is exact: a tile pair is FULL when every valid token pair is
 // legal, EMPTY when none is, PARTIAL otherwise.  Per-tile summaries (min/max of
@@ -21,6 +22,10 @@
 // tile are the tiles whose sample-id range meets the query tile's, which is a
 // contiguous run of tiles because samples are contiguous runs in the original
 // order and tiles are contiguous pieces of it.
+//
+// Positions need not rise with the index: a layout transform (MARBLE section
+// 04, "Layout transforms") may permute tokens, each carrying its original
+// position.  Only the dense calls need rising positions.
 
 #include "planner.hpp"
 
@@ -30,6 +35,7 @@
 #include <numeric>
 #include <thread>
 #include <unordered_map>
+#include <cstring>
 #include <utility>
 
 namespace bsm {
@@ -41,13 +47,14 @@ struct Summary {
 };
 
 Summary summarize(const Plan& p, int64_t a, int64_t b) {
-  Summary s{p.sample[a], p.sample[b - 1], INT32_MAX, INT32_MIN, INT32_MAX, INT32_MIN,
-            p.pos[a], p.pos[b - 1]};
+  Summary s{p.sample[a], p.sample[b - 1], INT32_MAX, INT32_MIN, INT32_MAX, INT32_MIN, INT32_MAX, INT32_MIN};
   for (int64_t i = a; i < b; ++i) {
     s.gmin = std::min(s.gmin, p.seg[i]);
     s.gmax = std::max(s.gmax, p.seg[i]);
     s.nmin = std::min(s.nmin, p.noise[i]);
     s.nmax = std::max(s.nmax, p.noise[i]);
+    s.pmin = std::min(s.pmin, p.pos[i]);
+    s.pmax = std::max(s.pmax, p.pos[i]);
   }
   return s;
 }
@@ -122,82 +129,142 @@ int validate(const bsm_plan_desc& d) {
     if (d.sample[i] < 0) { set_error("sample ids must be >= 0"); return BSM_E_INVALID; }
     if (d.seg[i] < -1 || d.noise[i] < -1) { set_error("seg and noise ids must be >= -1"); return BSM_E_INVALID; }
     if (d.pos[i] < 0) { set_error("pos must be >= 0"); return BSM_E_INVALID; }
-    if (i > 0) {
-      if (d.sample[i] < d.sample[i - 1]) {
-        set_error("samples must be contiguous runs with non-decreasing ids");
-        return BSM_E_INVALID;
-      }
-      if (d.pos[i] <= d.pos[i - 1]) { set_error("pos must be strictly increasing"); return BSM_E_INVALID; }
+    if (i > 0 && d.sample[i] < d.sample[i - 1]) {
+      set_error("samples must be contiguous runs with non-decreasing ids");
+      return BSM_E_INVALID;
     }
   }
   return BSM_OK;
 }
 
-using Run = std::pair<int64_t, int64_t>;  // token index range [first, second)
+// Key intervals in the index coordinate.  For key k of sample run S the legal
+// query set is L = ((C u G) n Z) with C = tokens of S with 0 <= pos_q - pos_k
+// < W, G = tokens of S with k's seg id (when it is >= 0), Z = tokens of S with
+// k's noise id (all of S when it is < 0).  L is one run of indices exactly when
+// |L| = max index - min index + 1; the planner computes |L| and its extreme
+// indices from position-sorted token lists, and gives no range whenever it
+// cannot (the kernels then test the four tracks, which is always exact).
+struct RangeIndex {
+  // tokens of one sample run sorted by (pos, index); sparse tables of the
+  // indices' min and max over that order when positions do not rise with the
+  // index (else the order is the index order and they are the ends)
+  int64_t s0 = 0;
+  bool rising = true;
+  std::vector<int32_t> pos;  // ascending
+  std::vector<int32_t> idx;
+  std::vector<std::vector<int32_t>> mn, mx;
 
-// Maximal runs of each id >= 0 of a track, in index order.
-std::unordered_map<int32_t, std::vector<Run>> id_runs(const std::vector<int32_t>& t) {
-  std::unordered_map<int32_t, std::vector<Run>> runs;
-  const int64_t n = (int64_t)t.size();
-  for (int64_t i = 0; i < n;) {
-    int64_t j = i + 1;
-    while (j < n && t[j] == t[i]) ++j;
-    if (t[i] >= 0) runs[t[i]].push_back({i, j});
-    i = j;
-  }
-  return runs;
-}
-
-// Sorted, merged union of ranges (touching ranges join).
-void merge_runs(std::vector<Run>& v) {
-  std::sort(v.begin(), v.end());
-  size_t k = 0;
-  for (size_t i = 0; i < v.size(); ++i) {
-    if (k && v[i].first <= v[k - 1].second)
-      v[k - 1].second = std::max(v[k - 1].second, v[i].second);
-    else
-      v[k++] = v[i];
-  }
-  v.resize(k);
-}
-
-// The legal query set of key k as index ranges: (causal window U span of its
-// seg id) within its sample, restricted to the noise span of its noise id.
-// It is one range of positions whenever it is one range of indices, since
-// pos rises strictly with the index.
-void key_interval(const Plan& p, int64_t k, int64_t s0, int64_t s1,
-                  const std::unordered_map<int32_t, std::vector<Run>>& seg_runs,
-                  const std::unordered_map<int32_t, std::vector<Run>>& noise_runs, std::vector<Run>& u,
-                  int32_t& lo, int32_t& hi) {
-  u.clear();
-  // causal: 0 <= pos_q - pos_k < W  <=>  q in [k, first index with pos >= pos_k + W)
-  const int64_t lim = (int64_t)p.pos[k] + p.window;
-  const int64_t c1 = std::lower_bound(p.pos.begin() + k, p.pos.begin() + s1, lim,
-                                      [](int32_t a, int64_t b) { return (int64_t)a < b; }) -
-                     p.pos.begin();
-  u.push_back({k, c1});
-  if (p.seg[k] >= 0)
-    for (const Run& r : seg_runs.at(p.seg[k])) {
-      const int64_t a = std::max(r.first, s0), b = std::min(r.second, s1);
-      if (a < b) u.push_back({a, b});
+  void build(const Plan& p, int64_t a, int64_t b) {
+    s0 = a;
+    const int64_t n = b - a;
+    rising = true;
+    for (int64_t i = a + 1; i < b; ++i)
+      if (p.pos[i] <= p.pos[i - 1]) rising = false;
+    std::vector<std::pair<int32_t, int32_t>> v((size_t)n);
+    for (int64_t i = 0; i < n; ++i) v[(size_t)i] = {p.pos[a + i], (int32_t)(a + i)};
+    if (!rising) std::sort(v.begin(), v.end());
+    pos.resize((size_t)n);
+    idx.resize((size_t)n);
+    for (int64_t i = 0; i < n; ++i) {
+      pos[(size_t)i] = v[(size_t)i].first;
+      idx[(size_t)i] = v[(size_t)i].second;
     }
-  merge_runs(u);
-  if (p.noise[k] >= 0) {
-    std::vector<Run> w;
-    for (const Run& r : noise_runs.at(p.noise[k]))
-      for (const Run& x : u) {
-        const int64_t a = std::max(r.first, x.first), b = std::min(r.second, x.second);
-        if (a < b) w.push_back({a, b});
+    if (rising) return;
+    mn.assign(1, idx);
+    mx.assign(1, idx);
+    for (int64_t w = 1; 2 * w <= n; w *= 2) {
+      const std::vector<int32_t>&pm = mn.back(), &px = mx.back();
+      std::vector<int32_t> nm((size_t)(n - 2 * w + 1)), nx((size_t)(n - 2 * w + 1));
+      for (int64_t i = 0; i + 2 * w <= n; ++i) {
+        nm[(size_t)i] = std::min(pm[(size_t)i], pm[(size_t)(i + w)]);
+        nx[(size_t)i] = std::max(px[(size_t)i], px[(size_t)(i + w)]);
       }
-    merge_runs(w);
-    u.swap(w);
+      mn.push_back(std::move(nm));
+      mx.push_back(std::move(nx));
+    }
   }
-  if (u.size() == 1) {
-    lo = p.pos[u[0].first];
-    hi = p.pos[u[0].second - 1] + 1;
+  // min and max index over sorted positions [i0, i1), i1 > i0
+  void extremes(int64_t i0, int64_t i1, int64_t& lo, int64_t& hi) const {
+    if (rising) {
+      lo = idx[(size_t)i0];
+      hi = idx[(size_t)(i1 - 1)];
+      return;
+    }
+    int l = 0;
+    while ((int64_t(2) << l) <= i1 - i0) ++l;
+    const int64_t j = i1 - (int64_t(1) << l);
+    lo = std::min(mn[l][(size_t)i0], mn[l][(size_t)j]);
+    hi = std::max(mx[l][(size_t)i0], mx[l][(size_t)j]);
+  }
+  // sorted-order range of positions [a, b)
+  void span(int64_t a, int64_t b, int64_t& i0, int64_t& i1) const {
+    i0 = std::lower_bound(pos.begin(), pos.end(), a, [](int32_t x, int64_t y) { return (int64_t)x < y; }) -
+         pos.begin();
+    i1 = std::lower_bound(pos.begin(), pos.end(), b, [](int32_t x, int64_t y) { return (int64_t)x < y; }) -
+         pos.begin();
+  }
+};
+
+// The tokens of one id (seg or noise) within one sample run.
+struct IdSet {
+  int64_t lo = INT64_MAX, hi = INT64_MIN, count = 0;
+  std::vector<int32_t> pos;  // ascending (seg sets: for |C n G|)
+  std::vector<int32_t> tok;  // token indices (noise sets: for the explicit scan)
+  int32_t seg = INT32_MIN;   // noise sets: the seg id all tokens share, else INT32_MIN
+  bool mixed = false;
+};
+
+uint64_t id_key(int64_t run, int32_t id) { return ((uint64_t)run << 32) | (uint32_t)id; }
+
+constexpr int64_t kNoiseScan = 4096;  // explicit scan of a noise set up to this size
+
+void key_interval(const Plan& p, int64_t k, const RangeIndex& ri, const IdSet* g, const IdSet* z,
+                  int32_t& lo, int32_t& hi) {
+  lo = 0;
+  hi = -1;
+  const int64_t pk = p.pos[k];
+  const int64_t lim = pk + (int64_t)p.window;  // causal: pk <= pos_q < pk + W
+  if (z && !(z->seg == p.seg[k] && p.seg[k] >= 0 && !z->mixed)) {
+    // the noise set is not inside the key's seg: scan it (small sets only)
+    if (z->count > kNoiseScan) return;
+    int64_t c = 0, mn = INT64_MAX, mx = INT64_MIN;
+    for (int32_t q : z->tok) {
+      const int64_t pq = p.pos[q];
+      if ((pq >= pk && pq < lim) || (p.seg[k] >= 0 && p.seg[q] == p.seg[k])) {
+        ++c;
+        mn = std::min<int64_t>(mn, q);
+        mx = std::max<int64_t>(mx, q);
+      }
+    }
+    if (c > 0 && c == mx - mn + 1) {
+      lo = (int32_t)mn;
+      hi = (int32_t)(mx + 1);
+    }
+    return;
+  }
+  int64_t count, mn, mx;
+  if (z) {  // every token of the noise set is in the key's seg: L is the noise set
+    count = z->count;
+    mn = z->lo;
+    mx = z->hi;
   } else {
-    lo = 0;
-    hi = -1;
+    int64_t i0, i1;
+    ri.span(pk, lim, i0, i1);
+    count = i1 - i0;  // >= 1: the key itself
+    ri.extremes(i0, i1, mn, mx);
+    if (g) {
+      const int64_t a = std::lower_bound(g->pos.begin(), g->pos.end(), pk,
+                                         [](int32_t x, int64_t y) { return (int64_t)x < y; }) - g->pos.begin();
+      const int64_t b = std::lower_bound(g->pos.begin(), g->pos.end(), lim,
+                                         [](int32_t x, int64_t y) { return (int64_t)x < y; }) - g->pos.begin();
+      count += g->count - (b - a);
+      mn = std::min(mn, g->lo);
+      mx = std::max(mx, g->hi);
+    }
+  }
+  if (count == mx - mn + 1) {
+    lo = (int32_t)mn;
+    hi = (int32_t)(mx + 1);
   }
 }
 
@@ -353,27 +420,55 @@ int build_plan(const bsm_plan_desc& d, Plan& p) {
     for (int64_t x = p.tstart[p.tiles_new[i]]; x < p.tend[p.tiles_new[i]]; ++x) p.perm.push_back((int32_t)x);
 
   // key intervals (MARBLE section 03, "Block classification": a partial tile
-  // can test one position range per key instead of the full predicate)
+  // can test one range per key instead of the full predicate)
   {
-    const auto seg_runs = id_runs(p.seg), noise_runs = id_runs(p.noise);
-    p.klo.assign(d.n, 0);
-    p.khi.assign(d.n, -1);
-    std::vector<int64_t> s0(d.n), s1(d.n);
+    p.pos_rising = true;
+    for (int64_t i = 1; i < d.n; ++i)
+      if (p.pos[i] <= p.pos[i - 1]) p.pos_rising = false;
+    std::vector<std::pair<int64_t, int64_t>> runs;  // sample runs
+    std::vector<int32_t> run_of(d.n);
     for (int64_t i = 0; i < d.n;) {
       int64_t j = i + 1;
       while (j < d.n && p.sample[j] == p.sample[i]) ++j;
-      for (int64_t x = i; x < j; ++x) {
-        s0[x] = i;
-        s1[x] = j;
-      }
+      for (int64_t x = i; x < j; ++x) run_of[x] = (int32_t)runs.size();
+      runs.push_back({i, j});
       i = j;
     }
+    std::vector<RangeIndex> ri(runs.size());
+    parallel_for((int64_t)runs.size(), threads, [&](int64_t r) { ri[r].build(p, runs[r].first, runs[r].second); });
+    std::unordered_map<uint64_t, IdSet> segs, noises;
+    for (int64_t i = 0; i < d.n; ++i) {
+      if (p.seg[i] >= 0) {
+        IdSet& g = segs[id_key(run_of[i], p.seg[i])];
+        g.lo = std::min<int64_t>(g.lo, i);
+        g.hi = std::max<int64_t>(g.hi, i);
+        ++g.count;
+        g.pos.push_back(p.pos[i]);
+      }
+      if (p.noise[i] >= 0) {
+        IdSet& z = noises[id_key(run_of[i], p.noise[i])];
+        z.lo = std::min<int64_t>(z.lo, i);
+        z.hi = std::max<int64_t>(z.hi, i);
+        if (z.count == 0) z.seg = p.seg[i];
+        else if (z.seg != p.seg[i]) z.mixed = true;
+        ++z.count;
+        if (z.count <= kNoiseScan) z.tok.push_back((int32_t)i);
+      }
+    }
+    for (auto& e : segs)
+      if (!std::is_sorted(e.second.pos.begin(), e.second.pos.end()))
+        std::sort(e.second.pos.begin(), e.second.pos.end());
+    p.klo.assign(d.n, 0);
+    p.khi.assign(d.n, -1);
     const int64_t chunk = 4096, nchunks = (d.n + chunk - 1) / chunk;
     parallel_for(nchunks, threads, [&](int64_t c) {
-      std::vector<Run> u;
       const int64_t b = std::min(d.n, (c + 1) * chunk);
-      for (int64_t k = c * chunk; k < b; ++k)
-        key_interval(p, k, s0[k], s1[k], seg_runs, noise_runs, u, p.klo[k], p.khi[k]);
+      for (int64_t k = c * chunk; k < b; ++k) {
+        const int32_t run = run_of[k];
+        const IdSet* g = p.seg[k] >= 0 ? &segs.at(id_key(run, p.seg[k])) : nullptr;
+        const IdSet* z = p.noise[k] >= 0 ? &noises.at(id_key(run, p.noise[k])) : nullptr;
+        key_interval(p, k, ri[run], g, z, p.klo[k], p.khi[k]);
+      }
     });
     p.tile_kint.assign(nt, 1);
     p.interval_keys = 0;
@@ -396,6 +491,50 @@ int build_plan(const bsm_plan_desc& d, Plan& p) {
     }
   }
   p.seconds = std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
+  return BSM_OK;
+}
+
+int vision_group_order(int64_t n, const int32_t* sample, const int32_t* seg, int32_t* out) {
+  if (n < 1 || n > (int64_t(1) << 30)) { set_error("n must be in [1, 2^30]"); return BSM_E_INVALID; }
+  if (!sample || !seg || !out) { set_error("null pointer"); return BSM_E_INVALID; }
+  for (int64_t i = 0; i < n; ++i) {
+    if (sample[i] < 0 || seg[i] < -1) { set_error("need sample >= 0 and seg >= -1"); return BSM_E_INVALID; }
+    if (i > 0 && sample[i] < sample[i - 1]) {
+      set_error("samples must be contiguous runs with non-decreasing ids");
+      return BSM_E_INVALID;
+    }
+  }
+  int64_t w = 0;
+  std::vector<std::pair<int64_t, int64_t>> spans;  // runs of one seg id >= 0 in the sample
+  std::unordered_map<int32_t, int32_t> nruns;      // seg id -> runs in the sample
+  for (int64_t a = 0; a < n;) {
+    int64_t b = a + 1;
+    while (b < n && sample[b] == sample[a]) ++b;
+    spans.clear();
+    nruns.clear();
+    for (int64_t i = a; i < b;) {
+      int64_t j = i + 1;
+      while (j < b && seg[j] == seg[i]) ++j;
+      if (seg[i] >= 0) {
+        spans.push_back({i, j});
+        ++nruns[seg[i]];
+      }
+      i = j;
+    }
+    // a group: one seg id over two or more spans of the sample
+    std::vector<uint8_t> in_group((size_t)(b - a), 0);
+    std::vector<std::pair<int64_t, int64_t>> groups;
+    for (const auto& sp : spans)
+      if (nruns[seg[sp.first]] >= 2) {
+        groups.push_back(sp);
+        for (int64_t i = sp.first; i < sp.second; ++i) in_group[(size_t)(i - a)] = 1;
+      }
+    for (int64_t i = a; i < b; ++i)
+      if (!in_group[(size_t)(i - a)]) out[w++] = (int32_t)i;
+    for (auto it = groups.rbegin(); it != groups.rend(); ++it)
+      for (int64_t i = it->first; i < it->second; ++i) out[w++] = (int32_t)i;
+    a = b;
+  }
   return BSM_OK;
 }
 

@@ -33,8 +33,10 @@ struct Plan {
   // tracks, original order
   std::vector<int32_t> sample, seg, noise, pos;
   // Key intervals, original order: the queries key k is legal for are exactly
-  // the positions [klo[k], khi[k]), or the key has no such range (khi < klo).
+  // the tokens with index in [klo[k], khi[k]) (index in the caller's order),
+  // or the key has no such range (khi < klo).
   std::vector<int32_t> klo, khi;
+  bool pos_rising = true;          // positions rise strictly with the index
   std::vector<uint8_t> tile_kint;  // original tile: every key has an interval
   int64_t interval_keys = 0;
   int32_t busiest = 0;
@@ -46,6 +48,10 @@ struct Plan {
 
 // Build; returns BSM_OK or an error code (error text set).
 int build_plan(const bsm_plan_desc& desc, Plan& out);
+
+// Vision-group token order of a packed sequence (see bsm.h); out[i] = the
+// index of the token placed at position i.
+int vision_group_order(int64_t n, const int32_t* sample, const int32_t* seg, int32_t* out);
 
 // Legal pairs of rank r at step s and optional tile map.
 int64_t step_map(const Plan& p, int32_t r, int32_t s, uint8_t* map);

@@ -159,9 +159,10 @@ __device__ inline int4 key_mask_data(const int4* ktracks, const int2* kint, int6
   return ktracks[row];
 }
 
-// lo <= pos < hi as one unsigned compare (positions and bounds are int32 >= -1).
-__device__ inline bool in_interval(int32_t pos, int32_t lo, int32_t hi) {
-  return (uint32_t)(pos - lo) < (uint32_t)(hi - lo);
+// lo <= x < hi as one unsigned compare (x: a query's token index, -1 on pad
+// rows; 0 <= lo < hi <= 2^30).
+__device__ inline bool in_interval(int32_t x, int32_t lo, int32_t hi) {
+  return (uint32_t)(x - lo) < (uint32_t)(hi - lo);
 }
 
 }  // namespace dev

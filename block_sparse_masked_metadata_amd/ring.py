@@ -82,6 +82,13 @@ class Plan:
             pass
 
 
+def vision_group_order(tracks):
+    """The vision-group layout transform: new_to_orig over the tokens of
+    `tracks` (sample, seg, noise, pos), to be applied to tracks and
+    activations alike before planning."""
+    return C.bsm_vision_group_order(tracks[0], tracks[1])
+
+
 class DevicePlan:
     """Rank r's device plan in a torch uint8 buffer (the library allocates nothing)."""
 

@@ -97,7 +97,9 @@ typedef struct bsm_plan bsm_plan;
  *              need a sample id of their own)
  *   seg[i]     id of the bidirectional span / group, -1 for causal tokens
  *   noise[i]   id of the generated (noise) span, -1 otherwise
- *   pos[i]     original position, strictly increasing, >= 0
+ *   pos[i]     original position, >= 0; positions need not rise with the
+ *              index: a layout transform (bsm_vision_group_order) permutes
+ *              tokens, each keeping its original position
  * A query q may attend a key k iff
  *   ((0 <= pos[q]-pos[k] < window) or (seg[q] == seg[k] and seg[k] >= 0))
  *   and (noise[k] < 0 or noise[q] == noise[k]) and sample[q] == sample[k].
@@ -214,14 +216,34 @@ int bsm_plan_fetch_set(const bsm_plan* plan, int32_t r, uint8_t* needed, int64_t
 
 /*
  * Key intervals (MARBLE section 03, "Block classification": a partial tile can
- * test one range per key in a chosen coordinate).  For every key k in the
- * ORIGINAL order, when the queries k is legal for are exactly those with
- * lo[k] <= pos < hi[k] (the union of its causal window and the spans of its
- * seg id, within its sample and the span of its noise id, is one run of
- * tokens), lo/hi receive that range; otherwise lo[k] = 0, hi[k] = -1 and the
- * kernels keep the four-track predicate for its tiles.  Host int32[n] each.
+ * test one range per key in a chosen coordinate).  The coordinate is the token
+ * index in the caller's order (the order of the tracks given to
+ * bsm_plan_build).  For every key k, when the queries k is legal for are
+ * exactly the tokens with index in [lo[k], hi[k]) (the union of its causal
+ * window and the tokens of its seg id, within its sample and restricted to
+ * the tokens of its noise id, is one run of indices), lo/hi receive that
+ * range; otherwise lo[k] = 0, hi[k] = -1 and the kernels keep the four-track
+ * predicate for its tiles.  A key may also get no range when its noise span
+ * lies partly outside its seg and holds more than 4096 tokens (the planner
+ * does not scan such spans).  Host int32[n] each.
  */
 int bsm_plan_key_intervals(const bsm_plan* plan, int32_t* lo, int32_t* hi);
+
+/*
+ * Vision-group token order (MARBLE section 04, "Layout transforms": for
+ * vision-group sequences all text goes first and the group spans after it in
+ * reverse, so that each key's visible queries form one range).  Per sample (a
+ * contiguous run of one sample id), the tokens of group spans (runs of a seg
+ * id >= 0 that occurs in two or more runs of the sample) move after the rest:
+ * the other tokens keep their order, then the group spans follow in reverse
+ * order of their first token, each span's tokens in their order.  The caller
+ * permutes tracks and activations once with new_to_orig (position i of the
+ * new order holds token new_to_orig[i]) and plans the permuted sequence; each
+ * token keeps its position track, so the mask is unchanged.  Host pointers;
+ * sample ids >= 0, contiguous and non-decreasing, seg ids >= -1, else
+ * BSM_E_INVALID.
+ */
+int bsm_vision_group_order(int64_t n, const int32_t* sample, const int32_t* seg, int32_t* new_to_orig);
 
 /*
  * Dense calls (MARBLE section 03, "Chunked ring attention": for long, mostly
@@ -229,6 +251,8 @@ int bsm_plan_key_intervals(const bsm_plan* plan, int32_t* lo, int32_t* hi);
  * reverse causal over runs of tokens, instead of one masked block-sparse
  * call).  The calls of rank r at step s cover every legal pair between rank
  * r's query shard and key shard (r - s) mod R exactly once and no illegal one.
+ * Dense calls need positions that rise with the token index (BSM_E_UNSUPPORTED
+ * otherwise, e.g. after a vision-group order).
  * A call pairs query rows [q0, q0 + q_len) of the query shard with key rows
  * [k0, k0 + k_len) of the key shard (plan order, local to each shard) and
  * computes the pairs whose positions satisfy `kind`:
@@ -299,6 +323,9 @@ int bsm_dplan_calls_bytes(const bsm_plan* plan, int32_t r, int64_t* bytes);
 int bsm_dplan_calls_upload(const bsm_plan* plan, int32_t r, void* dev, int64_t bytes,
                            void* stream, bsm_dplan** out);
 
+/* What a device plan holds per step (MARBLE section 03, "Block classification":
+ * for every ring step the blocks the rank computes), for callers that skip
+ * steps without work and size workspaces. */
 typedef struct {
   int32_t rank;
   int32_t ranks;
@@ -416,7 +443,9 @@ int bsm_fwd_merge_fp32(const bsm_heads* heads, int64_t rows, float* o_run, float
                        void* stream);
 
 /*
- * The carried accumulator of bsm_fwd_step / bsm_fwd_single in row order:
+ * The carried accumulator of bsm_fwd_step / bsm_fwd_single in row order
+ * (MARBLE section 03, "Exact ring attention accumulation": the fp32 O_acc that
+ * stays in HBM between ring steps, here laid out tile by tile for the kernels):
  * out fp32 [rows, Hq, d] from o_acc (tile-blocked, ceil(rows / 128) * 128 *
  * Hq * d floats).  Stream-ordered on `stream`; rows >= 1.
  */
@@ -428,6 +457,8 @@ int bsm_state_unpack(const bsm_heads* heads, int64_t rows, const float* o_acc, f
  * ====================================================================== */
 
 /*
+ * Backward preparation (MARBLE section 03, "Exact ring attention
+ * accumulation": every backward step runs against the final output and LSE):
  * delta[h][i] = sum_c dO[i][h][c] * O[i][h][c] in fp32 (the row term of the
  * softmax backward), from the bf16 O the forward wrote.  rows >= 1.
  */

@@ -133,8 +133,8 @@ def test_invalid_metadata_errors():
     bad_cases = []
     s = good[0].copy(); s[10] = 5; s[11] = 1
     bad_cases.append(([s] + good[1:], WINDOW_INF, 2, "ptrr"))           # samples not contiguous
-    p = good[3].copy(); p[5] = p[4]
-    bad_cases.append((good[:3] + [p], WINDOW_INF, 2, "ptrr"))            # pos not increasing
+    p = good[3].copy(); p[5] = -3
+    bad_cases.append((good[:3] + [p], WINDOW_INF, 2, "ptrr"))            # pos < 0
     g = good[1].copy(); g[0] = -2
     bad_cases.append(([good[0], g] + good[2:], WINDOW_INF, 2, "ptrr"))  # seg < -1
     s = good[0].copy(); s[:100] = -1

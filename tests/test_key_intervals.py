@@ -2,9 +2,11 @@
 a partial tile may test one range per key) against the oracle predicate.
 
 For every key with a range, the queries it is legal for must be exactly the
-tokens with lo <= pos < hi; a key without one must really have a legal set
-that is not one run of tokens.  Brute force over random all-mode layouts and
-over sampled keys of the five workloads."""
+tokens whose index (in the order the plan was given) lies in [lo, hi); a key
+without one must really have a legal set that is not one run of tokens.
+Brute force over random all-mode layouts, the same layouts in vision-group
+order (positions then no longer rise with the index), and sampled keys of the
+workloads."""
 import numpy as np
 import pytest
 
@@ -21,14 +23,13 @@ def _runs(mask):
 
 def _check_keys(lay, keys, lo, hi):
     tr = lay.tracks()
-    pos = np.asarray(tr[3])
     sample = np.asarray(tr[0])
     for k in keys:
         # the legal set lies inside the key's sample: test that sample's queries
         qs = np.flatnonzero(sample == sample[k])
         got = legal(take(tr, qs), take(tr, [k]), lay.window)[:, 0]
         if hi[k] >= lo[k]:
-            want = (pos[qs] >= lo[k]) & (pos[qs] < hi[k])
+            want = (qs >= lo[k]) & (qs < hi[k])
             assert np.array_equal(got, want), (lay.name, int(k), int(lo[k]), int(hi[k]))
         else:
             assert _runs(got) > 1, (lay.name, int(k))
@@ -39,6 +40,21 @@ def test_intervals_random_layouts(seed):
     rng = np.random.default_rng(1000 + seed)
     n = int(rng.integers(8, 160))
     lay = random_small(rng, n)
+    plan = bsm.Plan(lay.tracks(), lay.window, 1, block=16, order="contiguous")
+    lo, hi = plan.key_intervals()
+    assert plan.info["interval_keys"] == int((hi >= lo).sum())
+    _check_keys(lay, range(n), lo, hi)
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_intervals_random_layouts_vision_group_order(seed):
+    """The same brute force after the vision-group order: positions no longer
+    rise with the index, and the coordinate of the ranges is the new index."""
+    from workloads import permuted
+    rng = np.random.default_rng(1100 + seed)
+    n = int(rng.integers(8, 200))
+    base = random_small(rng, n, max_span=20)
+    lay = permuted(base, bsm.vision_group_order(base.tracks()))
     plan = bsm.Plan(lay.tracks(), lay.window, 1, block=16, order="contiguous")
     lo, hi = plan.key_intervals()
     assert plan.info["interval_keys"] == int((hi >= lo).sum())

@@ -197,12 +197,49 @@ def long_mixed(n: int = 1048576, seed: int = 5, ranks: int = 8, clip: int = 1638
                    b.spans, hq=16, hkv=4, d=128, seed=seed, backward=True)
 
 
+def video_group(n: int = 131072, seed: int = 6, ranks: int = 8, frame: int = 196, stamp: int = 8,
+                min_frames: int = 16, max_frames: int = 96) -> Layout:
+    """Video samples whose frames form one bidirectional group (MARBLE section
+    01: the group mode, as Molmo2 combines all image spans of a sample).
+
+    Each sample: a causal text prompt (16-128 tokens), then per frame a causal
+    timestamp of `stamp` tokens followed by the frame (`frame` tokens), then a
+    causal answer (16-256 tokens).  Every frame of a sample carries the
+    sample's one seg id, so frames see each other in both directions but not
+    the timestamps between them.  Frame counts are drawn uniformly in
+    [min_frames, max_frames]; the last sample is cut at n.  The pages give no
+    frame or text sizes; 196 tokens is a 14 x 14 patch grid.
+    """
+    rng = np.random.default_rng(seed)
+    b = _Builder(n)
+    s = 0
+    while not b.full:
+        b.add(int(rng.integers(16, 129)), s, -1, -1, "causal")
+        for _ in range(int(rng.integers(min_frames, max_frames + 1))):
+            b.add(stamp, s, -1, -1, "causal")
+            b.add(frame, s, s, -1, "group")
+        b.add(int(rng.integers(16, 257)), s, -1, -1, "causal")
+        s += 1
+    return _finish("video_group_128k", b.sample, b.seg, b.noise, WINDOW_INF, ranks, "ptrr", b.spans,
+                   hq=16, hkv=4, d=128, seed=seed, backward=True)
+
+
+def permuted(lay: Layout, new_to_orig, name: str = None) -> Layout:
+    """The layout with its tokens permuted (position i holds token
+    new_to_orig[i]); every token keeps its tracks, its position included."""
+    import dataclasses
+    idx = np.asarray(new_to_orig, np.int64)
+    return dataclasses.replace(lay, name=name or lay.name + "_permuted", sample=lay.sample[idx],
+                               seg=lay.seg[idx], noise=lay.noise[idx], pos=lay.pos[idx], spans=[])
+
+
 CONFIGS = {
     1: ring_toy,
     2: packed_text,
     3: packed_multimodal,
     4: sliding_window,
     5: long_mixed,
+    6: video_group,
 }
 
 

@@ -480,37 +480,76 @@ __global__ __launch_bounds__(256) void merge_bf16_kernel(int64_t pairs, int64_t 
   if ((gid & 15) == 0) lse_run[li] = lnew;
 }
 
-__global__ __launch_bounds__(256) void merge_fp32_kernel(int64_t pairs, int64_t rows, int32_t hq, float* o_run,
-                                                         float* lse_run, const float* acc_s, const float* m_s,
-                                                         const float* l_s, unsigned short* o_bf16) {
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t pair = gid >> 4;
-  if (pair >= pairs) return;
-  const int64_t row = pair / hq;
-  const int32_t h = (int32_t)(pair % hq);
-  const int64_t li = (int64_t)h * rows + row;
-  const float l = l_s[li];
-  float* orp = o_run + gid * 8;
-  if (l > 0.f) {
-    const float ls = (m_s[li] + log2f(l)) * kLn2;  // the step's LSE (m in base-2 units)
-    const float lr = lse_run[li];
-    float wr, ws, lnew;
-    merge_weights(lr, ls, wr, ws, lnew);
-    // channels d0 .. d0 + 7 of the tile-blocked partial: two float4 runs
-    const int32_t d0 = (int32_t)(gid & 15) * 8;
-    const float4 a0 = *(const float4*)(acc_s + state_index(row, h, d0, hq));
-    const float4 a1 = *(const float4*)(acc_s + state_index(row, h, d0 + 4, hq));
-    const float ap[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) orp[i] = (lr == kNegInf ? 0.f : wr * orp[i]) + ws * (ap[i] / l);
-    if ((gid & 15) == 0) lse_run[li] = lnew;
+// One workgroup per 32-row block of one (query tile, head) of the
+// tile-blocked partial (4096 floats, one wave's rows in the forward): the
+// block is read in its stored order, 16 bytes per thread, coalesced; each
+// thread then updates the 4 channels of O_run that its float4 holds.  A
+// row's merge weights are computed once, into LDS, and LSE_run is written
+// only after every read of it.
+__global__ __launch_bounds__(256) void merge_fp32_kernel(int64_t rows, int32_t hq, float* o_run, float* lse_run,
+                                                         const float* acc_s, const float* m_s, const float* l_s,
+                                                         unsigned short* o_bf16) {
+  __shared__ float sw_r[32], sw_s[32], s_l[32], s_lnew[32];
+  __shared__ int s_live[32];  // 0: row past the end, 1: merge, 2: not reached by this step
+  __shared__ int s_fresh[32];  // no running value yet (LSE_run = -inf): O_run is ignored
+  const int64_t blk = blockIdx.x;  // ((tile * hq) + h) * 4 + w
+  const int w = (int)(blk & 3);
+  const int32_t h = (int32_t)((blk >> 2) % hq);
+  const int64_t t = (blk >> 2) / hq;
+  const int tid = threadIdx.x;
+  const int64_t row0 = t * kTile + 32 * w;
+  if (tid < 32) {
+    const int64_t row = row0 + tid;
+    int live = 0, fresh = 0;
+    float wr = 0.f, ws = 0.f, lv = 1.f, lnew = 0.f;
+    if (row < rows) {
+      const int64_t li = (int64_t)h * rows + row;
+      const float l = l_s[li];
+      const float lr = lse_run[li];
+      if (l > 0.f) {
+        const float ls = (m_s[li] + log2f(l)) * kLn2;  // the step's LSE (m in base-2 units)
+        merge_weights(lr, ls, wr, ws, lnew);
+        fresh = lr == kNegInf;
+        lv = l;
+        live = 1;
+      } else {
+        live = 2;  // reached by no key of this step: O_run unchanged
+      }
+    }
+    sw_r[tid] = wr;
+    sw_s[tid] = ws;
+    s_l[tid] = lv;
+    s_lnew[tid] = lnew;
+    s_live[tid] = live;
+    s_fresh[tid] = fresh;
   }
-  if (o_bf16) {
-    bf16x8 r8;
+  __syncthreads();
+  const float* ab = acc_s + (t * hq + h) * (int64_t)(kTile * kHeadDim) + w * (32 * kHeadDim);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) r8[i] = (__bf16)orp[i];
-    *(uint4*)(o_bf16 + gid * 8) = __builtin_bit_cast(uint4, r8);
+  for (int k = 0; k < 4; ++k) {
+    const int q = k * 256 + tid;                  // float4 q of the block: (4 db + i) * 64 + l + 32 hi
+    const int l = q & 31, hi = (q >> 5) & 1, dbi = q >> 6;
+    const int live = s_live[l];
+    if (live == 0) continue;                      // row past the shard's end
+    const int64_t row = row0 + l;
+    const int d0 = 32 * (dbi >> 2) + 8 * (dbi & 3) + 4 * hi;
+    float4* orp = (float4*)(o_run + (row * hq + h) * kHeadDim + d0);
+    float4 o = *orp;
+    if (live == 1) {
+      const float4 a = *(const float4*)(ab + 4 * q);
+      const float wr = sw_r[l], ws = sw_s[l], lv = s_l[l];
+      const bool fresh = s_fresh[l] != 0;
+      o = make_float4((fresh ? 0.f : wr * o.x) + ws * (a.x / lv), (fresh ? 0.f : wr * o.y) + ws * (a.y / lv),
+                      (fresh ? 0.f : wr * o.z) + ws * (a.z / lv), (fresh ? 0.f : wr * o.w) + ws * (a.w / lv));
+      *orp = o;
+    }
+    if (o_bf16) {
+      __bf16 b4[4] = {(__bf16)o.x, (__bf16)o.y, (__bf16)o.z, (__bf16)o.w};
+      *(uint2*)(o_bf16 + (row * hq + h) * kHeadDim + d0) = __builtin_bit_cast(uint2, b4);
+    }
   }
+  __syncthreads();  // every read of lse_run came before this (tid < 32 above)
+  if (tid < 32 && s_live[tid] == 1) lse_run[(int64_t)h * rows + row0 + tid] = s_lnew[tid];
 }
 
 __global__ __launch_bounds__(256) void state_unpack_kernel(int64_t quads, int32_t hq, const float* o_acc,
@@ -571,10 +610,10 @@ hipError_t launch_merge_bf16(int64_t rows, int32_t hq, uint16_t* o_run, float* l
 
 hipError_t launch_merge_fp32(int64_t rows, int32_t hq, float* o_run, float* lse_run, const float* acc_s,
                              const float* m_s, const float* l_s, uint16_t* o_bf16, hipStream_t stream) {
-  const int64_t pairs = rows * hq;
-  const int64_t blocks = (pairs * 16 + 255) / 256;
-  hipLaunchKernelGGL(merge_fp32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, pairs, rows, hq, o_run,
-                     lse_run, acc_s, m_s, l_s, (unsigned short*)o_bf16);
+  const int64_t tiles = (rows + kTile - 1) / kTile;
+  const int64_t blocks = tiles * hq * 4;  // 32-row blocks of every (tile, head)
+  hipLaunchKernelGGL(merge_fp32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, rows, hq, o_run, lse_run,
+                     acc_s, m_s, l_s, (unsigned short*)o_bf16);
   return hipGetLastError();
 }
 

@@ -562,28 +562,40 @@ __global__ __launch_bounds__(256) void state_unpack_kernel(int64_t quads, int32_
   *(float4*)(out + e) = *(const float4*)(o_acc + state_index(row, h, d, hq));
 }
 
-__global__ __launch_bounds__(256) void bwd_prep_kernel(int64_t pairs, int64_t rows, int32_t hq,
-                                                       const unsigned short* o,
+// delta[h][row] = sum_c dO[row][h][c] O[row][h][c].  One workgroup per 64 rows
+// of one head: 16 lanes cover a row's 128 channels (8 each), every thread
+// issues its 4 rows' loads before reducing any (8 loads of 16 bytes in
+// flight), and the 64 results of the head are written as one contiguous run.
+__global__ __launch_bounds__(256) void bwd_prep_kernel(int64_t rows, int32_t hq, const unsigned short* o,
                                                        const unsigned short* dout, float* delta) {
-  // one thread per 8 channels; 16 lanes cover one (row, head) of 128 channels
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t pair = gid >> 4;
-  float s = 0.f;
-  if (pair < pairs) {
-    const uint4 a4 = *(const uint4*)(o + gid * 8);
-    const uint4 b4 = *(const uint4*)(dout + gid * 8);
-    const bf16x8 av = as_bf16x8(a4), bv = as_bf16x8(b4);
+  constexpr int kRows = 64, kPass = 4;
+  const int32_t h = (int32_t)(blockIdx.x % hq);
+  const int64_t r0 = (int64_t)(blockIdx.x / hq) * kRows;
+  const int tid = threadIdx.x, sub = tid >> 4, c8 = (tid & 15) * 8;
+  uint4 a4[kPass], b4[kPass];
+#pragma unroll
+  for (int p = 0; p < kPass; ++p) {
+    const int64_t row = r0 + p * 16 + sub;
+    a4[p] = make_uint4(0, 0, 0, 0);
+    b4[p] = make_uint4(0, 0, 0, 0);
+    if (row < rows) {
+      const int64_t off = (row * hq + h) * kHeadDim + c8;
+      a4[p] = *(const uint4*)(o + off);
+      b4[p] = *(const uint4*)(dout + off);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < kPass; ++p) {
+    const bf16x8 av = as_bf16x8(a4[p]), bv = as_bf16x8(b4[p]);
+    float s = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) s += (float)av[i] * (float)bv[i];
-  }
-  s += __shfl_xor(s, 8);
-  s += __shfl_xor(s, 4);
-  s += __shfl_xor(s, 2);
-  s += __shfl_xor(s, 1);
-  if (pair < pairs && (gid & 15) == 0) {
-    const int64_t row = pair / hq;
-    const int32_t h = (int32_t)(pair % hq);
-    delta[(int64_t)h * rows + row] = s;
+    s += __shfl_xor(s, 8);
+    s += __shfl_xor(s, 4);
+    s += __shfl_xor(s, 2);
+    s += __shfl_xor(s, 1);
+    const int64_t row = r0 + p * 16 + sub;
+    if ((tid & 15) == 0 && row < rows) delta[(int64_t)h * rows + row] = s;
   }
 }
 
@@ -626,10 +638,8 @@ hipError_t launch_state_unpack(int64_t rows, int32_t hq, const float* o_acc, flo
 
 hipError_t launch_bwd_prep(int64_t rows, int32_t hq, const uint16_t* o,
                            const uint16_t* dout, float* delta, hipStream_t stream) {
-  const int64_t pairs = rows * hq;
-  const int64_t threads = pairs * 16;
-  const int64_t blocks = (threads + 255) / 256;
-  hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, pairs, rows, hq,
+  const int64_t blocks = (rows + 63) / 64 * hq;  // (64-row block, head)
+  hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, rows, hq,
                      (const unsigned short*)o, (const unsigned short*)dout, delta);
   return hipGetLastError();
 }

@@ -12,21 +12,27 @@
 // the mask predicate of section 01 on every element.
 //
 // Work decomposition: one workgroup of 4 waves per (query tile, query head);
-// wave w owns query rows [32w, 32w+32) of the tile.  Per listed key tile:
-//   1. the 128x128 K and V tiles are staged in LDS (row-major, padded rows);
-//   2. S^T = K Q^T on v_mfma_f32_32x32x16_bf16: K from LDS is the A operand,
-//      Q (kept in registers for the whole item) the B operand, so the result
-//      puts one query per lane (lane l and l^32 share query l%32, each holding
-//      half of the tile's keys);
-//   3. the online softmax is then mostly lane-local (one cross-lane exchange
-//      for the row max and one for the row sum), in base-2 units with
-//      scale*log2(e) folded into one multiply;
-//   4. O^T += V^T P^T on MFMA: P (bf16) is the B operand straight from the
-//      registers of step 3, with the 16 key slots of each MFMA permuted to
-//      match the accumulator layout; V^T is read from the row-major V tile
-//      with the gfx950 LDS transpose read (ds_read_b64_tr_b16) at the same
-//      permutation.  The output accumulator again holds one query per lane,
-//      so the rescale by exp2(m_old - m_new) is a per-lane scalar.
+// wave w owns query rows [32w, 32w+32) of the tile.  Listed key tiles are
+// processed as 64-key sub-tiles n = 0, 1, ...:
+//   - S^T = K Q^T on v_mfma_f32_32x32x16_bf16: K from LDS is the A operand,
+//     Q (kept in registers for the whole item) the B operand, so the result
+//     puts one query per lane (lane l and l^32 share query l%32, each holding
+//     half of the sub-tile's keys) and the softmax is lane-local but for one
+//     cross-lane exchange for the row max and one for the row sum, in base-2
+//     units with scale*log2(e) folded into one multiply;
+//   - O^T += V^T P^T on MFMA: P (bf16) is the B operand straight from the
+//     registers of the softmax, with the 16 key slots of each MFMA permuted to
+//     match the accumulator layout; V^T is read from the row-major V tile with
+//     the gfx950 LDS transpose read (ds_read_b64_tr_b16) at the same
+//     permutation.  The output accumulator again holds one query per lane, so
+//     a rescale is a per-lane scalar.
+// Software pipeline: iteration n runs the exponentials of S(n) beside the
+// MFMAs of S(n+1), then the MFMAs of P(n) V(n) beside the row sum of P(n) and
+// the mask and row max of S(n+1); a row's reference moves (rescaling O_acc and
+// l) only when its max grows past it by more than 2^8, so no exponential is
+// ever taken twice.  K and V reach LDS by direct-to-LDS buffer loads (no
+// register staging), two buffers each: the loads of K(n+2) and V(n+1) fly
+// during iteration n, with one workgroup barrier per sub-tile.
 
 #include "tile_common.hpp"
 
@@ -39,10 +45,12 @@ using dev::kNegInf;
 using dev::kLn2;
 using dev::kSub;
 using dev::as_bf16x8;
+using dev::mfma;
 using dev::lds_tr8;
 using dev::legal;
 using dev::query_tracks;
 using dev::map_block;
+using dev::in_interval;
 
 // ---- LDS sub-tiles: 64 key rows x 256 B, unpadded, 16-byte chunks XOR-swizzled ----
 // K: chunk c of row r sits in slot c ^ (r & 15), so the MFMA A-operand reads
@@ -52,177 +60,215 @@ using dev::map_block;
 __device__ inline int k_slot(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
 __device__ inline int v_slot(int r, int c) { return r * 256 + ((c ^ ((r & 3) << 2)) << 4); }
 
-constexpr int kListCache = 512;      // list entries of an item kept in LDS
-constexpr float kSumCap = 4096.0f;   // a lane sum below 2^12 keeps every p below 2^12
+constexpr int kListCache = 512;           // list entries of an item kept in LDS
+constexpr float kGrowth = 8.0f;           // every p stays at or below 2^8
 constexpr int kBufferFlags = 0x00020000;  // buffer descriptor word 3: 32-bit data format, untyped loads
 
-// One sub-tile of K, V (and key tracks) staged through registers: thread t
-// holds chunk t%16 of rows t/16 + 16i (i = 0..3), so every 16 lanes read one
-// 256-byte row contiguously.  Rows past `len` are zero.
-struct SubTile {
-  uint4 k[4], v[4];
-  int4 kt;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Sub-tile of an item: half `half` of a list entry.
+struct Sub {
+  int32_t k0;  // first key row
+  int len;     // valid rows, 0..64
+  bool partial, interval;
+  int32_t ey;  // the entry word (dense-call row range and relation)
 };
-
-// kbase/vbase: the head's element 0 of key row 0 (uniform).  k0 is uniform, so
-// the row base of a full sub-tile and the strides of its 4 loads are scalar;
-// `lane_off` = (t/16) * row_bytes + 16 (t%16) is loop-invariant.  Key-row byte
-// offsets stay below 2^32 (a key buffer holds fewer than 2^32 bytes).
-// On partial sub-tiles the key's mask data rides along: its tracks, or with
-// `interval` its key interval (lo, hi) in the first two fields.  Keys past len
-// keep (-1, -1, -1, 0): sample -1 and the empty range [-1, -1) admit no query.
-// With kDense (dense-call lists) a partial sub-tile carries only the key's
-// position, and keys past len take position 2^31 - 1, outside every range.
-template <bool kDense>
-__device__ inline void fetch_sub(SubTile& t, const char* kbase, const char* vbase,
-                                 const int4* ktracks, const int2* kint, int32_t k0, int len, bool partial,
-                                 bool interval, uint32_t row_bytes, uint32_t lane_off, int tid) {
-  t.kt = make_int4(kDense ? INT32_MAX : -1, -1, -1, 0);
-  if (partial && tid < len) {
-    if (kDense) {
-      t.kt.x = ktracks[k0 + tid].w;
-    } else if (interval) {
-      const int2 iv = kint[k0 + tid];
-      t.kt = make_int4(iv.x, iv.y, 0, 0);
-    } else {
-      t.kt = ktracks[k0 + tid];
-    }
-  }
-  const uint32_t r0 = (uint32_t)k0 * row_bytes;
-  if (len == kSub) {
-    // raw buffer loads: the uniform row offset rides in soffset and the
-    // loop-invariant lane offset in voffset, so no per-load address
-    // arithmetic.  The record count is the full 32-bit range: every byte
-    // offset of a key buffer (under 4 GiB) is in range.
-    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, 0, -1, kBufferFlags);
-    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, 0, -1, kBufferFlags);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t ro = r0 + 16u * i * row_bytes;
-      t.k[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, lane_off, ro, 0));
-      t.v[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vr, lane_off, ro, 0));
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = (tid >> 4) + 16 * i;
-      const uint32_t ro = r0 + 16u * i * row_bytes;
-      t.k[i] = make_uint4(0, 0, 0, 0);
-      t.v[i] = make_uint4(0, 0, 0, 0);
-      if (row < len) {
-        t.k[i] = *(const uint4*)(kbase + ro + lane_off);
-        t.v[i] = *(const uint4*)(vbase + ro + lane_off);
-      }
-    }
-  }
-}
-
-__device__ inline void store_sub(const SubTile& t, char* sK, char* sV, int4* sKT, int tid) {
-  const int c = tid & 15;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = (tid >> 4) + 16 * i;
-    *(uint4*)(sK + k_slot(row, c)) = t.k[i];
-    *(uint4*)(sV + v_slot(row, c)) = t.v[i];
-  }
-  if (tid < kSub) sKT[tid] = t.kt;
-}
-
-// Sub-tile n of an item: half n%2 of list entry n/2.
-__device__ inline void sub_bounds(const int2 ent, int n, int32_t& k0, int& len, bool& partial, bool& interval) {
-  const int half = n & 1;
+__device__ inline Sub sub_of(const int2 ent, int half) {
+  Sub b;
   const int klen = ent.y & kLenMask;
-  k0 = ent.x + half * kSub;
-  len = klen - half * kSub;
-  len = len < 0 ? 0 : (len > kSub ? kSub : len);
-  partial = (ent.y & kPartialBit) != 0;
-  interval = (ent.y & kIntervalBit) != 0;
+  b.k0 = ent.x + half * kSub;
+  const int len = klen - half * kSub;
+  b.len = len < 0 ? 0 : (len > kSub ? kSub : len);
+  b.partial = (ent.y & kPartialBit) != 0;
+  b.interval = (ent.y & kIntervalBit) != 0;
+  b.ey = ent.y;
+  return b;
 }
 
-// S^T = K Q^T for one 64-key sub-tile: s[kb][r] = S[query l32][key 32kb + 8(r/4) + 4hi + r%4],
-// operand reads issued 4 at a time ahead of their MFMAs; on partial sub-tiles
-// illegal pairs (and keys past len) become -inf.
-// With kDense, a partial sub-tile keeps the pairs whose key position lies in
-// the range dense_range gives the lane's query for entry word `ey`.
+// Direct-to-LDS copy of one 64-row sub-tile of K or V (one KV head): wave w
+// issues 4 buffer loads of 16 B per lane, load i filling rows 16i + 4w .. +3
+// (1 KiB, lane l at byte 16 l).  `voff` (per lane, loop-invariant) picks each
+// lane's source chunk so that the KiB holds the swizzled layout; the uniform
+// row offset rides in soffset.  The record count ends at the sub-tile's last
+// valid row, so rows past `len` arrive as zeros.  Byte offsets stay below
+// 2^32 (a key buffer holds fewer than 2^32 bytes).
+__device__ inline void dma_sub(const char* base, char* lds, const Sub& b, uint32_t row_bytes, uint32_t voff,
+                               int wave) {
+  // both values are uniform; readfirstlane keeps them in scalar registers (a
+  // descriptor or offset held in a vector register costs a waterfall loop)
+  const int nrec = __builtin_amdgcn_readfirstlane((int)((uint32_t)(b.k0 + b.len) * row_bytes));
+  const uint32_t so = (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)b.k0 * row_bytes));
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, nrec, kBufferFlags);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds + 4096 * i + 1024 * wave), 16, voff,
+                                             so + 16u * i * row_bytes, 0, 0);
+}
+
+// Mask data of key `lane` of a partial sub-tile (wave 0 stages it through a
+// register): the key's tracks, its interval (lo, hi) in the first two
+// fields, or with kDense its position alone.  Keys past len keep
+// (-1, -1, -1, 0): sample -1 and the empty range [-1, -1) admit no query;
+// with kDense they take position 2^31 - 1, outside every range.
 template <bool kDense>
-__device__ inline void scores(f32x16 (&s)[2], const char* sK, const bf16x8 (&qf)[8], const int4* sKT,
-                              const int4 qt, int32_t qc, bool partial, bool interval, int32_t window, int l32,
-                              int hi, int32_t ey, int row) {
-  __builtin_amdgcn_s_setprio(1);
+__device__ inline int4 key_data(const Sub& b, const int4* ktracks, const int2* kint, int lane) {
+  int4 kt = make_int4(kDense ? INT32_MAX : -1, -1, -1, 0);
+  if (lane < b.len) {
+    if (kDense) {
+      kt.x = ktracks[b.k0 + lane].w;
+    } else if (b.interval) {
+      const int2 iv = kint[b.k0 + lane];
+      kt = make_int4(iv.x, iv.y, 0, 0);
+    } else {
+      kt = ktracks[b.k0 + lane];
+    }
+  }
+  return kt;
+}
+
+// S^T = K Q^T for one staged 64-key sub-tile (unmasked):
+// s[kb][r] = S[query l32][key 32kb + 8(r/4) + 4hi + r%4].
+__device__ inline void qk(f32x16 (&s)[2], const char* sK, const bf16x8 (&qf)[8], int l32, int hi) {
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
     const int row = kb * 32 + l32;
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      bf16x8 kf[4];
+    for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) kf[kk] = as_bf16x8(*(const uint4*)(sK + k_slot(row, 2 * (4 * g + kk) + hi)));
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // 4 LDS reads
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // then 4 MFMAs
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[4 * g + kk], s[kb], 0, 0, 0);
-    }
+    for (int kk = 0; kk < 8; ++kk)
+      s[kb] = mfma(as_bf16x8(*(const uint4*)(sK + k_slot(row, 2 * kk + hi))), qf[kk], s[kb]);
   }
-  __builtin_amdgcn_s_setprio(0);
+}
+
+// Illegal pairs of a partial sub-tile (and keys past len) become -inf.  Every
+// lane of a half-wave reads the same key's data (an LDS broadcast); no branch
+// per element.  Key intervals: legal iff lo <= qc < hi (qc: the query's token
+// index, -1 on pad rows), one unsigned compare.  kDense: the key position
+// lies in the range dense_range gives the lane's query row `row` for the
+// entry word.
+template <bool kDense>
+__device__ inline void mask_sub(f32x16 (&s)[2], const int4* sT, const Sub& b, const int4 qt, int32_t qc,
+                                int32_t window, int hi, int row) {
   if (kDense) {
-    if (partial) {
-      int32_t dlo;
-      uint32_t dspan;
-      dense_range(ey, row, qt.w, window, dlo, dspan);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          s[kb][r] = (uint32_t)sKT[key].x - (uint32_t)dlo < dspan ? s[kb][r] : kNegInf;
-        }
-    }
-  } else if (partial && interval) {
-    // Key intervals: legal iff lo <= qc < hi (qc: the query's token index),
-    // one unsigned compare.
+    int32_t dlo;
+    uint32_t dspan;
+    dense_range(b.ey, row, qt.w, window, dlo, dspan);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-        const int2 iv = *(const int2*)&sKT[key];
-        s[kb][r] = (uint32_t)(qc - iv.x) < (uint32_t)(iv.y - iv.x) ? s[kb][r] : kNegInf;
+        s[kb][r] = (uint32_t)sT[key].x - (uint32_t)dlo < dspan ? s[kb][r] : kNegInf;
       }
-  } else if (partial) {
-    // Keys past len carry sample -1 and fail the sample test.  Every lane of
-    // a half-wave reads the same key track (an LDS broadcast); no branches.
+  } else if (b.interval) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-        s[kb][r] = legal(qt, sKT[key], window) ? s[kb][r] : kNegInf;
+        const int2 iv = *(const int2*)&sT[key];
+        s[kb][r] = in_interval(qc, iv.x, iv.y) ? s[kb][r] : kNegInf;
+      }
+  } else {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+        s[kb][r] = legal(qt, sT[key], window) ? s[kb][r] : kNegInf;
       }
   }
 }
 
-// p = 2^(s * scale_log2 + nbase) in place; returns the lane's sum of p.
-__device__ inline float exp_sum(f32x16 (&s)[2], float scale_log2, float nbase) {
-  float ls = 0.f;
+// Row max of the sub-tile's scores in base-2 units (-inf for a row with no
+// legal key): the lane's 32, then its partner half-wave's.
+__device__ inline float row_max(const f32x16 (&s)[2], float c) {
+  float m0 = kNegInf, m1 = kNegInf;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    m0 = fmaxf(m0, s[0][r]);
+    m1 = fmaxf(m1, s[1][r]);
+  }
+  const float mx = fmaxf(m0, m1);
+  return fmaxf(mx, __shfl_xor(mx, 32)) * c;
+}
+
+// p = 2^(s c + nbase) in place, and P^T as the B operand of 4 MFMAs of 16 keys.
+__device__ inline void exp_cvt(f32x16 (&s)[2], float c, float nbase, bf16x8 (&pb)[4]) {
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], scale_log2, nbase));
-      s[kb][r] = p;
-      ls += p;
-    }
-  return ls;
+    for (int r = 0; r < 16; ++r) s[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, nbase));
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pb[t][i] = (__bf16)s[t >> 1][8 * (t & 1) + i];
+}
+
+// The row's sum of p over the sub-tile (both half-waves).
+__device__ inline float row_sum(const f32x16 (&s)[2]) {
+  float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    a0 += s[0][r];
+    a1 += s[1][r];
+  }
+  const float ls = a0 + a1;
+  return ls + __shfl_xor(ls, 32);
+}
+
+// Lane constants of the V transpose reads.
+struct TrV {
+  int row0, chunk, off8;
+  __device__ inline explicit TrV(int lane) {
+    const int G = lane >> 4, jl = lane & 15;
+    row0 = 4 * (G >> 1) + (jl >> 2);
+    chunk = 2 * (G & 1) + ((jl & 3) >> 1);  // + 4 db
+    off8 = (jl & 1) * 8;
+  }
+};
+
+// O^T += V^T P^T over one staged sub-tile, 16 keys per MFMA (the 8 transpose
+// reads of a key group first).
+__device__ inline void pv(f32x16 (&acc)[4], const char* sV, const bf16x8 (&pb)[4], const TrV& tr) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int r0 = 16 * t + tr.row0;
+    bf16x8 vf[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+      vf[db] = lds_tr8(sV + v_slot(r0, 4 * db + tr.chunk) + tr.off8, sV + v_slot(r0 + 8, 4 * db + tr.chunk) + tr.off8);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) acc[db] = mfma(vf[db], pb[t], acc[db]);
+  }
+}
+
+// Lazy reference: when some row's max mt (base 2) exceeds its reference by
+// more than 2^kGrowth, every row whose max is above its reference moves the
+// reference there and rescales O_acc and l by 2^(old - new) (0 from -inf).
+// O_acc and l always share one reference, so the result is exact either way.
+__device__ inline void move_reference(float mt, float& mref, float& lrun, f32x16 (&acc)[4], float& nbase) {
+  if (__any(mt > mref + kGrowth)) {
+    const float mnew = fmaxf(mref, mt);
+    const float alpha = mnew == mref ? 1.f : __builtin_amdgcn_exp2f(mref - mnew);
+    lrun *= alpha;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+    mref = mnew;
+    nbase = mref == kNegInf ? 0.f : -mref;
+  }
 }
 
 template <bool kDense>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a) {
-  __shared__ __attribute__((aligned(1024))) char sK[kSub * 256];
-  __shared__ __attribute__((aligned(1024))) char sV[kSub * 256];
-  __shared__ int4 sKT[kSub];
+  __shared__ __attribute__((aligned(1024))) char sK0[kSub * 256];
+  __shared__ __attribute__((aligned(1024))) char sK1[kSub * 256];
+  __shared__ __attribute__((aligned(1024))) char sV0[kSub * 256];
+  __shared__ __attribute__((aligned(1024))) char sV1[kSub * 256];
+  __shared__ int4 sT0[kSub];
+  __shared__ int4 sT1[kSub];
   __shared__ int2 sEnt[kListCache];
 
   int32_t item, h;
@@ -230,12 +276,14 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a) {
   if (item < 0) return;
   // Prologue in two memory round trips: the item record and its first list
   // entry (scalar loads, side by side), then every other load at once: the
-  // list, the first K/V sub-tile, Q, the query tracks and the state.
+  // list, K of sub-tiles 0 and 1 and V of sub-tile 0 (the two halves of the
+  // first entry), their mask data, Q, the query tracks and the state.
   int4 it = a.items[item];
   if (a.step_only) it.y = kFirst | kLast;  // this step's keys alone
   int2 ent = a.first[item];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // the item's list goes to LDS in chunks of kListCache entries, so the loop
   // never waits on a memory load for it (two entries per thread)
   const int nl = it.w < kListCache ? it.w : kListCache;
@@ -251,20 +299,25 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a) {
   const uint32_t row_bytes = (uint32_t)a.hkv * kHeadDim * 2u;
   const char* kbase = (const char*)(a.k + (int64_t)kvh * kHeadDim);
   const char* vbase = (const char*)(a.v + (int64_t)kvh * kHeadDim);
-  const int nsub = 2 * it.w;
+  // source chunk of this lane's 16 bytes in each direct-to-LDS load: row
+  // 16i + rw of the sub-tile, slot lane % 16
+  const int rw = 4 * wave + (lane >> 4);
+  const uint32_t koff = (uint32_t)rw * row_bytes + 16u * (uint32_t)((lane & 15) ^ (rw & 15));
+  const uint32_t voff = (uint32_t)rw * row_bytes + 16u * (uint32_t)((lane & 15) ^ ((rw & 3) << 2));
+  const float c = a.scale_log2;
 
-  // prologue: fetch the first sub-tile, then Q and the state
-  SubTile pf;
-  const uint32_t lane_off = (uint32_t)(tid >> 4) * row_bytes + (uint32_t)(tid & 15) * 16u;
   ent.x = __builtin_amdgcn_readfirstlane(ent.x);
   ent.y = __builtin_amdgcn_readfirstlane(ent.y);
-  {
-    int32_t k0;
-    int len;
-    bool part, kin;
-    sub_bounds(ent, 0, k0, len, part, kin);
-    fetch_sub<kDense>(pf, kbase, vbase, a.ktracks, a.kint, k0, len, part, kin, row_bytes, lane_off, tid);
+  const Sub b0 = sub_of(ent, 0), b1 = sub_of(ent, 1);
+  const bool stage0 = b0.partial && wave == 0;
+  int4 t0 = make_int4(0, 0, 0, 0), t1 = make_int4(0, 0, 0, 0);
+  if (stage0) {
+    t0 = key_data<kDense>(b0, a.ktracks, a.kint, lane);
+    t1 = key_data<kDense>(b1, a.ktracks, a.kint, lane);
   }
+  dma_sub(kbase, sK0, b0, row_bytes, koff, wave);
+  dma_sub(vbase, sV0, b0, row_bytes, voff, wave);
+  dma_sub(kbase, sK1, b1, row_bytes, koff, wave);
 
   // Q^T as the B operand: lane holds query l32, channels [16kk + 8hi, +8).
   bf16x8 qf[8];
@@ -305,109 +358,80 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a) {
   }
   if (tid < nl) sEnt[tid] = le0;
   if (tid + 256 < nl) sEnt[tid + 256] = le1;
-  store_sub(pf, sK, sV, sKT, tid);
-  // Drain every prologue load here, once: a register loaded before the loop
-  // with a load still pending would make each iteration's first use of it
-  // wait on the memory counter, i.e. on the in-flight prefetch as well.
+  if (stage0) {
+    sT0[lane] = t0;
+    sT1[lane] = t1;
+  }
+  // Drain every prologue load here, once (the direct-to-LDS loads included).
   __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 
-  // lane constants of the V transpose reads
-  const int G = lane >> 4, jl = lane & 15;
-  const int tr_row0 = 4 * (G >> 1) + (jl >> 2);
-  const int tr_chunk = 2 * (G & 1) + ((jl & 3) >> 1);  // + 4 db
-  const int tr_off8 = (jl & 1) * 8;
+  const TrV tr(lane);
+  float nbase = mref == kNegInf ? 0.f : -mref;
+  f32x16 s0[2], s1[2];
+  qk(s0, sK0, qf, l32, hi);
+  if (b0.partial) mask_sub<kDense>(s0, sT0, b0, qt, qc, a.window, hi, (int)qi);
+  move_reference(row_max(s0, c), mref, lrun, acc, nbase);
 
-  for (int n = 0; n < nsub; ++n) {
-    int32_t k0;
-    int len;
-    bool partial, interval;
-    sub_bounds(ent, n, k0, len, partial, interval);
-    const int32_t ey = ent.y;
-    __syncthreads();  // sub-tile n is in LDS
-    const bool more = n + 1 < nsub;
+  // Sub-tiles in pairs (2e, 2e + 1) = the halves of entry e.  Buffers: K of
+  // even sub-tiles in sK0, odd in sK1; V and mask data likewise.  At the top
+  // of iteration n, S(n) is in registers (masked, reference moved), K(n+1),
+  // V(n) and the mask data of n+1 are in LDS.
+  int2 entE = ent;
+  for (int e = 0; e < it.w; ++e) {
+    const bool more = e + 1 < it.w;  // sub-tiles 2e + 2 and 2e + 3 exist
+    __syncthreads();  // every wave is done with sub-tile 2e - 1's V, 2e's K and mask data
+    int2 entF = entE;
     if (more) {
-      if (n & 1) {
-        const int e1 = (n + 1) >> 1;
-        if (e1 % kListCache == 0) {  // next chunk of the list (long lists only)
-          for (int i = tid; i < kListCache && e1 + i < it.w; i += 256) sEnt[i] = a.entries[it.z + e1 + i];
-          __syncthreads();
-        }
-        ent = sEnt[e1 % kListCache];
-        ent.x = __builtin_amdgcn_readfirstlane(ent.x);
-        ent.y = __builtin_amdgcn_readfirstlane(ent.y);
+      const int e1 = e + 1;
+      if (e1 % kListCache == 0) {  // next chunk of the list (long lists only)
+        for (int i = tid; i < kListCache && e1 + i < it.w; i += 256) sEnt[i] = a.entries[it.z + e1 + i];
+        __syncthreads();
       }
-      int32_t nk0;
-      int nlen;
-      bool npart, nkin;
-      sub_bounds(ent, n + 1, nk0, nlen, npart, nkin);
-      fetch_sub<kDense>(pf, kbase, vbase, a.ktracks, a.kint, nk0, nlen, npart, nkin, row_bytes, lane_off, tid);
+      entF = sEnt[e1 % kListCache];
+      entF.x = __builtin_amdgcn_readfirstlane(entF.x);
+      entF.y = __builtin_amdgcn_readfirstlane(entF.y);
     }
-
-    f32x16 s[2];
-    scores<kDense>(s, sK, qf, sKT, qt, qc, partial, interval, a.window, l32, hi, ey, (int)qi);
-
-    // Online softmax in base-2 units against a lazily updated reference mref.
-    // Common case: exponentiate against the current reference; every p stays
-    // below 2^12 whenever the lane's sum does, and then nothing moves.  When a
-    // row has no reference yet, or a lane's sum reaches 2^12 (the scores are
-    // then recomputed: K is still in LDS), the wave takes the tile's row
-    // maxima, moves the references and rescales O_acc and l.  Exact either
-    // way: O_acc and l always share one reference.
-    float ls;
-    bool fast = !__any(mref == kNegInf);
-    if (fast) {
-      ls = exp_sum(s, a.scale_log2, -mref);
-      if (__any(!(ls < kSumCap))) {
-        fast = false;
-        scores<kDense>(s, sK, qf, sKT, qt, qc, partial, interval, a.window, l32, hi, ey, (int)qi);
+    {  // n = 2e: S(n) in s0
+      const Sub bn = sub_of(entE, 1), bl = sub_of(entF, 0);  // sub-tiles n + 1, n + 2
+      const bool stage = more && bl.partial && wave == 0;
+      int4 tl = make_int4(0, 0, 0, 0);
+      if (stage) tl = key_data<kDense>(bl, a.ktracks, a.kint, lane);
+      if (more) dma_sub(kbase, sK0, bl, row_bytes, koff, wave);
+      dma_sub(vbase, sV1, bn, row_bytes, voff, wave);
+      bf16x8 pb[4];
+      qk(s1, sK1, qf, l32, hi);
+      exp_cvt(s0, c, nbase, pb);
+      pv(acc, sV0, pb, tr);
+      lrun += row_sum(s0);
+      if (bn.partial) mask_sub<kDense>(s1, sT1, bn, qt, qc, a.window, hi, (int)qi);
+      move_reference(row_max(s1, c), mref, lrun, acc, nbase);
+      if (stage) sT0[lane] = tl;
+      __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's loads of K(n+2), V(n+1) have landed
+    }
+    __syncthreads();  // every wave is done with sub-tile 2e's V, 2e + 1's K and mask data
+    {  // n = 2e + 1: S(n) in s1
+      const Sub bn = sub_of(entF, 0), bl = sub_of(entF, 1);  // sub-tiles n + 1, n + 2 (when more)
+      const bool stage = more && bl.partial && wave == 0;
+      int4 tl = make_int4(0, 0, 0, 0);
+      if (stage) tl = key_data<kDense>(bl, a.ktracks, a.kint, lane);
+      if (more) {
+        dma_sub(kbase, sK1, bl, row_bytes, koff, wave);
+        dma_sub(vbase, sV0, bn, row_bytes, voff, wave);
       }
-    }
-    if (!fast) {
-      float mx = kNegInf;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
-      const float mnew = fmaxf(mref, mx);
-      // 1 when this row's reference stays (also when it is still -inf), 0 from -inf
-      const float alpha = mnew == mref ? 1.f : __builtin_amdgcn_exp2f(mref - mnew);
-      lrun *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
-      mref = mnew;
-      ls = exp_sum(s, a.scale_log2, mref == kNegInf ? 0.f : -mref);
-    }
-    ls += __shfl_xor(ls, 32);
-    lrun += ls;
-    bf16x8 pb[4];  // P^T as the B operand of 4 MFMAs of 16 keys each
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) pb[t][i] = (__bf16)s[t >> 1][8 * (t & 1) + i];
-
-    // O^T += V^T P^T, 16 keys per MFMA (the 4 operand reads of a key group first)
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int r0 = 16 * t + tr_row0;
-      bf16x8 vf[4];
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const char* p0 = sV + v_slot(r0, 4 * db + tr_chunk) + tr_off8;
-        const char* p1 = sV + v_slot(r0 + 8, 4 * db + tr_chunk) + tr_off8;
-        vf[db] = lds_tr8(p0, p1);
+      bf16x8 pb[4];
+      if (more) qk(s0, sK0, qf, l32, hi);
+      exp_cvt(s1, c, nbase, pb);
+      pv(acc, sV1, pb, tr);
+      lrun += row_sum(s1);
+      if (more) {
+        if (bn.partial) mask_sub<kDense>(s0, sT0, bn, qt, qc, a.window, hi, (int)qi);
+        move_reference(row_max(s0, c), mref, lrun, acc, nbase);
       }
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);  // 8 transpose reads
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);  // then 4 MFMAs
-#pragma unroll
-      for (int db = 0; db < 4; ++db) acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], pb[t], acc[db], 0, 0, 0);
+      if (stage) sT1[lane] = tl;
+      __builtin_amdgcn_s_waitcnt(0x0f70);
     }
-    __builtin_amdgcn_s_setprio(0);
-    __syncthreads();  // every wave is done with sub-tile n
-    if (more) store_sub(pf, sK, sV, sKT, tid);
+    entE = entF;
   }
 
   if (!qvalid) return;
@@ -436,7 +460,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a) {
       for (int i = 0; i < 4; ++i) {
         __bf16 b4[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) b4[c] = (__bf16)(acc[db][4 * i + c] * rl);
+        for (int cc = 0; cc < 4; ++cc) b4[cc] = (__bf16)(acc[db][4 * i + cc] * rl);
         *(uint2*)(out + db * 32 + i * 8 + hi * 4) = __builtin_bit_cast(uint2, b4);
       }
     if (hi == 0) a.lse[sidx] = any ? (mref + __log2f(lrun)) * kLn2 : kNegInf;

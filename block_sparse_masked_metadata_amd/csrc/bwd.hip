@@ -69,20 +69,50 @@ __device__ inline void two_products(f32x16& s, f32x16& dp, const char* ta, const
   }
 }
 
+constexpr int kBufferFlags = 0x00020000;  // buffer descriptor word 3: 32-bit data format, untyped loads
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Direct-to-LDS copy of one 64-row sub-tile of K or V (one KV head) into the
+// tile_slot layout: wave w issues 4 buffer loads of 16 B per lane, load i
+// filling rows 16i + 4w .. +3 (1 KiB, lane l at byte 16 l).  Row r = 16i +
+// 4w + l/16 has r % 4 = l/16 and (r / 4) % 4 = w, so the slot-to-chunk map,
+// and with it each lane's source offset `voff`, is the same for every load.
+// The record count ends at the sub-tile's last valid row, so rows past `len`
+// arrive as zeros.  Both values are uniform; readfirstlane keeps them in
+// scalar registers (one in a vector register costs a waterfall loop).  Byte
+// offsets stay below 2^32 (a key buffer holds fewer than 2^32 bytes).
+__device__ inline void dma_tile(const char* base, char* lds, int64_t r0, int len, uint32_t row_bytes, uint32_t voff,
+                                int wave) {
+  const int nrec = __builtin_amdgcn_readfirstlane((int)((uint32_t)(r0 + len) * row_bytes));
+  const uint32_t so = (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)r0 * row_bytes));
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, nrec, kBufferFlags);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds + 4096 * i + 1024 * wave), 16, voff,
+                                             so + 16u * i * row_bytes, 0, 0);
+}
+
 // kDense: dense-call lists (entries carry a relation and query rows; the
 // staged key data is the key's position, 2^31 - 1 past the valid rows).
+// K and V sub-tiles reach LDS by direct-to-LDS loads into two buffers each
+// (sub-tile n in set n % 2): the loads of sub-tile n + 1 fly while n
+// computes, one workgroup barrier per sub-tile.
 template <bool kDense>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
-  __shared__ __attribute__((aligned(1024))) char sK[kSub * 256];
-  __shared__ __attribute__((aligned(1024))) char sV[kSub * 256];
-  __shared__ int4 sKT[kSub];
+  __shared__ __attribute__((aligned(1024))) char sK0[kSub * 256];
+  __shared__ __attribute__((aligned(1024))) char sK1[kSub * 256];
+  __shared__ __attribute__((aligned(1024))) char sV0[kSub * 256];
+  __shared__ __attribute__((aligned(1024))) char sV1[kSub * 256];
+  __shared__ int4 sKT0[kSub];
+  __shared__ int4 sKT1[kSub];
   __shared__ int2 sEnt[kListCache];
 
   int32_t item, h;
   map_block((int32_t)blockIdx.x, a.nitems, a.hq, a.heads_per_xcd, item, h);
   if (item < 0) return;
   const int4 it = a.items[item];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   const int64_t qrow = (int64_t)it.x * kTile + wave * 32 + l32;
   const bool qvalid = qrow < a.rows;
@@ -91,21 +121,27 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
   const char* kbase = (const char*)(a.k + (int64_t)kvh * kHeadDim);
   const char* vbase = (const char*)(a.v + (int64_t)kvh * kHeadDim);
   const int nsub = 2 * it.w;
+  // this lane's source chunk in each direct-to-LDS load (tile_slot layout)
+  const int rw = 4 * wave + (lane >> 4);
+  const uint32_t voff = (uint32_t)rw * row_bytes + 16u * (uint32_t)((lane & 15) ^ (4 * (lane >> 4) + wave));
 
   int list_base = 0;
 
   // prologue: the first sub-tile, Q, dO, the row scalars, the first key data
   // and the list window are all issued before anything uses a loaded value,
   // into registers that nothing else writes, so it takes one memory round
-  // trip.  An invalid query row reads the tile's first row (always present)
-  // and is replaced afterwards; its p is 0 through the -inf LSE.
-  PairStage pf;
+  // trip after the first list entry.  An invalid query row reads the tile's
+  // first row (always present) and is replaced afterwards; its p is 0 through
+  // the -inf LSE.
   int2 ent = a.entries[it.z];
+  ent.x = __builtin_amdgcn_readfirstlane(ent.x);
+  ent.y = __builtin_amdgcn_readfirstlane(ent.y);
   int64_t r0f;
   int lenf;
   bool partf;
   sub_bounds(ent, 0, r0f, lenf, partf);
-  pf.fetch(kbase, vbase, r0f, lenf, row_bytes, tid);
+  dma_tile(kbase, sK0, r0f, lenf, row_bytes, voff, wave);
+  dma_tile(vbase, sV0, r0f, lenf, row_bytes, voff, wave);
   const int64_t qr = qvalid ? qrow : (int64_t)it.x * kTile;
   bf16x8 qf[8], df[8];
   {
@@ -141,12 +177,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
   const float dl = qvalid ? dl_raw : 0.f;
   const int4 qt = query_tracks(qvalid ? qt_raw : make_int4(0, -1, -1, 0));
   const int32_t qc = qvalid ? qc_raw : -1;  // the query's token index (key-interval coordinate)
-  int4 kt_pf = make_int4(kDense ? INT32_MAX : -1, -1, -1, 0);  // keys past len: sample -1, empty range
+  int4 kt0 = make_int4(kDense ? INT32_MAX : -1, -1, -1, 0);  // keys past len: sample -1, empty range
   if (kload && tid < lenf) {
     if (kDense)
-      kt_pf.x = kraw.x;
+      kt0.x = kraw.x;
     else
-      kt_pf = kinterval ? make_int4(kraw.x, kraw.y, 0, 0) : kraw;
+      kt0 = kinterval ? make_int4(kraw.x, kraw.y, 0, 0) : kraw;
   }
 
   f32x16 acc[4];  // dQ^T[d = 32db + 8(r/4) + 4hi + r%4][query l32], unscaled
@@ -154,34 +190,41 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
-  pf.store(sK, sV, tid);
-  if (tid < kSub) sKT[tid] = kt_pf;
-  __builtin_amdgcn_s_waitcnt(0);  // no load is pending when the loop starts
+  if (tid < kSub) sKT0[tid] = kt0;
+  __builtin_amdgcn_s_waitcnt(0);  // no load is pending when the loop starts (direct-to-LDS ones included)
+  __syncthreads();
   const TrLane tr(lane);
 
-  for (int n = 0; n < nsub; ++n) {
+  // Sub-tile n from buffer set (sK, sV, sKT); the loads of n + 1 go to the
+  // other set (nK, nV, nKT), which every wave finished with before the
+  // barrier that precedes this call.
+  auto step = [&](int n, const char* sK, const char* sV, const int4* sKT, char* nK, char* nV, int4* nKT) {
     int64_t r0;
     int len;
     bool partial;
     sub_bounds(ent, n, r0, len, partial);
     const bool interval = (ent.y & kIntervalBit) != 0;
     const int32_t ey = ent.y;
-    __syncthreads();  // sub-tile n is in LDS
     const bool more = n + 1 < nsub;
+    int4 kt_pf = make_int4(kDense ? INT32_MAX : -1, -1, -1, 0);  // keys past len: sample -1, empty range
     if (more) {
-      if (n & 1) ent = list_entry(sEnt, list_base, a.entries, it, (n + 1) >> 1, tid);
+      if (n & 1) {
+        ent = list_entry(sEnt, list_base, a.entries, it, (n + 1) >> 1, tid);
+        ent.x = __builtin_amdgcn_readfirstlane(ent.x);
+        ent.y = __builtin_amdgcn_readfirstlane(ent.y);
+      }
       int64_t nr0;
       int nlen;
       bool npart;
       sub_bounds(ent, n + 1, nr0, nlen, npart);
-      kt_pf = make_int4(kDense ? INT32_MAX : -1, -1, -1, 0);  // keys past len: sample -1, empty range
       if (npart && tid < nlen) {
         if (kDense)
           kt_pf.x = a.ktracks[nr0 + tid].w;
         else
           kt_pf = key_mask_data(a.ktracks, a.kint, nr0 + tid, (ent.y & kIntervalBit) != 0);
       }
-      pf.fetch(kbase, vbase, nr0, nlen, row_bytes, tid);
+      dma_tile(kbase, nK, nr0, nlen, row_bytes, voff, wave);
+      dma_tile(vbase, nV, nr0, nlen, row_bytes, voff, wave);
     }
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
@@ -227,11 +270,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
         for (int db = 0; db < 4; ++db) acc[db] = mfma(tr.read(sK, kc * 32 + 16 * hf, db), dsb, acc[db]);
       }
     }
-    __syncthreads();  // every wave is done with sub-tile n
-    if (more) {
-      pf.store(sK, sV, tid);
-      if (tid < kSub) sKT[tid] = kt_pf;
-    }
+    if (more && tid < kSub) nKT[tid] = kt_pf;
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's loads of sub-tile n + 1 have landed
+    __syncthreads();  // sub-tile n + 1 is in LDS; every wave is done with sub-tile n
+  };
+  for (int n = 0; n < nsub; n += 2) {
+    step(n, sK0, sV0, sKT0, sK1, sV1, sKT1);
+    step(n + 1, sK1, sV1, sKT1, sK0, sV0, sKT0);
   }
 
   if (!qvalid) return;

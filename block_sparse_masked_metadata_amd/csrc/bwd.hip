@@ -314,10 +314,14 @@ struct RowStage {
 // of the tile they apply to).
 template <bool kDense>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
-  // two buffer sets: sub-tile m computes from set m % 2 while m + 1 is staged
-  // into the other, one barrier per sub-tile
-  __shared__ __attribute__((aligned(1024))) char sQ[2][kSub * 256];
-  __shared__ __attribute__((aligned(1024))) char sO[2][kSub * 256];
+  // two buffer sets: sub-tile m computes from set m % 2 while m + 1 is
+  // loaded into the other, one barrier per sub-tile.  Q and dO reach LDS by
+  // direct-to-LDS loads (each set its own array, so the compiler tells a load
+  // into one from reads of the other); the row scalars go through registers.
+  __shared__ __attribute__((aligned(1024))) char sQ0[kSub * 256];
+  __shared__ __attribute__((aligned(1024))) char sQ1[kSub * 256];
+  __shared__ __attribute__((aligned(1024))) char sO0[kSub * 256];
+  __shared__ __attribute__((aligned(1024))) char sO1[kSub * 256];
   __shared__ __attribute__((aligned(16))) float sL[2][kSub];
   __shared__ __attribute__((aligned(16))) float sD[2][kSub];
   __shared__ int4 sQT[2][kSub];
@@ -330,7 +334,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
   // query head of the group (a split list cuts long lists into such ranges)
   const int4 wk = a.work ? a.work[unit] : make_int4(unit, 0, -1, -1);
   const int4 it = a.items[wk.x];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   const int64_t key = (int64_t)it.x + wave * 32 + l32;  // it.x: the tile's first key row
   const bool kvalid = wave * 32 + l32 < key_rows(it.y);
@@ -345,14 +350,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
   // token index against it (staged in place of the query tracks)
   const bool kin = (it.y & kKeyInterval) != 0;
 
-  // Stage (head g*grp + m/nsub, sub-tile m%nsub) into registers.
-  PairStage pf;
+  // this lane's source chunk in each direct-to-LDS load (tile_slot layout)
+  const int rw = 4 * wave + (lane >> 4);
+  const uint32_t voff = (uint32_t)rw * row_bytes + 16u * (uint32_t)((lane & 15) ^ (4 * (lane >> 4) + wave));
+  // Load (head g*grp + m/nsub, sub-tile m%nsub): Q and dO into buffer set
+  // (dq, ddo) by direct-to-LDS loads, the row scalars into registers.
   RowStage rs;
   int2 ent;
   bool cur_partial = false, nxt_partial = false;
   int cur_len = 0, nxt_len = 0;
   int32_t cur_ey = 0, nxt_ey = 0;  // entry words (dense-call relation and key rows)
-  auto fetch = [&](int m, int2 e2) {
+  auto fetch = [&](int m, int2 e2, char* dq_, char* ddo) {
     const int32_t h = g * grp + m / nsub;
     int64_t r0;
     sub_bounds(e2, n0 + m % nsub, r0, nxt_len, nxt_partial);
@@ -372,11 +380,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
       else
         rs.t = a.qtracks[r0 + row];
     }
-    pf.fetch((const char*)(a.q + (int64_t)h * kHeadDim), (const char*)(a.dout + (int64_t)h * kHeadDim),
-             r0, nxt_len, row_bytes, tid);
+    dma_tile((const char*)(a.q + (int64_t)h * kHeadDim), dq_, r0, nxt_len, row_bytes, voff, wave);
+    dma_tile((const char*)(a.dout + (int64_t)h * kHeadDim), ddo, r0, nxt_len, row_bytes, voff, wave);
   };
   auto stage = [&](int buf) {
-    pf.store(sQ[buf], sO[buf], tid);
     if (tid < kSub) sL[buf][tid] = tid < nxt_len ? -rs.v * kLog2e : kNegInf;
     else if (tid < 2 * kSub) sD[buf][tid - kSub] = rs.v;
     else if (tid < 3 * kSub) sQT[buf][tid - 2 * kSub] = query_tracks(rs.t);
@@ -412,7 +419,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
     kraw = a.ktracks[krow];
   }
   ent = a.entries[it.z + (n0 >> 1)];
-  fetch(0, ent);
+  ent.x = __builtin_amdgcn_readfirstlane(ent.x);
+  ent.y = __builtin_amdgcn_readfirstlane(ent.y);
+  fetch(0, ent, sQ0, sO0);
   for (int i = tid; i < it.w && i < kListCache; i += 256) sEnt[i] = a.entries[it.z + i];
   const int4 kt = kvalid ? kraw : make_int4(-1, -1, -1, 0);
   f32x16 dk[4], dv[4];  // dK^T / dV^T[d = 32db + 8(r/4) + 4hi + r%4][key]
@@ -427,7 +436,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
   cur_len = nxt_len;
   cur_partial = nxt_partial;
   cur_ey = nxt_ey;
-  __builtin_amdgcn_s_waitcnt(0);  // no load is pending when the loop starts
+  __builtin_amdgcn_s_waitcnt(0);  // no load is pending when the loop starts (direct-to-LDS ones included)
+  __syncthreads();
   const TrLane tr(lane);
 
   // P = exp2(S * scale*log2(e) - LSE*log2(e)) and dS = P (dP - delta) for the
@@ -494,37 +504,50 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
       }
   };
 
-  for (int m = 0; m < total; ++m) {
+  // Sub-tile m computes from set (cq, co, cb); the loads of m + 1 go to the
+  // other set (nq, no), which every wave finished with before the barrier
+  // that precedes this call.
+  auto step = [&](int m, const char* cq, const char* co, int cb, char* nq, char* no) {
     const bool partial = cur_partial;
     const int32_t ey = cur_ey;
-    const int cb = m & 1;
-    __syncthreads();  // sub-tile m is in LDS; every wave is done with m - 1
     const bool more = m + 1 < total;
     if (more) {
       // next sub-tile n0 + (m + 1) % nsub: a new list entry at an even
       // sub-tile, and at the start of the next head's range
       const int r1 = (m + 1) % nsub, n1 = n0 + r1;
-      if ((n1 & 1) == 0 || r1 == 0) ent = list_entry(sEnt, list_base, a.entries, it, n1 >> 1, tid);
-      fetch(m + 1, ent);
+      if ((n1 & 1) == 0 || r1 == 0) {
+        ent = list_entry(sEnt, list_base, a.entries, it, n1 >> 1, tid);
+        ent.x = __builtin_amdgcn_readfirstlane(ent.x);
+        ent.y = __builtin_amdgcn_readfirstlane(ent.y);
+      }
+      fetch(m + 1, ent, nq, no);
     }
     // The two 32-query halves qc are software-pipelined inside the wave: the
     // S and dP MFMAs of half 1 run while the vector unit builds P and dS of
     // half 0, and the dV/dK MFMAs of half 0 while it builds those of half 1.
     f32x16 s0, dp0, s1, dp1;
     bf16x8 pb0[2], ds0[2], pb1[2], ds1[2];
-    two_products(s0, dp0, sQ[cb], sO[cb], l32, kf, vf, hi);
-    two_products(s1, dp1, sQ[cb], sO[cb], 32 + l32, kf, vf, hi);
+    two_products(s0, dp0, cq, co, l32, kf, vf, hi);
+    two_products(s1, dp1, cq, co, 32 + l32, kf, vf, hi);
     p_and_ds(s0, dp0, pb0, ds0, 0, partial, sL[cb], sD[cb], sQT[cb], ey);
-    accumulate(pb0, ds0, 0, sQ[cb], sO[cb]);
+    accumulate(pb0, ds0, 0, cq, co);
     p_and_ds(s1, dp1, pb1, ds1, 32, partial, sL[cb], sD[cb], sQT[cb], ey);
-    accumulate(pb1, ds1, 32, sQ[cb], sO[cb]);
+    accumulate(pb1, ds1, 32, cq, co);
     if (more) {
       stage(cb ^ 1);  // the other set was last read in iteration m - 1
       cur_len = nxt_len;
       cur_partial = nxt_partial;
       cur_ey = nxt_ey;
     }
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's loads of sub-tile m + 1 have landed
+    __syncthreads();  // sub-tile m + 1 is in LDS; every wave is done with m
+  };
+  int m = 0;
+  for (; m + 1 < total; m += 2) {
+    step(m, sQ0, sO0, 0, sQ1, sO1);
+    step(m + 1, sQ1, sO1, 1, sQ0, sO0);
   }
+  if (m < total) step(m, sQ0, sO0, 0, sQ1, sO1);
 
   if (!kvalid) return;
   if (wk.w >= 0) {

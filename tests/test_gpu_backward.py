@@ -6,7 +6,7 @@ import torch
 import block_sparse_masked_metadata_amd as bsm
 from workloads import random_small, sliding_window, long_mixed, packed_multimodal
 from oracle import backward as obwd
-from gpu_common import Case, grad_ok, needs_gpu
+from gpu_common import Case, check_rows, grad_ok, needs_gpu
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not needs_gpu, reason="needs a GPU")]
 
@@ -56,6 +56,27 @@ def test_random_layouts_backward(seed):
     lay.hq, lay.hkv, lay.d = [(4, 2), (2, 2), (6, 3), (4, 1)][seed] + (128,)
     for r in range(ranks):
         _check_full(Case(lay, rank=r, with_do=True))
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_ragged_shards_forward_and_backward(seed):
+    """Shards that are not multiples of 128 rows: the last tile of every shard
+    is ragged, and with S % 128 <= 64 its second 64-row half has no valid row
+    (the sub-tile the kernels stage as zeros by the record count).  O/LSE,
+    dQ and dK/dV of every rank against the oracle, several GQA ratios."""
+    rng = np.random.default_rng(1700 + seed)
+    ranks = [2, 3, 1, 4][seed]
+    S = [164, 100, 37, 230][seed]
+    lay = random_small(rng, S * ranks, max_span=120)
+    lay.ranks, lay.order, lay.seed = ranks, "contiguous", 80 + seed  # block orders need whole blocks
+    lay.hq, lay.hkv, lay.d = [(4, 2), (3, 1), (2, 2), (8, 4)][seed] + (128,)
+    for r in range(ranks):
+        case = Case(lay, rank=r, with_do=True)
+        assert case.S == S
+        o, lse, _ = case.ring()
+        torch.cuda.synchronize()
+        check_rows(case, o, lse)
+        _check_full(case)
 
 
 def test_sliding_window_scaled_full_backward():

@@ -180,6 +180,18 @@ __device__ inline void mask_sub(f32x16 (&s)[2], const int4* sT, const Sub& b, co
   }
 }
 
+// The two half-waves' values of x side by side, on the vector unit (gfx950
+// v_permlane32_swap trades the upper half of its first operand with the lower
+// half of its second): lo holds lanes 0-31 of x in both halves, hi lanes
+// 32-63, so a symmetric function of (lo, hi) is the pair's value in every
+// lane, with the same operand order in both halves.  The s_nop keeps the two
+// wait states the instruction needs after a vector write of its operands.
+__device__ inline void half_pair(float x, float& lo, float& hi) {
+  lo = x;
+  hi = x;
+  asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(lo), "+v"(hi));
+}
+
 // Row max of the sub-tile's scores in base-2 units (-inf for a row with no
 // legal key): the lane's 32, then its partner half-wave's.
 __device__ inline float row_max(const f32x16 (&s)[2], float c) {
@@ -189,8 +201,9 @@ __device__ inline float row_max(const f32x16 (&s)[2], float c) {
     m0 = fmaxf(m0, s[0][r]);
     m1 = fmaxf(m1, s[1][r]);
   }
-  const float mx = fmaxf(m0, m1);
-  return fmaxf(mx, __shfl_xor(mx, 32)) * c;
+  float lo, hi;
+  half_pair(fmaxf(m0, m1), lo, hi);
+  return fmaxf(lo, hi) * c;
 }
 
 // p = 2^(s c + nbase) in place, and P^T as the B operand of 4 MFMAs of 16 keys.
@@ -213,8 +226,9 @@ __device__ inline float row_sum(const f32x16 (&s)[2]) {
     a0 += s[0][r];
     a1 += s[1][r];
   }
-  const float ls = a0 + a1;
-  return ls + __shfl_xor(ls, 32);
+  float lo, hi;
+  half_pair(a0 + a1, lo, hi);
+  return lo + hi;
 }
 
 // Lane constants of the V transpose reads.

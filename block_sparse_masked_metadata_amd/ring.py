@@ -348,8 +348,40 @@ def bwd_step(dp: DevicePlan, s, hd, q, k, v, dout, lse, delta, dq, dk, dv, works
                           workspace.numel() * workspace.element_size(), _stream())
 
 
+# A dK/dV unit (one key tile and KV head) loops over the query tiles that
+# reach it.  When some step's units average more legal queries per key than
+# this, the units fill the chip for several rounds at one workgroup per CU and
+# a concurrent dK/dV launch of the next step takes CUs from those rounds; below
+# it the launches are short and overlapping two of them fills their tails.
+SHORT_UNIT_QUERIES = 4096
+
+
+def kv_side_streams(dp: DevicePlan):
+    """How many side streams the dK/dV launches of a backward should alternate
+    between: 2 when every step's units are short (see SHORT_UNIT_QUERIES), else 1."""
+    items, pairs = dp.info["bwd_items"], dp.info["step_pairs"]
+    longest = max((pairs[s] / (128.0 * items[s]) for s in range(dp.ranks) if items[s] > 0), default=0.0)
+    return 2 if longest <= SHORT_UNIT_QUERIES else 1
+
+
+_SIDE_STREAMS = {}
+
+
+def _side_streams(device, n):
+    """The first n of two side streams kept per device for the dK/dV launches.
+    Streams share the device's few hardware queues; one taken afresh per call
+    can land on the current stream's queue and run behind its work, so the
+    same ones serve every call."""
+    import torch
+    idx = torch.device(device).index
+    idx = torch.cuda.current_device() if idx is None else idx
+    if idx not in _SIDE_STREAMS:
+        _SIDE_STREAMS[idx] = [torch.cuda.Stream(device=idx) for _ in range(2)]
+    return _SIDE_STREAMS[idx][:n]
+
+
 def bwd_ring(dp: DevicePlan, hd, q, k_shards, v_shards, dout, o, lse, grads=None, steps=None,
-             split=True, two_streams=True):
+             split=True, two_streams=True, kv_streams=None):
     """Backward over ring steps s = 0..R-1.  Returns (dq, dk_shards, dv_shards) in fp32.
 
     dk/dv shards are accumulated (+=) by the kernels: they are cleared here
@@ -358,7 +390,11 @@ def bwd_ring(dp: DevicePlan, hd, q, k_shards, v_shards, dout, o, lse, grads=None
     be split (bsm_bwd_step_ws).  two_streams: run every step's dK/dV update
     on a second stream beside the dQ chain (bsm_bwd_step_streams), so each
     kernel's launch tail is filled by the other's work; the gradients are
-    bit-identical either way."""
+    bit-identical either way.  kv_streams (with two_streams): how many side
+    streams the dK/dV launches of successive steps alternate between, each
+    with its own workspace; None picks kv_side_streams(dp).  The launches of
+    different steps write different shards' accumulators, so they may
+    overlap."""
     import torch
     rows = dp.rows
     _need(dout, torch.bfloat16, (rows, hd.hq, hd.d), "dout")
@@ -373,17 +409,27 @@ def bwd_ring(dp: DevicePlan, hd, q, k_shards, v_shards, dout, o, lse, grads=None
         dq, dks, dvs = grads
         for t in dks + dvs:
             t.zero_()
-    ws = bwd_workspace(dp, hd, q.device) if split else None
     main = torch.cuda.current_stream()
-    side = torch.cuda.Stream(device=q.device) if two_streams else None
-    if side is not None:
-        side.wait_stream(main)  # delta and the cleared accumulators
+    if two_streams:
+        nside = kv_side_streams(dp) if kv_streams is None else int(kv_streams)
+        if nside not in (1, 2):
+            raise ValueError(f"kv_streams: expected 1 or 2, got {kv_streams}")
+        sides = _side_streams(q.device, nside)
+        for side in sides:
+            side.wait_stream(main)  # delta and the cleared accumulators
+    else:
+        sides = [None]
+    wss = [bwd_workspace(dp, hd, q.device) if split else None for _ in sides]
+    launch = 0
     for s in (range(dp.ranks) if steps is None else steps):
         j = (dp.rank - s) % dp.ranks
-        bwd_step(dp, s, hd, q, k_shards[j], v_shards[j], dout, lse, delta, dq, dks[j], dvs[j], ws,
-                 kv_stream=side)
-    if side is not None:
-        # joined before returning: whatever reuses these buffers later on the
-        # current stream runs after the side stream's work
-        main.wait_stream(side)
+        i = launch % len(sides)
+        bwd_step(dp, s, hd, q, k_shards[j], v_shards[j], dout, lse, delta, dq, dks[j], dvs[j], wss[i],
+                 kv_stream=sides[i])
+        launch += dp.info["bwd_items"][s] > 0
+    for side in sides:
+        if side is not None:
+            # joined before returning: whatever reuses these buffers later on
+            # the current stream runs after the side streams' work
+            main.wait_stream(side)
     return dq, dks, dvs

@@ -170,3 +170,17 @@ def test_single_hip_runtime_in_process():
                          cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
     libs = eval(out.stdout.strip().splitlines()[-1])
     assert len(libs) == 1, libs
+
+
+def test_kv_side_streams_rule():
+    """Two dK/dV side streams only when every step's key tiles average at most
+    SHORT_UNIT_QUERIES legal queries per key; steps without work are ignored."""
+    from types import SimpleNamespace
+    from block_sparse_masked_metadata_amd.ring import SHORT_UNIT_QUERIES as T
+
+    def dp(items, pairs):
+        return SimpleNamespace(ranks=len(items), info={"bwd_items": items, "step_pairs": pairs})
+    assert bsm.kv_side_streams(dp([4, 2, 0], [4 * 128 * 600, 2 * 128 * T, 0])) == 2
+    assert bsm.kv_side_streams(dp([4, 2, 0], [4 * 128 * 600, 2 * 128 * T + 1, 0])) == 1
+    assert bsm.kv_side_streams(dp([4, 1], [4 * 128 * 16384, 128 * 2048])) == 1
+    assert bsm.kv_side_streams(dp([0, 0], [0, 0])) == 2

@@ -203,8 +203,9 @@ def test_split_workspace_too_small_is_refused():
 
 @pytest.mark.parametrize("maker", ["packed_text", "random"])
 def test_two_streams_equal_one_stream(maker):
-    """bsm_bwd_step_streams: the dK/dV chain on a second stream gives the
-    one-stream gradients bit for bit (same kernels, same inputs)."""
+    """bsm_bwd_step_streams: the dK/dV chain on a second stream, or its
+    launches alternating over two side streams, gives the one-stream
+    gradients bit for bit (same kernels, same inputs)."""
     from workloads import packed_text
     if maker == "packed_text":
         lay = packed_text()
@@ -218,11 +219,15 @@ def test_two_streams_equal_one_stream(maker):
     one = bsm.bwd_ring(case.dp, case.heads, case.q, case.k_shards, case.v_shards, case.dout, o, lse,
                        two_streams=False)
     two = bsm.bwd_ring(case.dp, case.heads, case.q, case.k_shards, case.v_shards, case.dout, o, lse,
-                       two_streams=True)
+                       two_streams=True, kv_streams=1)
+    # dK/dV launches of successive steps alternating over two side streams
+    three = bsm.bwd_ring(case.dp, case.heads, case.q, case.k_shards, case.v_shards, case.dout, o, lse,
+                         two_streams=True, kv_streams=2)
     torch.cuda.synchronize()
-    assert torch.equal(one[0], two[0])
-    for a, b in zip(one[1] + one[2], two[1] + two[2]):
-        assert torch.equal(a, b)
+    for other in (two, three):
+        assert torch.equal(one[0], other[0])
+        for a, b in zip(one[1] + one[2], other[1] + other[2]):
+            assert torch.equal(a, b)
     if maker == "random":
         sel = np.arange(case.S)
         ref = _oracle(case, sel)

@@ -22,6 +22,7 @@ forward launch of the last timed pass.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import platform
@@ -563,6 +564,11 @@ def main():
         for side in sides:
             main.wait_stream(side)
 
+    # The GPU events time the gaps between markers, so a host pause between a
+    # marker and the launches after it counts as GPU time: collect Python
+    # garbage now and keep the collector off until the timed passes end.
+    gc.collect()
+    gc.disable()
     for _ in range(args.warmup):
         forward()
         if do_bwd:
@@ -591,6 +597,7 @@ def main():
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    gc.enable()
 
     total_ms = start.elapsed_time(end)
     fwd_each = sorted(a.elapsed_time(b) for a, b in marks)

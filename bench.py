@@ -70,6 +70,9 @@ def parse():
     ap.add_argument("--fit-tau", action="store_true",
                     help="fit the chunk cost's per-range term: time the ring critical path at "
                          "1, 2, 4, ..., 64 chunks per rank and print one JSON line with the fit")
+    ap.add_argument("--kv-streams", type=int, choices=(1, 2), default=None,
+                    help="backward: side streams the dK/dV launches alternate over "
+                         "(default: as kv_side_streams picks for the plan)")
     ap.add_argument("--one-stream", action="store_true",
                     help="backward: the dK/dV launches on the same stream as the dQ launches "
                          "(counter runs; no per-kernel backward roofline)")
@@ -517,7 +520,7 @@ def main():
     # the dK/dV launches alternate between as many side streams as bwd_ring
     # would use for this plan, each with its own workspace (which lets long
     # dK/dV lists split over the GPU)
-    sides = [torch.cuda.Stream() for _ in range(bsm.kv_side_streams(dp))]
+    sides = [torch.cuda.Stream() for _ in range(args.kv_streams or bsm.kv_side_streams(dp))]
     bwss = [bsm.bwd_workspace(dp, hd) for _ in sides]
 
     def event(stream=None):

@@ -104,8 +104,6 @@ class DevicePlan:
         self.rank = r
         self.ranks = plan.info["ranks"]
         self.rows = plan.info["shard_tokens"]
-        tiles = plan.info["full_tiles"] + plan.info["partial_tiles"]
-        self.partial_share = plan.info["partial_tiles"] / tiles if tiles else 0.0
 
     def close(self):
         if self.handle:
@@ -351,19 +349,21 @@ def bwd_step(dp: DevicePlan, s, hd, q, k, v, dout, lse, delta, dq, dk, dv, works
 
 
 # The dK/dV launches of successive steps may overlap (each writes its own
-# shard's accumulators).  Overlapping two of them pays where many tiles are
-# partial: masked units vary in length and leave long launch tails for the
-# other launch to fill.  Where nearly every tile is full the units are
-# MFMA-bound and even, and a second launch only contends for the caches and
-# for the CUs of the dQ chain.  Measured per layout (one side stream -> two):
-# partial share 0.46, 0.16, 0.11 faster; 0.05, 0.04, 0.00 level or slower.
-MASKED_SHARE = 0.10
+# shard's accumulators), and two of them side by side fill each other's launch
+# tails.  A unit (one key tile and KV head) loops over the query tiles that
+# reach it.  When some step's units average more legal queries per key than
+# this, the units fill the chip for several rounds at one workgroup per CU and
+# a concurrent launch of the next step takes CUs from those rounds; there one
+# side stream is kept.
+SHORT_UNIT_QUERIES = 4096
 
 
 def kv_side_streams(dp: DevicePlan):
     """How many side streams the dK/dV launches of a backward should alternate
-    between: 2 when at least MASKED_SHARE of the plan's tiles are partial, else 1."""
-    return 2 if dp.partial_share >= MASKED_SHARE else 1
+    between: 2 when every step's units are short (see SHORT_UNIT_QUERIES), else 1."""
+    items, pairs = dp.info["bwd_items"], dp.info["step_pairs"]
+    longest = max((pairs[s] / (128.0 * items[s]) for s in range(dp.ranks) if items[s] > 0), default=0.0)
+    return 2 if longest <= SHORT_UNIT_QUERIES else 1
 
 
 _SIDE_STREAMS = {}

@@ -173,16 +173,14 @@ def test_single_hip_runtime_in_process():
 
 
 def test_kv_side_streams_rule():
-    """Two dK/dV side streams only when at least MASKED_SHARE of the plan's
-    tiles are partial; the share is the host plan's."""
+    """Two dK/dV side streams only when every step's key tiles average at most
+    SHORT_UNIT_QUERIES legal queries per key; steps without work are ignored."""
     from types import SimpleNamespace
-    from block_sparse_masked_metadata_amd.ring import MASKED_SHARE as T
-    assert bsm.kv_side_streams(SimpleNamespace(partial_share=T)) == 2
-    assert bsm.kv_side_streams(SimpleNamespace(partial_share=0.46)) == 2
-    assert bsm.kv_side_streams(SimpleNamespace(partial_share=T - 1e-9)) == 1
-    assert bsm.kv_side_streams(SimpleNamespace(partial_share=0.0)) == 1
-    # the share a device plan carries is the host plan's partial tiles over all its tiles
-    lay = packed_text()
-    p = bsm.Plan.from_layout(lay)
-    share = p.info["partial_tiles"] / (p.info["full_tiles"] + p.info["partial_tiles"])
-    assert 0.15 < share < 0.17
+    from block_sparse_masked_metadata_amd.ring import SHORT_UNIT_QUERIES as T
+
+    def dp(items, pairs):
+        return SimpleNamespace(ranks=len(items), info={"bwd_items": items, "step_pairs": pairs})
+    assert bsm.kv_side_streams(dp([4, 2, 0], [4 * 128 * 600, 2 * 128 * T, 0])) == 2
+    assert bsm.kv_side_streams(dp([4, 2, 0], [4 * 128 * 600, 2 * 128 * T + 1, 0])) == 1
+    assert bsm.kv_side_streams(dp([4, 1], [4 * 128 * 16384, 128 * 2048])) == 1
+    assert bsm.kv_side_streams(dp([0, 0], [0, 0])) == 2

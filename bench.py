@@ -70,6 +70,9 @@ def parse():
     ap.add_argument("--fit-tau", action="store_true",
                     help="fit the chunk cost's per-range term: time the ring critical path at "
                          "1, 2, 4, ..., 64 chunks per rank and print one JSON line with the fit")
+    ap.add_argument("--fwd-chains", type=int, choices=(1, 2), default=None,
+                    help="forward ring: 1 launch per step, or the plan's two chains of query tiles on "
+                         "two streams (default: as fwd_chains picks for the plan)")
     ap.add_argument("--kv-streams", type=int, choices=(1, 2), default=None,
                     help="backward: side streams the dK/dV launches alternate over "
                          "(default: as kv_side_streams picks for the plan)")
@@ -475,6 +478,18 @@ def main():
 
     if args.fetch:
         kf, vf = bsm.gather_fetched(plan, r, k_all, v_all)
+    ring_mode = not (args.fetch or args.single or args.merge != "carry")
+
+    def bsm_chain_items(s, c):
+        n, c0 = dp.info["fwd_items"][s], dp.info["fwd_chain0_items"][s]
+        return c0 if c == 0 else n - c0
+    nchains = (args.fwd_chains or bsm.fwd_chains(dp, hd)) if ring_mode else 1
+    # two side streams, made once: the forward's two chains and the
+    # backward's dK/dV launches run on them (as fwd_ring and bwd_ring do).
+    # Streams map onto a few hardware queues; more streams than queues would
+    # put a side stream on the current stream's queue, behind its work.
+    side_streams = [torch.cuda.Stream() for _ in range(2)]
+    fwd_sides = side_streams if nchains == 2 else []
 
     def forward(events=None):
         if args.fetch:
@@ -504,6 +519,29 @@ def main():
                 events.append(torch.cuda.Event(enable_timing=True))
                 events[-1].record()
             return
+        if nchains == 2:
+            # the plan's two chains of query tiles, each on its own stream
+            # with its steps in order, as fwd_ring runs them; events (per
+            # launch) on the stream the launch runs on
+            main = torch.cuda.current_stream()
+            for side in fwd_sides:
+                side.wait_stream(main)
+            for s in fwd_steps:
+                j = (r - s) % R
+                for c, side in enumerate(fwd_sides):
+                    if bsm_chain_items(s, c) == 0:
+                        continue
+                    with torch.cuda.stream(side):
+                        if events is not None:
+                            events.append(torch.cuda.Event(enable_timing=True))
+                            events[-1].record()
+                        bsm.fwd_step(dp, s, hd, q, ks[j], vs[j], state, o, lse, chain=c)
+                        if events is not None:
+                            events.append(torch.cuda.Event(enable_timing=True))
+                            events[-1].record()
+            for side in fwd_sides:
+                main.wait_stream(side)
+            return
         for s in fwd_steps:
             j = (r - s) % R
             if events is not None:
@@ -520,7 +558,7 @@ def main():
     # the dK/dV launches alternate between as many side streams as bwd_ring
     # would use for this plan, each with its own workspace (which lets long
     # dK/dV lists split over the GPU)
-    sides = [torch.cuda.Stream() for _ in range(args.kv_streams or bsm.kv_side_streams(dp))]
+    sides = side_streams[:args.kv_streams or bsm.kv_side_streams(dp)]
     bwss = [bsm.bwd_workspace(dp, hd) for _ in sides]
 
     def event(stream=None):
@@ -612,7 +650,8 @@ def main():
     fwd_flops = 4 * d * lay.hq * total_pairs
     bwd_flops = 10 * d * lay.hq * total_pairs
     fwd_tflops = fwd_flops / (fwd_ms * 1e-3) / 1e12
-    nlaunch = 1 if args.single or args.fetch or args.merge != "carry" else len(fwd_steps)
+    nlaunch = (1 if not ring_mode else len(fwd_steps) if nchains == 1 else
+               sum(bsm_chain_items(s, c) > 0 for s in fwd_steps for c in (0, 1)))
     per_launch_flops = fwd_flops / nlaunch
     per_launch_bytes = sum(fwd_algorithmic_bytes(plan, r, R, S, lay.hq, lay.hkv, d,
                                                  args.single or args.fetch)) / nlaunch
@@ -699,7 +738,16 @@ def main():
                      "hbm_gbs": round(hbm_gbs, 1),
                      "hbm_frac": round(hbm_gbs / PEAK_HBM_GBS, 4),
                      "avg_launch_us": round(avg_launch_ms * 1e3, 2),
-                     "launches_per_step": nlaunch},
+                     "launches_per_step": nlaunch,
+                     "chains": nchains,
+                     "launches": ("one per ring step" if nchains == 1 else
+                                  "one per ring step and chain of query tiles; the two chains run on two "
+                                  "streams side by side, so each launch's duration is measured while the "
+                                  "other chain's launch shares the GPU"),
+                     # the whole forward's rate: every launch's algorithmic bytes over the forward's time
+                     "aggregate_hbm_gbs": round(per_launch_bytes * nlaunch / (fwd_ms * 1e-3) / 1e9, 1),
+                     "aggregate_hbm_frac": round(per_launch_bytes * nlaunch / (fwd_ms * 1e-3) / 1e9
+                                                 / PEAK_HBM_GBS, 4)},
         "mode": ("dense calls" + (" (single pass)" if args.single else "") if args.dense else
                  "single-pass diagnostic" if args.single else
                  "sparse fetch: one pass over the shard and fetched tiles (contiguous chunks)" if args.fetch else

@@ -9,11 +9,11 @@ ImportError if libbsm.so has not been built (there is no fallback).
 """
 from . import _capi
 from ._capi import BsmError, LIB_PATH
-from .ring import (Plan, DevicePlan, vision_group_order, heads, new_state, state_rows, fwd_step, fwd_ring, fwd_ring_merged, fwd_single,
+from .ring import (Plan, DevicePlan, vision_group_order, heads, new_state, state_rows, fwd_step, fwd_chains, fwd_ring, fwd_ring_merged, fwd_single,
                    fetch_rows, gather_fetched, fwd_fetched, bwd_fetched, fetched_accumulate,
                    bwd_prep, bwd_step, bwd_ring, bwd_workspace, kv_side_streams)
 
 __all__ = ["_capi", "BsmError", "LIB_PATH", "Plan", "DevicePlan", "vision_group_order", "heads", "new_state", "state_rows",
-           "fwd_step", "fwd_ring", "fwd_ring_merged", "fwd_single", "fetch_rows", "gather_fetched",
+           "fwd_step", "fwd_chains", "fwd_ring", "fwd_ring_merged", "fwd_single", "fetch_rows", "gather_fetched",
            "fwd_fetched", "bwd_fetched", "fetched_accumulate", "bwd_prep", "bwd_step", "bwd_ring", "bwd_workspace",
            "kv_side_streams"]

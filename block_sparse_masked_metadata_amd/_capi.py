@@ -43,7 +43,7 @@ EXPORTS = [
     "bsm_plan_permutation", "bsm_plan_block_cost", "bsm_plan_step_map", "bsm_plan_pairs",
     "bsm_plan_key_intervals", "bsm_plan_fetch_set", "bsm_plan_chunk_order", "bsm_fwd_fetched",
     "bsm_dplan_bytes", "bsm_dplan_upload", "bsm_dplan_free", "bsm_dplan_get_info",
-    "bsm_fwd_step", "bsm_fwd_single", "bsm_fwd_merge_bf16", "bsm_fwd_merge_fp32",
+    "bsm_fwd_step", "bsm_fwd_step_chain", "bsm_fwd_single", "bsm_fwd_merge_bf16", "bsm_fwd_merge_fp32",
     "bsm_bwd_prep", "bsm_bwd_step", "bsm_plan_dense_calls", "bsm_dplan_calls_bytes",
     "bsm_dplan_calls_upload", "bsm_state_unpack", "bsm_bwd_step_ws", "bsm_bwd_step_streams",
     "bsm_bwd_step_noalloc", "bsm_bwd_fetched", "bsm_fetched_accumulate", "bsm_vision_group_order",
@@ -79,7 +79,7 @@ class bsm_dplan_info(C.Structure):
                 ("fwd_items", C.c_int64 * 64), ("bwd_items", C.c_int64 * 64),
                 ("step_pairs", C.c_int64 * 64), ("single_items", C.c_int64),
                 ("fetch_tiles", C.c_int64), ("fetch_rows", C.c_int64), ("dense_calls", C.c_int32),
-                ("bwd_workspace_slots", C.c_int32)]
+                ("bwd_workspace_slots", C.c_int32), ("fwd_chain0_items", C.c_int64 * 64)]
 
 
 class bsm_call(C.Structure):
@@ -123,6 +123,8 @@ _sig = {
     "bsm_dplan_get_info": (C.c_int, [_P, C.POINTER(bsm_dplan_info)]),
     "bsm_fwd_step": (C.c_int, [_P, C.c_int32, C.POINTER(bsm_heads), _P, _P, _P, _P, _P, _P,
                                _P, _P, C.c_int32, _P]),
+    "bsm_fwd_step_chain": (C.c_int, [_P, C.c_int32, C.c_int32, C.POINTER(bsm_heads), _P, _P, _P, _P, _P,
+                                     _P, _P, _P, C.c_int32, _P]),
     "bsm_fwd_single": (C.c_int, [_P, C.POINTER(bsm_heads), _P, _P, _P, _P, _P, _P, _P, _P,
                                  C.c_int32, _P]),
     "bsm_fwd_merge_bf16": (C.c_int, [C.POINTER(bsm_heads), C.c_int64, _P, _P, _P, _P, _P]),
@@ -328,7 +330,8 @@ def bsm_dplan_get_info(dplan) -> dict:
             "fwd_items": list(info.fwd_items[:rk]), "bwd_items": list(info.bwd_items[:rk]),
             "step_pairs": list(info.step_pairs[:rk]), "single_items": info.single_items,
             "fetch_tiles": info.fetch_tiles, "fetch_rows": info.fetch_rows,
-            "dense_calls": bool(info.dense_calls), "bwd_workspace_slots": info.bwd_workspace_slots}
+            "dense_calls": bool(info.dense_calls), "bwd_workspace_slots": info.bwd_workspace_slots,
+            "fwd_chain0_items": list(info.fwd_chain0_items[:rk])}
 
 
 def _heads(hq, hkv, d, scale):
@@ -338,6 +341,11 @@ def _heads(hq, hkv, d, scale):
 def bsm_fwd_step(dplan, s, heads, q, k, v, o_acc, m, l, o, lse, flags, stream):
     _check(_lib.bsm_fwd_step(dplan, int(s), C.byref(heads), q, k, v, o_acc, m, l, o, lse,
                              int(flags), stream))
+
+
+def bsm_fwd_step_chain(dplan, s, chain, heads, q, k, v, o_acc, m, l, o, lse, flags, stream):
+    _check(_lib.bsm_fwd_step_chain(dplan, int(s), int(chain), C.byref(heads), q, k, v, o_acc, m, l, o, lse,
+                                   int(flags), stream))
 
 
 def bsm_fwd_single(dplan, heads, q, k_all, v_all, o_acc, m, l, o, lse, flags, stream):

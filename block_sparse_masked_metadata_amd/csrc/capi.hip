@@ -43,6 +43,8 @@ int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 
 struct StepLists {
   std::vector<int4> fitems, bitems;
+  std::vector<int4> citems;  // fitems by chain: chain 0's items first (bsm_fwd_step_chain)
+  int64_t nchain0 = 0;
   std::vector<int4> bwork, breduce;  // split dK/dV work and its reduction
   int32_t slots = 0;                 // workspace slots of the split work
   int64_t pairs = 0;
@@ -68,6 +70,7 @@ struct Packed {
   // byte offsets in the device buffer
   int64_t off_tracks = 0, off_coord = 0, off_kint = 0, off_items = 0, off_entries = 0, bytes = 0;
   std::vector<int64_t> off_f, off_b, off_ff;  // off_ff: first list entry of each forward item
+  std::vector<int64_t> off_c, off_cf;         // the chain-ordered forward items and their first entries
   std::vector<int64_t> off_w, off_r;         // split dK/dV work units and reduce entries
   int64_t off_s = 0, off_sf = 0, off_x = 0, off_xf = 0, off_xtracks = 0, off_xkint = 0;
   int64_t off_y = 0, off_xsrc = 0;
@@ -133,6 +136,51 @@ static void order_items(std::vector<int4>& v, G group) {
   std::vector<int4> out(v.size());
   for (size_t i = 0; i < idx.size(); ++i) out[i] = v[idx[i]];
   v.swap(out);
+}
+
+// Two chains of query tiles for the forward (bsm_fwd_step_chain): a step's
+// items of one chain depend only on that chain's items of earlier steps, so
+// the two chains can run on two streams and fill each other's launch tails.
+// Whole samples (the sample of a tile's first row) go to one chain, so a
+// chain keeps order_items' grouping of a sample's items; heaviest sample
+// first to the lighter chain, weighed by list entries over all steps, ties
+// by sample id.  Each step's items in chain order, order_items' order kept
+// within a chain.
+template <class W, class G>
+static void chain_items(Packed& pk, int32_t T, int32_t R, W entries_of, G group) {
+  std::vector<std::pair<int32_t, int64_t>> gw;  // (sample, list entries)
+  for (int32_t a = 0; a < T; ++a) {
+    int64_t w = 0;
+    for (int32_t s = 0; s < R; ++s) w += entries_of(s, a);
+    if (w == 0) continue;
+    const int32_t g = group(a);
+    auto it = std::find_if(gw.begin(), gw.end(), [&](const std::pair<int32_t, int64_t>& e) { return e.first == g; });
+    if (it == gw.end()) gw.push_back({g, w});
+    else it->second += w;
+  }
+  std::sort(gw.begin(), gw.end(), [](const std::pair<int32_t, int64_t>& x, const std::pair<int32_t, int64_t>& y) {
+    return x.second != y.second ? x.second > y.second : x.first < y.first;
+  });
+  std::vector<std::pair<int32_t, int32_t>> gc;  // (sample, chain)
+  int64_t load[2] = {0, 0};
+  for (const auto& e : gw) {
+    const int32_t c = load[1] < load[0] ? 1 : 0;
+    gc.push_back({e.first, c});
+    load[c] += e.second;
+  }
+  auto chain_of = [&](int32_t a) {
+    const int32_t g = group(a);
+    for (const auto& e : gc)
+      if (e.first == g) return e.second;
+    return 0;
+  };
+  for (int32_t s = 0; s < R; ++s) {
+    StepLists& st = pk.steps[s];
+    st.citems = st.fitems;
+    auto mid = std::stable_partition(st.citems.begin(), st.citems.end(),
+                                     [&](const int4& x) { return chain_of(x.x) == 0; });
+    st.nchain0 = mid - st.citems.begin();
+  }
 }
 
 static void pack(const Plan& p, int32_t r, Packed& pk) {
@@ -212,6 +260,7 @@ static void pack(const Plan& p, int32_t r, Packed& pk) {
     std::stable_sort(st.bitems.begin(), st.bitems.end(), by_len);
     split_work(st);
   }
+  chain_items(pk, T, R, [&](int32_t s, int32_t a) { return (int64_t)rows[s][a].size(); }, qsample);
   // merged single-pass lists: ring step order, then ascending key tile
   pk.sitems.clear();
   for (int32_t a = 0; a < T; ++a) {
@@ -319,6 +368,8 @@ static void layout(const Plan& p, Packed& pk) {
   pk.off_f.assign(R, 0);
   pk.off_b.assign(R, 0);
   pk.off_ff.assign(R, 0);
+  pk.off_c.assign(R, 0);
+  pk.off_cf.assign(R, 0);
   pk.off_w.assign(R, 0);
   pk.off_r.assign(R, 0);
   for (int32_t s = 0; s < R; ++s) {
@@ -326,6 +377,10 @@ static void layout(const Plan& p, Packed& pk) {
     off = align256(off + (int64_t)pk.steps[s].fitems.size() * sizeof(int4));
     pk.off_ff[s] = off;
     off = align256(off + (int64_t)pk.steps[s].fitems.size() * sizeof(int2));
+    pk.off_c[s] = off;
+    off = align256(off + (int64_t)pk.steps[s].citems.size() * sizeof(int4));
+    pk.off_cf[s] = off;
+    off = align256(off + (int64_t)pk.steps[s].citems.size() * sizeof(int2));
     pk.off_b[s] = off;
     off = align256(off + (int64_t)pk.steps[s].bitems.size() * sizeof(int4));
     pk.off_w[s] = off;
@@ -512,6 +567,7 @@ static int pack_calls(const Plan& p, int32_t r, Packed& pk) {
                      [](const int4& x, const int4& y) { return x.w != y.w ? x.w > y.w : x.x < y.x; });
     split_work(st);
   }
+  chain_items(pk, T, R, [&](int32_t s, int32_t a) { return (int64_t)lists[s][a].size(); }, qsample);
   pk.sitems.clear();
   for (int32_t a = 0; a < T; ++a) {
     const int32_t beg = (int32_t)pk.entries.size();
@@ -551,6 +607,9 @@ struct bsm_dplan {
   const int2* entries = nullptr;
   const int4* fitems[64] = {};
   const int2* ffirst[64] = {};
+  const int4* citems[64] = {};  // forward items by chain (chain 0 first) and their first entries
+  const int2* cfirst[64] = {};
+  int64_t nc0[64] = {};         // items of chain 0
   const int4* bitems[64] = {};
   int64_t nf[64] = {}, nb[64] = {}, pairs[64] = {};
   const int4* bwork[64] = {};   // split dK/dV work units
@@ -757,6 +816,9 @@ int dplan_upload(const bsm_plan* plan, int32_t r, bool dense, void* dev, int64_t
       std::memcpy(img.data() + pk.off_f[s], pk.steps[s].fitems.data(), pk.steps[s].fitems.size() * sizeof(int4));
       int2* ff = (int2*)(img.data() + pk.off_ff[s]);
       for (size_t i = 0; i < pk.steps[s].fitems.size(); ++i) ff[i] = pk.entries[pk.steps[s].fitems[i].z];
+      std::memcpy(img.data() + pk.off_c[s], pk.steps[s].citems.data(), pk.steps[s].citems.size() * sizeof(int4));
+      int2* cf = (int2*)(img.data() + pk.off_cf[s]);
+      for (size_t i = 0; i < pk.steps[s].citems.size(); ++i) cf[i] = pk.entries[pk.steps[s].citems[i].z];
       std::memcpy(img.data() + pk.off_b[s], pk.steps[s].bitems.data(), pk.steps[s].bitems.size() * sizeof(int4));
       std::memcpy(img.data() + pk.off_w[s], pk.steps[s].bwork.data(), pk.steps[s].bwork.size() * sizeof(int4));
       std::memcpy(img.data() + pk.off_r[s], pk.steps[s].breduce.data(), pk.steps[s].breduce.size() * sizeof(int4));
@@ -794,6 +856,9 @@ int dplan_upload(const bsm_plan* plan, int32_t r, bool dense, void* dev, int64_t
     for (int32_t s = 0; s < p.ranks; ++s) {
       d->fitems[s] = (const int4*)(base + pk.off_f[s]);
       d->ffirst[s] = (const int2*)(base + pk.off_ff[s]);
+      d->citems[s] = (const int4*)(base + pk.off_c[s]);
+      d->cfirst[s] = (const int2*)(base + pk.off_cf[s]);
+      d->nc0[s] = pk.steps[s].nchain0;
       d->bitems[s] = (const int4*)(base + pk.off_b[s]);
       d->nf[s] = (int64_t)pk.steps[s].fitems.size();
       d->nb[s] = (int64_t)pk.steps[s].bitems.size();
@@ -884,6 +949,7 @@ int bsm_dplan_get_info(const bsm_dplan* d, bsm_dplan_info* out) {
   out->window = d->window;
   for (int32_t s = 0; s < d->R; ++s) {
     out->fwd_items[s] = d->nf[s];
+    out->fwd_chain0_items[s] = d->nc0[s];
     out->bwd_items[s] = d->nb[s];
     out->step_pairs[s] = d->pairs[s];
   }
@@ -895,9 +961,14 @@ int bsm_dplan_get_info(const bsm_dplan* d, bsm_dplan_info* out) {
   return BSM_OK;
 }
 
-int bsm_fwd_step(const bsm_dplan* d, int32_t s, const bsm_heads* heads, const void* q,
-                 const void* k, const void* v, float* o_acc, float* m, float* l, void* o,
-                 float* lse, int32_t flags, void* stream) {
+}  // extern "C"
+
+namespace {
+// One ring step's launch over `n` forward items (with their first list
+// entries) of step s: all of them (bsm_fwd_step) or one chain's.
+int fwd_step_items(const bsm_dplan* d, int32_t s, const bsm_heads* heads, const void* q, const void* k,
+                   const void* v, float* o_acc, float* m, float* l, void* o, float* lse, int32_t flags,
+                   void* stream, int32_t chain) {
   if (!d) { set_error("null device plan"); return BSM_E_INVALID; }
   int rc = check_heads(heads);
   if (rc) return rc;
@@ -909,13 +980,15 @@ int bsm_fwd_step(const bsm_dplan* d, int32_t s, const bsm_heads* heads, const vo
   }
   if ((rc = check_rows(d->S, heads->hq, "q")) || (rc = check_rows(d->S, heads->hkv, "k/v"))) return rc;
   if ((rc = check_aligned({q, k, v, o_acc, o}, {m, l, lse}))) return rc;
-  if (d->nf[s] == 0) return BSM_OK;
+  if (chain < -1 || chain > 1) { set_error("chain must be 0 or 1"); return BSM_E_INVALID; }
+  const int64_t i0 = chain == 1 ? d->nc0[s] : 0, i1 = chain == 0 ? d->nc0[s] : d->nf[s];
+  if (i1 <= i0) return BSM_OK;
   const int32_t j = ((d->r - s) % d->R + d->R) % d->R;
   FwdArgs a{};
-  a.items = d->fitems[s];
-  a.first = d->ffirst[s];
+  a.items = chain < 0 ? d->fitems[s] : d->citems[s] + i0;
+  a.first = chain < 0 ? d->ffirst[s] : d->cfirst[s] + i0;
   a.entries = d->entries;
-  a.nitems = (int32_t)d->nf[s];
+  a.nitems = (int32_t)(i1 - i0);
   a.hq = heads->hq;
   a.hkv = heads->hkv;
   a.heads_per_xcd = heads_per_xcd(heads->hq);
@@ -939,6 +1012,22 @@ int bsm_fwd_step(const bsm_dplan* d, int32_t s, const bsm_heads* heads, const vo
   a.dense = d->dense;
   hipStream_t st = (hipStream_t)stream;
   return hip_status(launch_fwd(a, st), "forward step launch", st);
+}
+}  // namespace
+
+extern "C" {
+
+int bsm_fwd_step(const bsm_dplan* d, int32_t s, const bsm_heads* heads, const void* q,
+                 const void* k, const void* v, float* o_acc, float* m, float* l, void* o,
+                 float* lse, int32_t flags, void* stream) {
+  return fwd_step_items(d, s, heads, q, k, v, o_acc, m, l, o, lse, flags, stream, -1);
+}
+
+int bsm_fwd_step_chain(const bsm_dplan* d, int32_t s, int32_t chain, const bsm_heads* heads, const void* q,
+                       const void* k, const void* v, float* o_acc, float* m, float* l, void* o, float* lse,
+                       int32_t flags, void* stream) {
+  if (chain != 0 && chain != 1) { set_error("chain must be 0 or 1"); return BSM_E_INVALID; }
+  return fwd_step_items(d, s, heads, q, k, v, o_acc, m, l, o, lse, flags, stream, chain);
 }
 
 namespace {

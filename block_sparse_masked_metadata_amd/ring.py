@@ -141,17 +141,50 @@ def state_rows(hd, o_acc, rows):
     return out
 
 
-def fwd_step(dp: DevicePlan, s, hd, q, k, v, state, o, lse, keep_state=False):
+def fwd_step(dp: DevicePlan, s, hd, q, k, v, state, o, lse, keep_state=False, chain=None):
+    """One forward ring step on the current stream: every query tile with work
+    (bsm_fwd_step), or with chain 0 or 1 only that chain's tiles
+    (bsm_fwd_step_chain)."""
     o_acc, m, l = state
-    C.bsm_fwd_step(dp.handle, s, hd, _ptr(q), _ptr(k), _ptr(v), _ptr(o_acc), _ptr(m), _ptr(l),
-                   _ptr(o), _ptr(lse), C.BSM_FWD_KEEP_STATE if keep_state else 0, _stream())
+    flags = C.BSM_FWD_KEEP_STATE if keep_state else 0
+    if chain is None:
+        C.bsm_fwd_step(dp.handle, s, hd, _ptr(q), _ptr(k), _ptr(v), _ptr(o_acc), _ptr(m), _ptr(l),
+                       _ptr(o), _ptr(lse), flags, _stream())
+    else:
+        C.bsm_fwd_step_chain(dp.handle, s, chain, hd, _ptr(q), _ptr(k), _ptr(v), _ptr(o_acc), _ptr(m),
+                             _ptr(l), _ptr(o), _ptr(lse), flags, _stream())
+
+
+def fwd_chains(dp: DevicePlan, hd, device=None):
+    """How many chains the forward ring should run (bsm_fwd_step_chain): 2
+    when at every step with work each chain holds at least one full round of
+    workgroups (two per CU) of its own, so that each chain's launches fill the
+    chip and the other chain's launches fill their tails; else 1.  Below a
+    round per chain, the two half launches leave CUs idle (packed text 32K
+    was 7-8% slower with two chains)."""
+    import torch
+    full = 2 * torch.cuda.get_device_properties(device if device is not None else
+                                                torch.cuda.current_device()).multi_processor_count
+    work = False
+    for s in range(dp.ranks):
+        n, c0 = dp.info["fwd_items"][s], dp.info["fwd_chain0_items"][s]
+        if n == 0:
+            continue
+        work = True
+        if min(c0, n - c0) * hd.hq < full:
+            return 1
+    return 2 if work else 1
 
 
 def fwd_ring(dp: DevicePlan, hd, q, k_shards, v_shards, state=None, out=None, keep_state=False,
-             steps=None):
+             steps=None, chains=None):
     """Run ring steps s = 0..R-1 (shard j = (r - s) mod R from k_shards[j]).
 
-    Returns (o, lse, state)."""
+    chains: 1 runs every step in one launch on the current stream; 2 runs the
+    plan's two chains of query tiles on two side streams, each chain's steps
+    in order (bitwise the same result); None picks fwd_chains(dp, hd).  The
+    side streams wait for the current stream first and the current stream
+    waits for them before returning.  Returns (o, lse, state)."""
     import torch
     rows = dp.rows
     _need(q, torch.bfloat16, (rows, hd.hq, hd.d), "q")
@@ -164,9 +197,26 @@ def fwd_ring(dp: DevicePlan, hd, q, k_shards, v_shards, state=None, out=None, ke
         out = (torch.empty(rows, hd.hq, hd.d, dtype=torch.bfloat16, device=q.device),
                torch.empty(hd.hq, rows, dtype=torch.float32, device=q.device))
     o, lse = out
-    for s in (range(dp.ranks) if steps is None else steps):
+    todo = list(range(dp.ranks) if steps is None else steps)
+    nch = fwd_chains(dp, hd, q.device) if chains is None else int(chains)
+    if nch not in (1, 2):
+        raise ValueError(f"chains: expected 1 or 2, got {chains}")
+    if nch == 1:
+        for s in todo:
+            j = (dp.rank - s) % dp.ranks
+            fwd_step(dp, s, hd, q, k_shards[j], v_shards[j], state, o, lse, keep_state)
+        return o, lse, state
+    main = torch.cuda.current_stream()
+    sides = _side_streams(q.device, 2)
+    for side in sides:
+        side.wait_stream(main)
+    for s in todo:
         j = (dp.rank - s) % dp.ranks
-        fwd_step(dp, s, hd, q, k_shards[j], v_shards[j], state, o, lse, keep_state)
+        for c, side in enumerate(sides):
+            with torch.cuda.stream(side):
+                fwd_step(dp, s, hd, q, k_shards[j], v_shards[j], state, o, lse, keep_state, chain=c)
+    for side in sides:
+        main.wait_stream(side)
     return o, lse, state
 
 
@@ -370,7 +420,8 @@ _SIDE_STREAMS = {}
 
 
 def _side_streams(device, n):
-    """The first n of two side streams kept per device for the dK/dV launches.
+    """The first n of two side streams kept per device for the forward's two
+    chains and the backward's dK/dV launches.
     Streams share the device's few hardware queues; one taken afresh per call
     can land on the current stream's queue and run behind its work, so the
     same ones serve every call."""

@@ -341,6 +341,8 @@ typedef struct {
   int32_t dense_calls;       /* 1: a dense-call device plan                   */
   int32_t bwd_workspace_slots; /* max over steps of the split dK/dV work's
                                   workspace slots (each Hkv * 128 KiB)      */
+  int64_t fwd_chain0_items[64]; /* of fwd_items[s], those in chain 0 (the
+                                   rest are chain 1; bsm_fwd_step_chain)     */
 } bsm_dplan_info;
 
 int bsm_dplan_get_info(const bsm_dplan* dplan, bsm_dplan_info* out);
@@ -390,6 +392,25 @@ int bsm_fwd_step(const bsm_dplan* dplan, int32_t s, const bsm_heads* heads,
                  const void* q, const void* k, const void* v,
                  float* o_acc, float* m, float* l, void* o, float* lse,
                  int32_t flags, void* stream);
+
+/*
+ * The items of one chain of ring step s (MARBLE section 03, "Exact ring
+ * attention accumulation"; the order in which a rank's query tiles meet the
+ * ring's steps is free, only each tile's own steps are ordered).  The device
+ * plan splits the rank's query tiles into two chains (0 and 1) by whole
+ * samples, balanced by list entries; bsm_dplan_info.fwd_chain0_items[s] of
+ * the fwd_items[s] tiles are chain 0's.  A tile's state is touched only by
+ * its own chain, so the calls of chain 0 (steps in order) and those of chain
+ * 1 (steps in order) may run on two streams side by side; calling both
+ * chains of a step has the effect of bsm_fwd_step, bitwise (each tile runs
+ * the same list in the same order).  chain not 0 or 1 returns BSM_E_INVALID;
+ * a chain without items at step s returns BSM_OK without a launch.  Other
+ * arguments, flags and errors as for bsm_fwd_step.
+ */
+int bsm_fwd_step_chain(const bsm_dplan* dplan, int32_t s, int32_t chain, const bsm_heads* heads,
+                       const void* q, const void* k, const void* v,
+                       float* o_acc, float* m, float* l, void* o, float* lse,
+                       int32_t flags, void* stream);
 
 /*
  * Single pass over all R shards at once (the one-GPU result the ring must

@@ -155,13 +155,18 @@ def fwd_step(dp: DevicePlan, s, hd, q, k, v, state, o, lse, keep_state=False, ch
                              _ptr(l), _ptr(o), _ptr(lse), flags, _stream())
 
 
+CHAIN_MAX_ROUNDS = 8
+
+
 def fwd_chains(dp: DevicePlan, hd, device=None):
     """How many chains the forward ring should run (bsm_fwd_step_chain): 2
     when at every step with work each chain holds at least one full round of
-    workgroups (two per CU) of its own, so that each chain's launches fill the
-    chip and the other chain's launches fill their tails; else 1.  Below a
-    round per chain, the two half launches leave CUs idle (packed text 32K
-    was 7-8% slower with two chains)."""
+    workgroups (two per CU) and at most CHAIN_MAX_ROUNDS, so that each chain's
+    launches fill the chip and the other chain's launches fill their tails;
+    else 1.  Below a round per chain the two half launches leave CUs idle
+    (packed text 32K was 7-8% slower with two chains); over many rounds a
+    launch's tail is a small part of it and the second chain only contends
+    (long mixed 1M, 32 rounds per launch: 0.7% slower)."""
     import torch
     full = 2 * torch.cuda.get_device_properties(device if device is not None else
                                                 torch.cuda.current_device()).multi_processor_count
@@ -171,7 +176,7 @@ def fwd_chains(dp: DevicePlan, hd, device=None):
         if n == 0:
             continue
         work = True
-        if min(c0, n - c0) * hd.hq < full:
+        if min(c0, n - c0) * hd.hq < full or max(c0, n - c0) * hd.hq > CHAIN_MAX_ROUNDS * full:
             return 1
     return 2 if work else 1
 

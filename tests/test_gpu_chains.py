@@ -94,12 +94,16 @@ def test_chain_argument_checked():
 
 
 def test_fwd_chains_rule():
-    """Two chains exactly when every step with work gives each chain at least
-    one round of workgroups (two per CU)."""
+    """Two chains exactly when every step with work gives each chain between
+    one and CHAIN_MAX_ROUNDS rounds of workgroups (two per CU)."""
+    from block_sparse_masked_metadata_amd.ring import CHAIN_MAX_ROUNDS
     full = 2 * torch.cuda.get_device_properties(0).multi_processor_count
     for lay in (packed_text(), packed_multimodal(), _random(5)):
         case = Case(lay)
         info = case.dp.info
-        ok = [min(info["fwd_chain0_items"][s], info["fwd_items"][s] - info["fwd_chain0_items"][s]) * case.hq >= full
-              for s in range(case.R) if info["fwd_items"][s] > 0]
+        ok = []
+        for s in range(case.R):
+            n, c0 = info["fwd_items"][s], info["fwd_chain0_items"][s]
+            if n:
+                ok.append(min(c0, n - c0) * case.hq >= full and max(c0, n - c0) * case.hq <= CHAIN_MAX_ROUNDS * full)
         assert bsm.fwd_chains(case.dp, case.heads) == (2 if ok and all(ok) else 1)

@@ -480,7 +480,7 @@ def main():
         kf, vf = bsm.gather_fetched(plan, r, k_all, v_all)
     ring_mode = not (args.fetch or args.single or args.merge != "carry")
 
-    def bsm_chain_items(s, c):
+    def chain_items(s, c):
         n, c0 = dp.info["fwd_items"][s], dp.info["fwd_chain0_items"][s]
         return c0 if c == 0 else n - c0
     nchains = (args.fwd_chains or bsm.fwd_chains(dp, hd)) if ring_mode else 1
@@ -529,7 +529,7 @@ def main():
             for s in fwd_steps:
                 j = (r - s) % R
                 for c, side in enumerate(fwd_sides):
-                    if bsm_chain_items(s, c) == 0:
+                    if chain_items(s, c) == 0:
                         continue
                     with torch.cuda.stream(side):
                         if events is not None:
@@ -651,7 +651,7 @@ def main():
     bwd_flops = 10 * d * lay.hq * total_pairs
     fwd_tflops = fwd_flops / (fwd_ms * 1e-3) / 1e12
     nlaunch = (1 if not ring_mode else len(fwd_steps) if nchains == 1 else
-               sum(bsm_chain_items(s, c) > 0 for s in fwd_steps for c in (0, 1)))
+               sum(chain_items(s, c) > 0 for s in fwd_steps for c in (0, 1)))
     per_launch_flops = fwd_flops / nlaunch
     per_launch_bytes = sum(fwd_algorithmic_bytes(plan, r, R, S, lay.hq, lay.hkv, d,
                                                  args.single or args.fetch)) / nlaunch

@@ -6,7 +6,7 @@ import pytest
 import torch
 
 import block_sparse_masked_metadata_amd as bsm
-from workloads import random_small, packed_text, packed_multimodal
+from workloads import config, random_small, packed_text, packed_multimodal
 from gpu_common import Case, needs_gpu
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not needs_gpu, reason="needs a GPU")]
@@ -29,9 +29,10 @@ def _both(case):
     return one, two, st1, st2
 
 
-@pytest.mark.parametrize("maker", ["packed_text", "packed_multimodal", "random5", "random6"])
+@pytest.mark.parametrize("maker", ["packed_text", "packed_multimodal", "video_group", "random5", "random6"])
 def test_two_chains_equal_one_launch(maker):
-    lay = {"packed_text": packed_text, "packed_multimodal": packed_multimodal}.get(maker)
+    lay = {"packed_text": packed_text, "packed_multimodal": packed_multimodal,
+           "video_group": lambda: config(6)}.get(maker)
     lay = lay() if lay else _random(int(maker[-1]))
     case = Case(lay)
     one, two, st1, st2 = _both(case)

@@ -32,10 +32,11 @@ constexpr int kListCache = 512;  // list entries of an item kept in LDS at a tim
 // Entry e of an item's list through an LDS window of kListCache entries.
 // Called by all threads at the same point right after a __syncthreads();
 // reloads the window (with its own barrier) when e falls outside it.
-__device__ inline int2 list_entry(int2* sEnt, int& base, const int2* entries, int4 it, int e, int tid) {
+__device__ inline int2 list_entry(int2* sEnt, int& base, const int2* entries, int4 it, int e, int tid,
+                                 int nthreads) {
   if (e < base || e >= base + kListCache) {
     base = e - e % kListCache;
-    for (int i = tid; i < kListCache && base + i < it.w; i += 256) sEnt[i] = entries[it.z + base + i];
+    for (int i = tid; i < kListCache && base + i < it.w; i += nthreads) sEnt[i] = entries[it.z + base + i];
     __syncthreads();
   }
   return sEnt[e - base];
@@ -66,6 +67,26 @@ __device__ inline void two_products(f32x16& s, f32x16& dp, const char* ta, const
       s = mfma(x[k], b1[2 * g + k], s);
       dp = mfma(y[k], b2[2 * g + k], dp);
     }
+  }
+}
+
+// The same two products with both B operands read from staged tiles too:
+// row `krow` of tiles tk and tv (the unit's K and V rows in LDS).
+__device__ inline void two_products_lds(f32x16& s, f32x16& dp, const char* ta, const char* tb, int row,
+                                        const char* tk, const char* tv, int krow, int hi) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    s[r] = 0.f;
+    dp[r] = 0.f;
+  }
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    const bf16x8 x = row_operand(ta, row, kk, hi), y = row_operand(tb, row, kk, hi);
+    const bf16x8 b1 = row_operand(tk, krow, kk, hi), b2 = row_operand(tv, krow, kk, hi);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // 4 LDS reads
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // then 2 MFMAs
+    s = mfma(x, b1, s);
+    dp = mfma(y, b2, dp);
   }
 }
 
@@ -209,7 +230,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
     int4 kt_pf = make_int4(kDense ? INT32_MAX : -1, -1, -1, 0);  // keys past len: sample -1, empty range
     if (more) {
       if (n & 1) {
-        ent = list_entry(sEnt, list_base, a.entries, it, (n + 1) >> 1, tid);
+        ent = list_entry(sEnt, list_base, a.entries, it, (n + 1) >> 1, tid, 256);
         ent.x = __builtin_amdgcn_readfirstlane(ent.x);
         ent.y = __builtin_amdgcn_readfirstlane(ent.y);
       }
@@ -310,10 +331,19 @@ struct RowStage {
   int4 t;
 };
 
+// dK/dV workgroups: 8 waves over one (key tile, kv head) unit.  Waves w and
+// w + 4 hold the same 32 keys (w % 4) and take the two 32-query halves of
+// every staged query sub-tile, so two waves share each SIMD and one's vector
+// work runs beside the other's products.  The unit's K and V rows sit in LDS
+// (the B operands of S and dP), which leaves each wave its two fp32
+// accumulators and one half's products in 256 registers.  After the list the
+// two halves' partial sums meet through LDS: waves 0-3 finish dK, waves 4-7 dV.
+constexpr int kDkdvThreads = 512;
+
 // kDense: dense-call column lists (entries carry a relation and the key rows
 // of the tile they apply to).
 template <bool kDense>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
+__global__ __launch_bounds__(kDkdvThreads, 2) void bwd_dkdv_kernel(const BwdArgs a) {
   // two buffer sets: sub-tile m computes from set m % 2 while m + 1 is
   // loaded into the other, one barrier per sub-tile.  Q and dO reach LDS by
   // direct-to-LDS loads (each set its own array, so the compiler tells a load
@@ -322,6 +352,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char sQ1[kSub * 256];
   __shared__ __attribute__((aligned(1024))) char sO0[kSub * 256];
   __shared__ __attribute__((aligned(1024))) char sO1[kSub * 256];
+  __shared__ __attribute__((aligned(1024))) char sK[kTile * 256];  // the unit's K rows (two 64-row sub-tiles)
+  __shared__ __attribute__((aligned(1024))) char sV[kTile * 256];
   __shared__ __attribute__((aligned(16))) float sL[2][kSub];
   __shared__ __attribute__((aligned(16))) float sD[2][kSub];
   __shared__ int4 sQT[2][kSub];
@@ -336,9 +368,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
   const int4 it = a.items[wk.x];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kw = wave & 3, qh = wave >> 2;  // key group (32 keys), query half of each sub-tile
   const int l32 = lane & 31, hi = lane >> 5;
-  const int64_t key = (int64_t)it.x + wave * 32 + l32;  // it.x: the tile's first key row
-  const bool kvalid = wave * 32 + l32 < key_rows(it.y);
+  const int krel = kw * 32 + l32;            // the lane's key within the tile
+  const int64_t key = (int64_t)it.x + krel;  // it.x: the tile's first key row
+  const bool kvalid = krel < key_rows(it.y);
   const int32_t grp = a.hq / a.hkv;
   const uint32_t row_bytes = (uint32_t)a.hq * kHeadDim * 2u;
   const int n0 = wk.y;
@@ -350,9 +384,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
   // token index against it (staged in place of the query tracks)
   const bool kin = (it.y & kKeyInterval) != 0;
 
-  // this lane's source chunk in each direct-to-LDS load (tile_slot layout)
-  const int rw = 4 * wave + (lane >> 4);
-  const uint32_t voff = (uint32_t)rw * row_bytes + 16u * (uint32_t)((lane & 15) ^ (4 * (lane >> 4) + wave));
+  // this lane's source chunk in each direct-to-LDS load (tile_slot layout;
+  // waves 0-3 issue them): query rows, and key/value rows
+  const int rw = 4 * kw + (lane >> 4);
+  const uint32_t swz = 16u * (uint32_t)((lane & 15) ^ (4 * (lane >> 4) + kw));
+  const uint32_t voff = (uint32_t)rw * row_bytes + swz;
+  const uint32_t krow_bytes = (uint32_t)a.hkv * kHeadDim * 2u;
+  const uint32_t kvoff = (uint32_t)rw * krow_bytes + swz;
   // Load (head g*grp + m/nsub, sub-tile m%nsub): Q and dO into buffer set
   // (dq, ddo) by direct-to-LDS loads, the row scalars into registers.
   RowStage rs;
@@ -380,8 +418,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
       else
         rs.t = a.qtracks[r0 + row];
     }
-    dma_tile((const char*)(a.q + (int64_t)h * kHeadDim), dq_, r0, nxt_len, row_bytes, voff, wave);
-    dma_tile((const char*)(a.dout + (int64_t)h * kHeadDim), ddo, r0, nxt_len, row_bytes, voff, wave);
+    if (wave < 4) {
+      dma_tile((const char*)(a.q + (int64_t)h * kHeadDim), dq_, r0, nxt_len, row_bytes, voff, wave);
+      dma_tile((const char*)(a.dout + (int64_t)h * kHeadDim), ddo, r0, nxt_len, row_bytes, voff, wave);
+    }
   };
   auto stage = [&](int buf) {
     if (tid < kSub) sL[buf][tid] = tid < nxt_len ? -rs.v * kLog2e : kNegInf;
@@ -390,17 +430,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
   };
 
   // the unit's K/V rows depend on nothing loaded: issue them before the
-  // list entry and the first query sub-tile that depends on it
-  bf16x8 kf[8], vf[8];
-  {
-    const int64_t off = (key * a.hkv + g) * kHeadDim + hi * 8;
-    const unsigned short* kp = (const unsigned short*)a.k + off;
-    const unsigned short* vp = (const unsigned short*)a.v + off;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      kf[kk] = kvalid ? as_bf16x8(*(const uint4*)(kp + kk * 16)) : as_bf16x8(make_uint4(0, 0, 0, 0));
-      vf[kk] = kvalid ? as_bf16x8(*(const uint4*)(vp + kk * 16)) : as_bf16x8(make_uint4(0, 0, 0, 0));
-    }
+  // list entry and the first query sub-tile that depends on it (rows past
+  // the tile's valid keys arrive as zeros)
+  if (wave < 4) {
+    const int krows = key_rows(it.y);
+    const char* kb = (const char*)(a.k + (int64_t)g * kHeadDim);
+    const char* vb = (const char*)(a.v + (int64_t)g * kHeadDim);
+    const int len0 = krows < kSub ? krows : kSub, len1 = krows - len0;
+    dma_tile(kb, sK, it.x, len0, krow_bytes, kvoff, wave);
+    dma_tile(kb, sK + kSub * 256, it.x + kSub, len1, krow_bytes, kvoff, wave);
+    dma_tile(vb, sV, it.x, len0, krow_bytes, kvoff, wave);
+    dma_tile(vb, sV + kSub * 256, it.x + kSub, len1, krow_bytes, kvoff, wave);
   }
   // this lane's key: its tracks, or its key interval when every key of the
   // tile has one (kKeyInterval); invalid keys admit no query
@@ -422,7 +462,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
   ent.x = __builtin_amdgcn_readfirstlane(ent.x);
   ent.y = __builtin_amdgcn_readfirstlane(ent.y);
   fetch(0, ent, sQ0, sO0);
-  for (int i = tid; i < it.w && i < kListCache; i += 256) sEnt[i] = a.entries[it.z + i];
+  for (int i = tid; i < it.w && i < kListCache; i += kDkdvThreads) sEnt[i] = a.entries[it.z + i];
   const int4 kt = kvalid ? kraw : make_int4(-1, -1, -1, 0);
   f32x16 dk[4], dv[4];  // dK^T / dV^T[d = 32db + 8(r/4) + 4hi + r%4][key]
 #pragma unroll
@@ -450,7 +490,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
       if (partial) {
         int32_t dlo;
         uint32_t dspan;
-        dense_key_range(ey, wave * 32 + l32, kt.w, a.window, dlo, dspan);
+        dense_key_range(ey, krel, kt.w, a.window, dlo, dspan);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int qi = q0 + 8 * (r >> 2) + 4 * hi + (r & 3);
@@ -516,23 +556,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
       // sub-tile, and at the start of the next head's range
       const int r1 = (m + 1) % nsub, n1 = n0 + r1;
       if ((n1 & 1) == 0 || r1 == 0) {
-        ent = list_entry(sEnt, list_base, a.entries, it, n1 >> 1, tid);
+        ent = list_entry(sEnt, list_base, a.entries, it, n1 >> 1, tid, kDkdvThreads);
         ent.x = __builtin_amdgcn_readfirstlane(ent.x);
         ent.y = __builtin_amdgcn_readfirstlane(ent.y);
       }
       fetch(m + 1, ent, nq, no);
     }
-    // The two 32-query halves qc are software-pipelined inside the wave: the
-    // S and dP MFMAs of half 1 run while the vector unit builds P and dS of
-    // half 0, and the dV/dK MFMAs of half 0 while it builds those of half 1.
-    f32x16 s0, dp0, s1, dp1;
-    bf16x8 pb0[2], ds0[2], pb1[2], ds1[2];
-    two_products(s0, dp0, cq, co, l32, kf, vf, hi);
-    two_products(s1, dp1, cq, co, 32 + l32, kf, vf, hi);
-    p_and_ds(s0, dp0, pb0, ds0, 0, partial, sL[cb], sD[cb], sQT[cb], ey);
-    accumulate(pb0, ds0, 0, cq, co);
-    p_and_ds(s1, dp1, pb1, ds1, 32, partial, sL[cb], sD[cb], sQT[cb], ey);
-    accumulate(pb1, ds1, 32, cq, co);
+    // this wave's 32-query half of the sub-tile against its 32 keys
+    const int q0 = 32 * qh;
+    f32x16 s0, dp0;
+    bf16x8 pb0[2], ds0[2];
+    two_products_lds(s0, dp0, cq, co, q0 + l32, sK, sV, krel, hi);
+    p_and_ds(s0, dp0, pb0, ds0, q0, partial, sL[cb], sD[cb], sQT[cb], ey);
+    accumulate(pb0, ds0, q0, cq, co);
     if (more) {
       stage(cb ^ 1);  // the other set was last read in iteration m - 1
       cur_len = nxt_len;
@@ -549,51 +585,71 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
   }
   if (m < total) step(m, sQ0, sO0, 0, sQ1, sO1);
 
+  // The two query halves' partial sums meet through LDS, free after the
+  // loop's last barrier: waves 4-7 leave their dK partials, waves 0-3 their
+  // dV partials (16 KiB a wave, lane l's float4 number n at 1024 n + 16 l),
+  // and each side adds the other's: waves 0-3 then hold dK, waves 4-7 dV.
+  {
+    char* xk = kw == 0 ? sQ0 : kw == 1 ? sQ1 : kw == 2 ? sO0 : sO1;
+    char* xv = (kw < 2 ? sK : sV) + (kw & 1) * 16384;
+    char* mine = qh ? xk : xv;
+    const f32x16* give = qh ? dk : dv;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *(float4*)(mine + 1024 * (4 * db + i) + 16 * lane) =
+            make_float4(give[db][4 * i], give[db][4 * i + 1], give[db][4 * i + 2], give[db][4 * i + 3]);
+    __syncthreads();
+    const char* theirs = qh ? xv : xk;
+    f32x16* keep = qh ? dv : dk;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 o4 = *(const float4*)(theirs + 1024 * (4 * db + i) + 16 * lane);
+        keep[db][4 * i + 0] += o4.x;
+        keep[db][4 * i + 1] += o4.y;
+        keep[db][4 * i + 2] += o4.z;
+        keep[db][4 * i + 3] += o4.w;
+      }
+  }
   if (!kvalid) return;
+  // waves 0-3: dK, scaled; waves 4-7: dV
+  const f32x16* res = qh ? dv : dk;
+  const float mul = qh ? 1.f : a.scale;
   if (wk.w >= 0) {
-    // a split unit: its scaled partial goes to its workspace slot
-    float* wp = a.ws + ((int64_t)wk.w * a.hkv + g) * (2 * kTile * kHeadDim) + (wave * 32 + l32) * kHeadDim;
+    // a split unit: its partial goes to its workspace slot (dK, then dV)
+    float* wp = a.ws + ((int64_t)wk.w * a.hkv + g) * (2 * kTile * kHeadDim) + qh * (kTile * kHeadDim) +
+                krel * kHeadDim;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int c = db * 32 + i * 8 + hi * 4;
-        *(float4*)(wp + c) = make_float4(a.scale * dk[db][4 * i], a.scale * dk[db][4 * i + 1],
-                                         a.scale * dk[db][4 * i + 2], a.scale * dk[db][4 * i + 3]);
-        *(float4*)(wp + kTile * kHeadDim + c) =
-            make_float4(dv[db][4 * i], dv[db][4 * i + 1], dv[db][4 * i + 2], dv[db][4 * i + 3]);
+        *(float4*)(wp + c) = make_float4(mul * res[db][4 * i], mul * res[db][4 * i + 1],
+                                         mul * res[db][4 * i + 2], mul * res[db][4 * i + 3]);
       }
     return;
   }
-  // every running value is read before the first store: dk and dv may alias
-  // as far as the compiler knows, so loads interleaved with the stores would
-  // take one memory round trip each
-  const int64_t off = (key * a.hkv + g) * kHeadDim;
-  float4 k4[16], v4[16];
+  // every running value is read before the first store (one memory round
+  // trip), then each is added to and stored
+  float* run = (qh ? a.dv : a.dk) + (key * a.hkv + g) * kHeadDim;
+  float4 r4[16];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r4[4 * db + i] = *(const float4*)(run + db * 32 + i * 8 + hi * 4);
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int c = db * 32 + i * 8 + hi * 4;
-      k4[4 * db + i] = *(const float4*)(a.dk + off + c);
-      v4[4 * db + i] = *(const float4*)(a.dv + off + c);
-    }
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = db * 32 + i * 8 + hi * 4;
-      float4 kx = k4[4 * db + i], vx = v4[4 * db + i];
-      kx.x += a.scale * dk[db][4 * i + 0];
-      kx.y += a.scale * dk[db][4 * i + 1];
-      kx.z += a.scale * dk[db][4 * i + 2];
-      kx.w += a.scale * dk[db][4 * i + 3];
-      vx.x += dv[db][4 * i + 0];
-      vx.y += dv[db][4 * i + 1];
-      vx.z += dv[db][4 * i + 2];
-      vx.w += dv[db][4 * i + 3];
-      *(float4*)(a.dk + off + c) = kx;
-      *(float4*)(a.dv + off + c) = vx;
+      float4 x = r4[4 * db + i];
+      x.x += mul * res[db][4 * i + 0];
+      x.y += mul * res[db][4 * i + 1];
+      x.z += mul * res[db][4 * i + 2];
+      x.w += mul * res[db][4 * i + 3];
+      *(float4*)(run + db * 32 + i * 8 + hi * 4) = x;
     }
 }
 
@@ -710,9 +766,9 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
   const int64_t blocks = (int64_t)a.nitems * a.hkv;
   if (blocks <= 0) return hipSuccess;
   if (a.dense)
-    hipLaunchKernelGGL(bwd_dkdv_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(bwd_dkdv_kernel<true>, dim3((unsigned)blocks), dim3(kDkdvThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL(bwd_dkdv_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(bwd_dkdv_kernel<false>, dim3((unsigned)blocks), dim3(kDkdvThreads), 0, stream, a);
   return hipGetLastError();
 }
 

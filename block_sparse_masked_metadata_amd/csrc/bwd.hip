@@ -384,13 +384,9 @@ __global__ __launch_bounds__(kDkdvThreads, 2) void bwd_dkdv_kernel(const BwdArgs
   // token index against it (staged in place of the query tracks)
   const bool kin = (it.y & kKeyInterval) != 0;
 
-  // this lane's source chunk in each direct-to-LDS load (tile_slot layout;
-  // waves 0-3 issue them): query rows, and key/value rows
-  const int rw = 4 * kw + (lane >> 4);
-  const uint32_t swz = 16u * (uint32_t)((lane & 15) ^ (4 * (lane >> 4) + kw));
-  const uint32_t voff = (uint32_t)rw * row_bytes + swz;
-  const uint32_t krow_bytes = (uint32_t)a.hkv * kHeadDim * 2u;
-  const uint32_t kvoff = (uint32_t)rw * krow_bytes + swz;
+  // direct-to-LDS loads (tile_slot layout; waves 0-3 issue them): lane l
+  // of wave w reads row 4 w + l / 16 of each group of 16, chunk (l % 16) ^
+  // f(row), as dma_tile lays them out
   // Load (head g*grp + m/nsub, sub-tile m%nsub): Q and dO into buffer set
   // (dq, ddo) by direct-to-LDS loads, the row scalars into registers.
   RowStage rs;
@@ -408,31 +404,34 @@ __global__ __launch_bounds__(kDkdvThreads, 2) void bwd_dkdv_kernel(const BwdArgs
     // nothing computes on a loaded value before stage(), and no register
     // is written after a load into it is issued, so no wave waits here
     // before issuing the Q/dO loads.
-    const int row = tid & (kSub - 1);
+    const int row = lane;  // the wave's 64 lanes cover the sub-tile's rows
     rs.v = 0.f;
     rs.t = make_int4(-2, -1, -1, -1);  // rows past len: no sample, no position
-    if (tid < 2 * kSub && row < nxt_len) rs.v = (tid < kSub ? a.lse : a.delta)[(int64_t)h * a.rows + r0 + row];
-    if (tid >= 2 * kSub && tid < 3 * kSub && nxt_partial && row < nxt_len) {
+    if (wave < 2 && row < nxt_len) rs.v = (wave == 0 ? a.lse : a.delta)[(int64_t)h * a.rows + r0 + row];
+    if (wave == 2 && nxt_partial && row < nxt_len) {
       if (kin)
         rs.t.w = a.qcoord[r0 + row];
       else
         rs.t = a.qtracks[r0 + row];
     }
     if (wave < 4) {
+      const uint32_t voff = (uint32_t)(4 * kw + (lane >> 4)) * row_bytes + 16u * (uint32_t)((lane & 15) ^ (4 * (lane >> 4) + kw));
       dma_tile((const char*)(a.q + (int64_t)h * kHeadDim), dq_, r0, nxt_len, row_bytes, voff, wave);
       dma_tile((const char*)(a.dout + (int64_t)h * kHeadDim), ddo, r0, nxt_len, row_bytes, voff, wave);
     }
   };
   auto stage = [&](int buf) {
-    if (tid < kSub) sL[buf][tid] = tid < nxt_len ? -rs.v * kLog2e : kNegInf;
-    else if (tid < 2 * kSub) sD[buf][tid - kSub] = rs.v;
-    else if (tid < 3 * kSub) sQT[buf][tid - 2 * kSub] = query_tracks(rs.t);
+    if (wave == 0) sL[buf][lane] = lane < nxt_len ? -rs.v * kLog2e : kNegInf;
+    else if (wave == 1) sD[buf][lane] = rs.v;
+    else if (wave == 2) sQT[buf][lane] = query_tracks(rs.t);
   };
 
   // the unit's K/V rows depend on nothing loaded: issue them before the
   // list entry and the first query sub-tile that depends on it (rows past
   // the tile's valid keys arrive as zeros)
   if (wave < 4) {
+    const uint32_t krow_bytes = (uint32_t)a.hkv * kHeadDim * 2u;
+    const uint32_t kvoff = (uint32_t)(4 * kw + (lane >> 4)) * krow_bytes + 16u * (uint32_t)((lane & 15) ^ (4 * (lane >> 4) + kw));
     const int krows = key_rows(it.y);
     const char* kb = (const char*)(a.k + (int64_t)g * kHeadDim);
     const char* vb = (const char*)(a.v + (int64_t)g * kHeadDim);

@@ -16,9 +16,10 @@
 //   dkdv : one workgroup per (key tile, key/value head), walking the tile's
 //          column list for every query head of the group in 64-query
 //          sub-tiles; S and dP put one key per lane; dV^T += dO^T P and
-//          dK^T += Q^T dS read dO^T and Q^T with the LDS transpose read.  K
-//          and V rows and both accumulators stay in registers (one wave per
-//          SIMD).
+//          dK^T += Q^T dS read dO^T and Q^T with the LDS transpose read.  8
+//          waves: four key groups of 32 times the two 32-query halves of a
+//          sub-tile (two waves per SIMD), K and V rows in LDS, both
+//          accumulators in registers; the halves' sums meet at the end.
 
 #include "tile_common.hpp"
 

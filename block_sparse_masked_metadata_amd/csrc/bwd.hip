@@ -10,7 +10,8 @@
 //   dQ_i += scale * dS_ij k_j,  dK_j += scale * dS_ij q_i,  dV_j += P_ij dO_i
 // (D_i = dO_i . O_i from the prep kernel).  Two deterministic kernels:
 //   dq   : one workgroup per (query tile, query head), walking the tile's row
-//          list in 64-key sub-tiles (the next one prefetched into registers);
+//          list in 64-key sub-tiles (the next one loaded direct-to-LDS into
+//          the other buffer set while one is used);
 //          S^T and dP^T put one query per lane, so LSE_i and D_i are lane
 //          scalars; dQ^T += K^T dS^T reads K^T with the LDS transpose read.
 //   dkdv : one workgroup per (key tile, key/value head), walking the tile's

@@ -44,15 +44,15 @@ __device__ inline int2 list_entry(int2* sEnt, int& base, const int2* entries, in
   return sEnt[e - base];
 }
 
-// s += A_rows(tileA) . b1 and dp += A_rows(tileB) . b2 over the 128 channels:
-// row `row` of two staged tiles against two register operands, with the LDS
-// operand reads issued 4 at a time ahead of their MFMAs.
+// s = A_rows(tileA) . b1 and dp = dp0 + A_rows(tileB) . b2 over the 128
+// channels: row `row` of two staged tiles against two register operands, with
+// the LDS operand reads issued 4 at a time ahead of their MFMAs.
 __device__ inline void two_products(f32x16& s, f32x16& dp, const char* ta, const char* tb, int row,
-                                    const bf16x8 (&b1)[8], const bf16x8 (&b2)[8], int hi) {
+                                    const bf16x8 (&b1)[8], const bf16x8 (&b2)[8], int hi, float dp0) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     s[r] = 0.f;
-    dp[r] = 0.f;
+    dp[r] = dp0;
   }
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
@@ -72,14 +72,15 @@ __device__ inline void two_products(f32x16& s, f32x16& dp, const char* ta, const
   }
 }
 
-// The same two products with both B operands read from staged tiles too:
-// row `krow` of tiles tk and tv (the unit's K and V rows in LDS).
+// The same two products with both B operands read from staged tiles too
+// (row `krow` of tiles tk and tv, the unit's K and V rows in LDS) and dp
+// started from dp0.
 __device__ inline void two_products_lds(f32x16& s, f32x16& dp, const char* ta, const char* tb, int row,
-                                        const char* tk, const char* tv, int krow, int hi) {
+                                        const char* tk, const char* tv, int krow, int hi, const f32x16& dp0) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     s[r] = 0.f;
-    dp[r] = 0.f;
+    dp[r] = dp0[r];
   }
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
@@ -252,7 +253,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
       f32x16 s, dp;
-      two_products(s, dp, sK, sV, kc * 32 + l32, qf, df, hi);
+      two_products(s, dp, sK, sV, kc * 32 + l32, qf, df, hi, -dl);  // dp = dP - delta
       // s[r] = S[query l32][key 32kc + 8(r/4) + 4hi + r%4]
       if (kDense) {
         if (partial) {
@@ -282,7 +283,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.scale_log2, nlse2));
-        dp[r] = p * (dp[r] - dl);
+        dp[r] = p * dp[r];
       }
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
@@ -424,7 +425,7 @@ __global__ __launch_bounds__(kDkdvThreads, 2) void bwd_dkdv_kernel(const BwdArgs
   };
   auto stage = [&](int buf) {
     if (wave == 0) sL[buf][lane] = lane < nxt_len ? -rs.v * kLog2e : kNegInf;
-    else if (wave == 1) sD[buf][lane] = rs.v;
+    else if (wave == 1) sD[buf][lane] = -rs.v;  // the dP products start from -delta
     else if (wave == 2) sQT[buf][lane] = query_tracks(rs.t);
   };
 
@@ -483,10 +484,11 @@ __global__ __launch_bounds__(kDkdvThreads, 2) void bwd_dkdv_kernel(const BwdArgs
 
   // P = exp2(S * scale*log2(e) - LSE*log2(e)) and dS = P (dP - delta) for the
   // 32 queries [q0, q0+32) of the staged sub-tile, as bf16 MFMA B operands
-  // (lane: key; register r: query q0 + 8(r/4) + 4hi + r%4).  On partial
-  // sub-tiles illegal pairs get P = 0; rows past len carry sample -2.
+  // (lane: key; register r: query q0 + 8(r/4) + 4hi + r%4); dp arrives as
+  // dP - delta (its products start from -delta).  On partial sub-tiles
+  // illegal pairs get P = 0; rows past len carry sample -2.
   auto p_and_ds = [&](f32x16& s, f32x16& dp, bf16x8 (&pb)[2], bf16x8 (&dsb)[2], int q0, bool partial,
-                      const float* sL, const float* sD, const int4* sQT, int32_t ey) {
+                      const float* sL, const int4* sQT, int32_t ey) {
     if (kDense) {
       if (partial) {
         int32_t dlo;
@@ -515,15 +517,13 @@ __global__ __launch_bounds__(kDkdvThreads, 2) void bwd_dkdv_kernel(const BwdArgs
     for (int i = 0; i < 4; ++i) {
       const int q4 = q0 + 8 * i + 4 * hi;
       const float4 l4 = *(const float4*)(sL + q4);
-      const float4 d4 = *(const float4*)(sD + q4);
       const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-      const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int r = 4 * i + c;
         const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.scale_log2, lv[c]));
         s[r] = p;
-        dp[r] = p * (dp[r] - dv4[c]);
+        dp[r] = p * dp[r];
       }
     }
 #pragma unroll
@@ -565,10 +565,18 @@ __global__ __launch_bounds__(kDkdvThreads, 2) void bwd_dkdv_kernel(const BwdArgs
     }
     // this wave's 32-query half of the sub-tile against its 32 keys
     const int q0 = 32 * qh;
-    f32x16 s0, dp0;
+    f32x16 s0, dp0, nd;  // nd: -delta of the lane's 16 query rows
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 d4 = *(const float4*)(sD[cb] + q0 + 8 * i + 4 * hi);
+      nd[4 * i + 0] = d4.x;
+      nd[4 * i + 1] = d4.y;
+      nd[4 * i + 2] = d4.z;
+      nd[4 * i + 3] = d4.w;
+    }
     bf16x8 pb0[2], ds0[2];
-    two_products_lds(s0, dp0, cq, co, q0 + l32, sK, sV, krel, hi);
-    p_and_ds(s0, dp0, pb0, ds0, q0, partial, sL[cb], sD[cb], sQT[cb], ey);
+    two_products_lds(s0, dp0, cq, co, q0 + l32, sK, sV, krel, hi, nd);  // dp0 = dP - delta
+    p_and_ds(s0, dp0, pb0, ds0, q0, partial, sL[cb], sQT[cb], ey);
     accumulate(pb0, ds0, q0, cq, co);
     if (more) {
       stage(cb ^ 1);  // the other set was last read in iteration m - 1

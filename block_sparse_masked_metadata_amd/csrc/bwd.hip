@@ -45,10 +45,11 @@ __device__ inline int2 list_entry(int2* sEnt, int& base, const int2* entries, in
 }
 
 // s = A_rows(tileA) . b1 and dp = dp0 + A_rows(tileB) . b2 over the 128
-// channels: row `row` of two staged tiles against two register operands, with
-// the LDS operand reads issued 4 at a time ahead of their MFMAs.
-__device__ inline void two_products(f32x16& s, f32x16& dp, const char* ta, const char* tb, int row,
-                                    const bf16x8 (&b1)[8], const bf16x8 (&b2)[8], int hi, float dp0) {
+// channels: the lane's row of two staged tiles (its 16-byte operands at the
+// per-lane byte offsets ao[kk]) against two register operands, with the LDS
+// operand reads issued 4 at a time ahead of their MFMAs.
+__device__ inline void two_products(f32x16& s, f32x16& dp, const char* ta, const char* tb, const uint32_t (&ao)[8],
+                                    const bf16x8 (&b1)[8], const bf16x8 (&b2)[8], float dp0) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     s[r] = 0.f;
@@ -59,8 +60,8 @@ __device__ inline void two_products(f32x16& s, f32x16& dp, const char* ta, const
     bf16x8 x[2], y[2];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      x[k] = row_operand(ta, row, 2 * g + k, hi);
-      y[k] = row_operand(tb, row, 2 * g + k, hi);
+      x[k] = as_bf16x8(*(const uint4*)(ta + ao[2 * g + k]));
+      y[k] = as_bf16x8(*(const uint4*)(tb + ao[2 * g + k]));
     }
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // 4 LDS reads
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // then 4 MFMAs
@@ -86,6 +87,26 @@ __device__ inline void two_products_lds(f32x16& s, f32x16& dp, const char* ta, c
   for (int kk = 0; kk < 8; ++kk) {
     const bf16x8 x = row_operand(ta, row, kk, hi), y = row_operand(tb, row, kk, hi);
     const bf16x8 b1 = row_operand(tk, krow, kk, hi), b2 = row_operand(tv, krow, kk, hi);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // 4 LDS reads
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // then 2 MFMAs
+    s = mfma(x, b1, s);
+    dp = mfma(y, b2, dp);
+  }
+}
+
+// The same two products over per-lane byte offsets inside the staged tiles:
+// ta/tb at ao[kk], tk/tv at ko[kk] (channels [16 kk + 8 hi, +8) of the rows).
+__device__ inline void two_products_off(f32x16& s, f32x16& dp, const char* ta, const char* tb, const uint32_t (&ao)[8],
+                                        const char* tk, const char* tv, const uint32_t (&ko)[8], const f32x16& dp0) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    s[r] = 0.f;
+    dp[r] = dp0[r];
+  }
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    const bf16x8 x = as_bf16x8(*(const uint4*)(ta + ao[kk])), y = as_bf16x8(*(const uint4*)(tb + ao[kk]));
+    const bf16x8 b1 = as_bf16x8(*(const uint4*)(tk + ko[kk])), b2 = as_bf16x8(*(const uint4*)(tv + ko[kk]));
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // 4 LDS reads
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // then 2 MFMAs
     s = mfma(x, b1, s);
@@ -217,7 +238,21 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
   if (tid < kSub) sKT0[tid] = kt0;
   __builtin_amdgcn_s_waitcnt(0);  // no load is pending when the loop starts (direct-to-LDS ones included)
   __syncthreads();
-  const TrLane tr(lane);
+  // Per-lane byte offsets of the loop's LDS reads inside a staged sub-tile,
+  // the same for every sub-tile: the row reads of the lane's key (keys
+  // 32 kc + l32 at +8192 kc) and the transposed reads (channels 32 db..,
+  // rows r and r + 8 of a 16-key group; group 2 kc + hf at +4096 (2 kc + hf)).
+  uint32_t kro[8], tro[4][2];
+  {
+    const TrLane tr(lane);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) kro[kk] = (uint32_t)tile_slot(l32, 2 * kk + hi);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      tro[db][0] = (uint32_t)(tile_slot(tr.row0, 4 * db + tr.chunk) + tr.off8);
+      tro[db][1] = (uint32_t)(tile_slot(tr.row0 + 8, 4 * db + tr.chunk) + tr.off8);
+    }
+  }
 
   // Sub-tile n from buffer set (sK, sV, sKT); the loads of n + 1 go to the
   // other set (nK, nV, nKT), which every wave finished with before the
@@ -253,7 +288,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
       f32x16 s, dp;
-      two_products(s, dp, sK, sV, kc * 32 + l32, qf, df, hi, -dl);  // dp = dP - delta
+      two_products(s, dp, sK + 8192 * kc, sV + 8192 * kc, kro, qf, df, -dl);  // dp = dP - delta
       // s[r] = S[query l32][key 32kc + 8(r/4) + 4hi + r%4]
       if (kDense) {
         if (partial) {
@@ -291,7 +326,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) dsb[i] = (__bf16)dp[8 * hf + i];
 #pragma unroll
-        for (int db = 0; db < 4; ++db) acc[db] = mfma(tr.read(sK, kc * 32 + 16 * hf, db), dsb, acc[db]);
+        for (int db = 0; db < 4; ++db) {
+          const char* t = sK + 4096 * (2 * kc + hf);
+          acc[db] = mfma(lds_tr8(t + tro[db][0], t + tro[db][1]), dsb, acc[db]);
+        }
       }
     }
     if (more && tid < kSub) nKT[tid] = kt_pf;
@@ -351,10 +389,10 @@ __global__ __launch_bounds__(kDkdvThreads, 2) void bwd_dkdv_kernel(const BwdArgs
   // loaded into the other, one barrier per sub-tile.  Q and dO reach LDS by
   // direct-to-LDS loads (each set its own array, so the compiler tells a load
   // into one from reads of the other); the row scalars go through registers.
-  __shared__ __attribute__((aligned(1024))) char sQ0[kSub * 256];
-  __shared__ __attribute__((aligned(1024))) char sQ1[kSub * 256];
-  __shared__ __attribute__((aligned(1024))) char sO0[kSub * 256];
-  __shared__ __attribute__((aligned(1024))) char sO1[kSub * 256];
+  __shared__ __attribute__((aligned(4096))) char sQ0[kSub * 256];
+  __shared__ __attribute__((aligned(4096))) char sQ1[kSub * 256];
+  __shared__ __attribute__((aligned(4096))) char sO0[kSub * 256];
+  __shared__ __attribute__((aligned(4096))) char sO1[kSub * 256];
   __shared__ __attribute__((aligned(1024))) char sK[kTile * 256];  // the unit's K rows (two 64-row sub-tiles)
   __shared__ __attribute__((aligned(1024))) char sV[kTile * 256];
   __shared__ __attribute__((aligned(16))) float sL[2][kSub];
@@ -480,7 +518,25 @@ __global__ __launch_bounds__(kDkdvThreads, 2) void bwd_dkdv_kernel(const BwdArgs
   cur_ey = nxt_ey;
   __builtin_amdgcn_s_waitcnt(0);  // no load is pending when the loop starts (direct-to-LDS ones included)
   __syncthreads();
-  const TrLane tr(lane);
+  // Per-lane byte offsets of the loop's LDS reads inside a staged tile, the
+  // same for every sub-tile: the transposed reads of the wave's query rows
+  // (channels 32 db.., rows r and r + 8; the second 16-row half at +4096),
+  // and the row reads of its query rows and of its keys.
+  uint32_t tro[4][2], qro[8], kro[8];
+  {
+    const TrLane tr(lane);
+    const int r = 32 * qh + tr.row0;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      tro[db][0] = (uint32_t)(tile_slot(r, 4 * db + tr.chunk) + tr.off8);
+      tro[db][1] = (uint32_t)(tile_slot(r + 8, 4 * db + tr.chunk) + tr.off8);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      qro[kk] = (uint32_t)tile_slot(32 * qh + l32, 2 * kk + hi);
+      kro[kk] = (uint32_t)tile_slot(krel, 2 * kk + hi);
+    }
+  }
 
   // P = exp2(S * scale*log2(e) - LSE*log2(e)) and dS = P (dP - delta) for the
   // 32 queries [q0, q0+32) of the staged sub-tile, as bf16 MFMA B operands
@@ -540,8 +596,8 @@ __global__ __launch_bounds__(kDkdvThreads, 2) void bwd_dkdv_kernel(const BwdArgs
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        dv[db] = mfma(tr.read(sO, q0 + 16 * hf, db), pb[hf], dv[db]);
-        dk[db] = mfma(tr.read(sQ, q0 + 16 * hf, db), dsb[hf], dk[db]);
+        dv[db] = mfma(lds_tr8(sO + 4096 * hf + tro[db][0], sO + 4096 * hf + tro[db][1]), pb[hf], dv[db]);
+        dk[db] = mfma(lds_tr8(sQ + 4096 * hf + tro[db][0], sQ + 4096 * hf + tro[db][1]), dsb[hf], dk[db]);
       }
   };
 
@@ -575,7 +631,7 @@ __global__ __launch_bounds__(kDkdvThreads, 2) void bwd_dkdv_kernel(const BwdArgs
       nd[4 * i + 3] = d4.w;
     }
     bf16x8 pb0[2], ds0[2];
-    two_products_lds(s0, dp0, cq, co, q0 + l32, sK, sV, krel, hi, nd);  // dp0 = dP - delta
+    two_products_off(s0, dp0, cq, co, qro, sK, sV, kro, nd);  // dp0 = dP - delta
     p_and_ds(s0, dp0, pb0, ds0, q0, partial, sL[cb], sQT[cb], ey);
     accumulate(pb0, ds0, q0, cq, co);
     if (more) {

@@ -631,9 +631,15 @@ __global__ __launch_bounds__(kDkdvThreads, 2) void bwd_dkdv_kernel(const BwdArgs
       nd[4 * i + 3] = d4.w;
     }
     bf16x8 pb0[2], ds0[2];
+    // the MFMA blocks run at raised wave priority: the SIMD's arbiter issues
+    // them ahead of the other wave's vector work
+    __builtin_amdgcn_s_setprio(1);
     two_products_off(s0, dp0, cq, co, qro, sK, sV, kro, nd);  // dp0 = dP - delta
+    __builtin_amdgcn_s_setprio(0);
     p_and_ds(s0, dp0, pb0, ds0, q0, partial, sL[cb], sQT[cb], ey);
+    __builtin_amdgcn_s_setprio(1);
     accumulate(pb0, ds0, q0, cq, co);
+    __builtin_amdgcn_s_setprio(0);
     if (more) {
       stage(cb ^ 1);  // the other set was last read in iteration m - 1
       cur_len = nxt_len;

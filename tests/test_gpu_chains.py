@@ -29,10 +29,15 @@ def _both(case):
     return one, two, st1, st2
 
 
-@pytest.mark.parametrize("maker", ["packed_text", "packed_multimodal", "video_group", "random5", "random6"])
+@pytest.mark.parametrize("maker", ["packed_text", "packed_multimodal", "video_group", "sliding_window", "long_mixed",
+                                   "random5", "random6"])
 def test_two_chains_equal_one_launch(maker):
+    """Every workload's full share, including the two whose rule picks one
+    chain (sliding window 128K, long mixed 1M): the split by samples is
+    exercised on them too."""
     lay = {"packed_text": packed_text, "packed_multimodal": packed_multimodal,
-           "video_group": lambda: config(6)}.get(maker)
+           "video_group": lambda: config(6), "sliding_window": lambda: config(4),
+           "long_mixed": lambda: config(5)}.get(maker)
     lay = lay() if lay else _random(int(maker[-1]))
     case = Case(lay)
     one, two, st1, st2 = _both(case)
